@@ -1,0 +1,178 @@
+"""ctypes binding of libdash.so (the C ABI in include/dash.h).
+
+Argument marshalling only: tensors supply device pointers and shapes, torch's
+current stream is passed through, and every step runs in the HIP library.
+There is no fallback: if libdash.so is missing or a call fails, an exception
+is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_int, c_size_t, c_void_p
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdash.so")
+
+DASH_OK, DASH_E_INVAL, DASH_E_SHAPE, DASH_E_DTYPE, DASH_E_ALIGN, DASH_E_WORKSPACE, DASH_E_HIP = range(7)
+DASH_F32, DASH_BF16 = 0, 1
+DASH_KV_ACTIVE, DASH_KV_ALL = 0, 1
+DASH_SEL_TOPK, DASH_SEL_THRESHOLD, DASH_SEL_ORDER_STAT = 0, 1, 2
+DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE = 0, 1, 2
+
+EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
+            "dash_attn_layer", "dash_select", "dash_compact", "dash_attn_active")
+
+
+class DashShape(Structure):
+    _fields_ = [("B", c_int), ("S", c_int), ("Hq", c_int), ("Hkv", c_int), ("D", c_int), ("hidden", c_int),
+                ("dtype", c_int)]
+
+
+class DashSel(Structure):
+    _fields_ = [("mode", c_int), ("k", c_int), ("rank", c_int), ("tau", c_void_p), ("patience", c_int),
+                ("counters", c_void_p), ("keep_first", c_int), ("keep_last", c_int)]
+
+
+class DashError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dash error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdash.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m attention_delta_token_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.dash_create.argtypes = [POINTER(c_void_p), c_int]
+    lib.dash_create.restype = c_int
+    lib.dash_destroy.argtypes = [c_void_p]
+    lib.dash_destroy.restype = None
+    lib.dash_last_error.argtypes = []
+    lib.dash_last_error.restype = c_char_p
+    lib.dash_version.argtypes = []
+    lib.dash_version.restype = c_char_p
+    lib.dash_workspace_size.argtypes = [c_void_p, c_int, POINTER(DashShape), c_int]
+    lib.dash_workspace_size.restype = c_size_t
+    lib.dash_attn_layer.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dash_attn_layer.restype = c_int
+    lib.dash_select.argtypes = [c_void_p, POINTER(DashSel), c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dash_select.restype = c_int
+    lib.dash_compact.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, c_size_t, c_void_p,
+                                 c_void_p]
+    lib.dash_compact.restype = c_int
+    lib.dash_attn_active.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_int,
+                                     c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]
+    lib.dash_attn_active.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != DASH_OK:
+        raise DashError(rc, load().dash_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DASH_BF16
+    if t.dtype == torch.float32:
+        return DASH_F32
+    raise DashError(DASH_E_DTYPE, f"unsupported tensor dtype {t.dtype}")
+
+
+def make_shape(B: int, S: int, Hq: int, Hkv: int, D: int, hidden: int, dtype: int) -> DashShape:
+    return DashShape(B, S, Hq, Hkv, D, hidden, dtype)
+
+
+def version() -> str:
+    return load().dash_version().decode()
+
+
+def dash_workspace_size(op: int, shape: DashShape, n_max: int) -> int:
+    return int(load().dash_workspace_size(None, op, ctypes.byref(shape), n_max))
+
+
+def workspace(op: int, shape: DashShape, n_max: int, device="cuda") -> torch.Tensor:
+    """Allocate (through torch) a workspace of dash_workspace_size bytes (at least 256)."""
+    n = max(256, dash_workspace_size(op, shape, n_max))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dash_attn_layer(Q, K, V, Wo, O, U, score=None, ws=None, stream=None) -> None:
+    """Full-length layer: O = causal GQA attention, U = O·Wo^T, score = ||U_t||_2.
+
+    Q [B,S,Hq,D] (or [S,Hq,D]); K, V [B,S,Hkv,D]; Wo [hidden, Hq*D]; O [B,S,Hq*D]; U [B,S,hidden]."""
+    q = Q if Q.dim() == 4 else Q.unsqueeze(0)
+    k = K if K.dim() == 4 else K.unsqueeze(0)
+    B, S, Hq, D = q.shape
+    shape = make_shape(B, S, Hq, k.shape[2], D, Wo.shape[0], _dtype_code(Q))
+    _check(load().dash_attn_layer(None, ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(Wo), _ptr(O),
+                                  _ptr(U), _ptr(score), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+
+
+def dash_select(score, idx=None, *, mode: int = DASH_SEL_TOPK, k: int = 0, rank: int = 0, tau=None,
+                patience: int = 2, counters=None, pos=None, n_dev=None, n_max: int | None = None, rows: int = 1,
+                n_out=None, tau_out=None, stream=None) -> None:
+    """Top-k / order statistic / threshold step (see include/dash.h)."""
+    if n_max is None:
+        n_max = score.shape[-1] if score is not None else 0
+    sel = DashSel(mode, k, rank, _ptr(tau), patience, _ptr(counters), 0, 0)
+    _check(load().dash_select(None, ctypes.byref(sel), _ptr(score), _ptr(pos), _ptr(n_dev), n_max, rows,
+                              _ptr(idx), _ptr(n_out), _ptr(tau_out), None, 0, _stream(stream)))
+
+
+def dash_compact(idx, X, Xa, n_dev=None, n_max: int | None = None, stream=None) -> None:
+    """Xa[r] = X[idx[r]] for r < n (n = *n_dev or n_max); X is [S, ...] row-major."""
+    S = X.shape[0]
+    row_bytes = X[0].numel() * X.element_size() if S > 0 else Xa[0].numel() * Xa.element_size()
+    if n_max is None:
+        n_max = idx.shape[0]
+    _check(load().dash_compact(None, _ptr(idx), _ptr(n_dev), n_max, _ptr(X), S, row_bytes, _ptr(Xa),
+                               _stream(stream)))
+
+
+def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: int | None = None, Wo=None,
+                     Ua=None, score=None, ws=None, S: int | None = None, hidden: int | None = None,
+                     stream=None) -> None:
+    """Post-halt attention (see include/dash.h).  Qa [n,Hq,D]; K, V [n or S, Hkv, D]."""
+    n_cap, Hq, D = Qa.shape
+    if n_max is None:
+        n_max = n_cap
+    if S is None:
+        S = K.shape[0] if kv_mode == DASH_KV_ALL else n_max
+    if hidden is None:
+        hidden = Wo.shape[0] if Wo is not None else Hq * D
+    shape = make_shape(1, S, Hq, K.shape[1], D, hidden, _dtype_code(Qa))
+    _check(load().dash_attn_active(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(n_dev), n_max, _ptr(K),
+                                   _ptr(V), kv_mode, _ptr(Oa), _ptr(Wo), _ptr(Ua), _ptr(score), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))

@@ -1,0 +1,70 @@
+"""Build the DASH HIP library (libdash.so) in-tree for gfx950 with hipcc.
+
+    python -m attention_delta_token_amd.build        # or: python attention_delta_token_amd/build.py
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libdash.so")
+SOURCES = ["attn_fwd.hip", "wo_gemm.hip", "select.hip", "compact.hip", "dash_abi.cpp"]
+ARCH = os.environ.get("DASH_OFFLOAD_ARCH", "gfx950")
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # keep the compiler from forming packed fp32 VALU ops (see the design notes)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libdash.so)")
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="dash_build_")
+    try:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            lang = ["-x", "hip"] if src.endswith(".cpp") else []
+            cmd = [cc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+            objs.append(obj)
+        failed = []
+        for src, p in procs:
+            out, _ = p.communicate()
+            text = out.decode(errors="replace")
+            # hipcc's host pass does not know the packed-fp32 feature: harmless
+            text = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+            if p.returncode != 0:
+                failed.append(src)
+                sys.stderr.write(text + "\n")
+            elif verbose and text.strip():
+                print(text)
+        if failed:
+            raise RuntimeError(f"hipcc failed on {failed}")
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp_lib, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,429 @@
+// Causal grouped-query attention for the DASH prefill path (gfx950).
+//
+// Full-length layers and post-halt layers share one kernel.  Queries carry
+// their original token positions (identity for a full-length layer); key row r
+// sits at position r of the K/V it is given.  Key r is visible to a query at
+// position p iff r <= p.  This covers:
+//   * the full-length layer: queries 0..S-1, keys 0..S-1;
+//   * post-halt with the pruned KV cache (keys and values compacted at the same
+//     ascending positions as the queries): causal in compacted order, which is
+//     the same order because the active set is ascending — CSDN explainer
+//     "DASH：基于注意力增量的Transformer令牌压缩，实现长序列推理高效加速", §3.1
+//     step 4 and §5.1 (only active tokens are computed and cached);
+//   * post-halt with the full KV cache (halted tokens keep their K/V but are no
+//     longer queries) — forum summary "DASH：通过注意力动态监测实现长上下文高效预填充",
+//     section 选择性停止机制.
+//
+// bf16 kernel: 256 threads = 4 waves, 128 queries of one q-head per workgroup
+// (32 per wave), 64 keys per step.  Scores are computed transposed,
+// S^T = K · Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one query and
+// 32 of the step's keys: the softmax max and sum stay in registers except for
+// one exchange with the partner half-wave.  The output is accumulated
+// transposed too, O^T += V^T · P^T, where P^T is fed straight from the score
+// accumulators (rounded to bf16) as the B operand and V^T is read from an LDS
+// copy of the V tile stored transposed with an XOR swizzle on 8-byte granules
+// (conflict-free operand reads).  K and V tiles are double-buffered in LDS
+// with register prefetch one tile ahead; one barrier per step.  Workgroups
+// are ordered heaviest-first (causal work grows with the query position) and
+// the q-heads that share a kv-head are placed on the same XCD so they share
+// its L2.
+#include "dash_common.h"
+#include "dash_kernels.h"
+
+namespace dash {
+
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kBQ = 128;  // queries per workgroup
+constexpr int kBKV = 64;  // keys per step
+
+// Logical (query tile, q-head) of workgroup `bid`: pairs (query tile, kv-head)
+// are enumerated heaviest query tile first; the g q-heads of a pair land on
+// workgroup ids that are equal mod 8 (one XCD).
+__device__ __forceinline__ void attn_tile_of(int bid, int n_qt, int Hkv, int g, int& qt, int& h) {
+  const int pairs = n_qt * Hkv;
+  const int full = pairs / 8;
+  const int grp = 8 * g;
+  int p, j;
+  if (bid < full * grp) {
+    const int gi = bid / grp, w = bid - gi * grp;
+    j = w >> 3;
+    p = gi * 8 + (w & 7);
+  } else {
+    const int r = pairs - full * 8;
+    const int w = bid - full * grp;
+    j = w / r;
+    p = full * 8 + (w - j * r);
+  }
+  const int kvh = p % Hkv;
+  qt = n_qt - 1 - p / Hkv;
+  h = kvh * g + j;
+}
+
+template <int D>
+struct AttnLds {
+  static constexpr int kKRow = D + 8;                   // padded K row (bf16)
+  static constexpr int kKElems = kBKV * kKRow;
+  static constexpr int kVtElems = D * kBKV;             // V^T [D][64], swizzled
+  static constexpr int kStage = kKElems + kVtElems;
+  static constexpr int kTotal = 2 * kStage;
+  static constexpr int kORow = D + 8;                   // output staging row
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                        int k0, int n_kv, int kv_ld, u32x4 (&rk)[D / 32],
+                                        u32x4 (&rv)[D / 64][2]) {
+  const int tid = threadIdx.x;
+  // K: 64 rows x D/8 chunks; thread takes chunks tid + i*256.
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int c = tid + i * kAttnThreads;
+    const int key = c / (D / 8);
+    const int dc = c % (D / 8);
+    const int row = k0 + key;
+    rk[i] = (row < n_kv) ? *reinterpret_cast<const u32x4*>(K + static_cast<size_t>(row) * kv_ld + dc * 8)
+                         : u32x4{0u, 0u, 0u, 0u};
+  }
+  // V: pairs of keys x D/8 chunks; item c: key pair c % 32, chunk c / 32.
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int c = tid + i * kAttnThreads;
+    const int kp = c & 31;
+    const int dc = c >> 5;
+    const int row = k0 + 2 * kp;
+    rv[i][0] = (row < n_kv) ? *reinterpret_cast<const u32x4*>(V + static_cast<size_t>(row) * kv_ld + dc * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+    rv[i][1] = (row + 1 < n_kv)
+                   ? *reinterpret_cast<const u32x4*>(V + static_cast<size_t>(row + 1) * kv_ld + dc * 8)
+                   : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Byte offset inside the V^T tile of the 8-byte granule holding keys
+// [4*gran, 4*gran+4) of row d.
+__device__ __forceinline__ int vt_granule_offset(int d, int gran) {
+  return d * (kBKV * 2) + ((gran ^ ((d >> 1) & 15)) << 3);
+}
+
+template <int D>
+__device__ __forceinline__ void store_kv(uint16_t* __restrict__ stage, const u32x4 (&rk)[D / 32],
+                                         const u32x4 (&rv)[D / 64][2]) {
+  const int tid = threadIdx.x;
+  uint16_t* ks = stage;
+  unsigned char* vt = reinterpret_cast<unsigned char*>(stage + AttnLds<D>::kKElems);
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int c = tid + i * kAttnThreads;
+    const int key = c / (D / 8);
+    const int dc = c % (D / 8);
+    *reinterpret_cast<u32x4*>(ks + key * AttnLds<D>::kKRow + dc * 8) = rk[i];
+  }
+  const int flip = (tid >> 5) & 1;  // half-waves write rows of opposite parity
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    const int c = tid + i * kAttnThreads;
+    const int kp = c & 31;
+    const int dc = c >> 5;
+    const u32x4 a = rv[i][0];  // 8 bf16 of key 2kp   (element e in word e/2, half e%2)
+    const u32x4 b = rv[i][1];  // 8 bf16 of key 2kp+1
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // Elements 2w and 2w+1; half-waves with flip set write them in swapped order.
+      const uint32_t a_lo = a[w] & 0xffffu, a_hi = a[w] >> 16;
+      const uint32_t b_lo = b[w] & 0xffffu, b_hi = b[w] >> 16;
+      const uint32_t first = flip ? (a_hi | (b_hi << 16)) : (a_lo | (b_lo << 16));
+      const uint32_t second = flip ? (a_lo | (b_lo << 16)) : (a_hi | (b_hi << 16));
+      const int d0 = dc * 8 + 2 * w + flip;
+      const int d1 = dc * 8 + 2 * w + (flip ^ 1);
+      *reinterpret_cast<uint32_t*>(vt + vt_granule_offset(d0, kp >> 1) + ((kp & 1) << 2)) = first;
+      *reinterpret_cast<uint32_t*>(vt + vt_granule_offset(d1, kp >> 1) + ((kp & 1) << 2)) = second;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 2)
+void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                          const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_dev, int n_q_max,
+                          int n_kv, int Hq, int Hkv, float c_log2, int64_t q_bs, int64_t kv_bs, int64_t o_bs) {
+  using L = AttnLds<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[L::kTotal];
+
+  int n_q = n_dev ? *n_dev : n_q_max;
+  if (n_q > n_q_max) n_q = n_q_max;
+  if (n_kv < 0) n_kv = n_q;  // keys compacted alongside the queries
+  const int n_qt = (n_q_max + kBQ - 1) / kBQ;
+  const int g = Hq / Hkv;
+  int qt, h;
+  attn_tile_of(blockIdx.x, n_qt, Hkv, g, qt, h);
+  const int q0 = qt * kBQ;
+  if (q0 >= n_q) return;
+  const int kvh = h / g;
+  const int64_t b = blockIdx.y;
+  Q += b * q_bs;
+  O += b * o_bs;
+  K += b * kv_bs + static_cast<int64_t>(kvh) * D;
+  V += b * kv_bs + static_cast<int64_t>(kvh) * D;
+  const int q_ld = Hq * D;
+  const int kv_ld = Hkv * D;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int qrow = q0 + wave * 32 + l32;
+  const int qrow_c = min(qrow, n_q - 1);
+  const int my_pos = q_pos ? q_pos[qrow_c] : qrow_c;
+  const int w_first = min(q0 + wave * 32, n_q - 1);
+  const int w_last = min(q0 + wave * 32 + 31, n_q - 1);
+  const int wave_pmin = q_pos ? q_pos[w_first] : w_first;
+  const int wave_pmax = q_pos ? q_pos[w_last] : w_last;
+  const int b_last = min(q0 + kBQ - 1, n_q - 1);
+  const int block_pmax = q_pos ? q_pos[b_last] : b_last;
+  const int kv_end = min(n_kv, block_pmax + 1);
+  const int n_tiles = (kv_end + kBKV - 1) / kBKV;
+
+  // This lane's query as the B operand of S^T = K Q^T: 8 dims per k-step.
+  bf16x8 qreg[D / 16];
+  {
+    const uint16_t* qp = Q + static_cast<size_t>(qrow_c) * q_ld + h * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  u32x4 rk[D / 32];
+  u32x4 rv[D / 64][2];
+  load_kv<D>(K, V, 0, n_kv, kv_ld, rk, rv);
+  store_kv<D>(lds, rk, rv);
+  if (n_tiles > 1) load_kv<D>(K, V, kBKV, n_kv, kv_ld, rk, rv);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int k0 = j * kBKV;
+    const uint16_t* st = lds + (j & 1) * L::kStage;
+    if (k0 <= wave_pmax) {
+      const uint16_t* ks_lds = st;
+      const unsigned char* vt = reinterpret_cast<const unsigned char*>(st + L::kKElems);
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(ks_lds + (kb * 32 + l32) * L::kKRow + ks * 16 + hi * 8);
+          s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
+        }
+      }
+      if (k0 + kBKV - 1 > wave_pmin) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            if (key > my_pos) s[kb][r] = -__builtin_inff();
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+      const float mc = m_new * c_log2;
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -mc));
+          s[kb][r] = p;
+          psum += p;
+        }
+      l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+#pragma unroll
+      for (int stp = 0; stp < 4; ++stp) {
+        const int kb = stp >> 1;
+        const int sub = stp & 1;
+        u32x4 pw;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pw[t] = pack_bf16x2(s[kb][8 * sub + 2 * t], s[kb][8 * sub + 2 * t + 1]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int d = db * 32 + l32;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + vt_granule_offset(d, 4 * stp + hi));
+          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vt + vt_granule_offset(d, 4 * stp + 2 + hi));
+          const u32x4 av = {lo[0], lo[1], hi2[0], hi2[1]};
+          o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), pb, o[db]);
+        }
+      }
+    }
+    if (j + 1 < n_tiles) store_kv<D>(lds + ((j + 1) & 1) * L::kStage, rk, rv);
+    if (j + 2 < n_tiles) load_kv<D>(K, V, (j + 2) * kBKV, n_kv, kv_ld, rk, rv);
+    __syncthreads();
+  }
+
+  // Normalise and stage the 128 x D output tile through LDS for 16-byte stores.
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.f / l_tot;
+  uint16_t* ot = lds;
+  const int ql = wave * 32 + l32;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = db * 32 + gq * 8 + hi * 4;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[db][gq * 4 + 0] * inv, o[db][gq * 4 + 1] * inv);
+      pk[1] = pack_bf16x2(o[db][gq * 4 + 2] * inv, o[db][gq * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(ot + ql * L::kORow + d) = pk;
+    }
+  __syncthreads();
+  constexpr int kChunks = kBQ * D / 8;
+#pragma unroll
+  for (int i = 0; i < kChunks / kAttnThreads; ++i) {
+    const int c = tid + i * kAttnThreads;
+    const int row = c / (D / 8);
+    const int dc = c % (D / 8);
+    const int q = q0 + row;
+    if (q < n_q)
+      *reinterpret_cast<u32x4*>(O + static_cast<size_t>(q) * q_ld + h * D + dc * 8) =
+          *reinterpret_cast<const u32x4*>(ot + row * L::kORow + dc * 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (small workloads): one wave = 64 queries of one head; K/V tiles
+// of 64 keys in LDS; each lane runs the online softmax over the keys in order.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64)
+void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+                         float* __restrict__ O, const int32_t* __restrict__ q_pos,
+                         const int32_t* __restrict__ n_dev, int n_q_max, int n_kv, int Hq, int Hkv, float scale,
+                         int64_t q_bs, int64_t kv_bs, int64_t o_bs) {
+  __shared__ float ks[64][D];
+  __shared__ float vs[64][D];
+  int n_q = n_dev ? *n_dev : n_q_max;
+  if (n_q > n_q_max) n_q = n_q_max;
+  if (n_kv < 0) n_kv = n_q;  // keys compacted alongside the queries
+  const int q0 = blockIdx.x * 64;
+  if (q0 >= n_q) return;
+  const int h = blockIdx.y;
+  const int kvh = h / (Hq / Hkv);
+  const int64_t b = blockIdx.z;
+  Q += b * q_bs;
+  O += b * o_bs;
+  K += b * kv_bs + static_cast<int64_t>(kvh) * D;
+  V += b * kv_bs + static_cast<int64_t>(kvh) * D;
+  const int q_ld = Hq * D, kv_ld = Hkv * D;
+  const int qi = q0 + threadIdx.x;
+  const int qc = min(qi, n_q - 1);
+  const int my_pos = q_pos ? q_pos[qc] : qc;
+  const int last = min(q0 + 63, n_q - 1);
+  const int pmax = q_pos ? q_pos[last] : last;
+  const int kv_end = min(n_kv, pmax + 1);
+  float q[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) { q[d] = Q[static_cast<size_t>(qc) * q_ld + h * D + d] * scale; acc[d] = 0.f; }
+  float m = -__builtin_inff(), l = 0.f;
+  for (int k0 = 0; k0 < kv_end; k0 += 64) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * D; e += 64) {
+      const int r = e / D, d = e % D;
+      const int row = k0 + r;
+      ks[r][d] = row < n_kv ? K[static_cast<size_t>(row) * kv_ld + d] : 0.f;
+      vs[r][d] = row < n_kv ? V[static_cast<size_t>(row) * kv_ld + d] : 0.f;
+    }
+    __syncthreads();
+    const int kend = min(64, kv_end - k0);
+    for (int r = 0; r < kend; ++r) {
+      if (k0 + r > my_pos) break;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) s = fmaf(q[d], ks[r][d], s);
+      const float mn = fmaxf(m, s);
+      const float a = expf(m - mn);
+      const float p = expf(s - mn);
+      l = l * a + p;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], a, p * vs[r][d]);
+      m = mn;
+    }
+  }
+  if (qi < n_q) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int d = 0; d < D; ++d) O[static_cast<size_t>(qi) * q_ld + h * D + d] = acc[d] * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* K, const void* V, void* O,
+                            const int32_t* q_pos, const int32_t* n_dev, int n_q_max, int n_kv, int Hq, int Hkv,
+                            int64_t q_bs, int64_t kv_bs, int64_t o_bs, hipStream_t stream) {
+  if (n_q_max <= 0 || B <= 0) return hipSuccess;
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  if (dtype == 1) {
+    const int n_qt = (n_q_max + kBQ - 1) / kBQ;
+    const dim3 grid(n_qt * Hq, B);
+    const float c = scale * 1.4426950408889634f;
+    auto q = static_cast<const uint16_t*>(Q);
+    auto k = static_cast<const uint16_t*>(K);
+    auto v = static_cast<const uint16_t*>(V);
+    auto o = static_cast<uint16_t*>(O);
+    if (D == 128)
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
+                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs);
+    else if (D == 64)
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
+                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    const dim3 grid((n_q_max + 63) / 64, Hq, B);
+    auto q = static_cast<const float*>(Q);
+    auto k = static_cast<const float*>(K);
+    auto v = static_cast<const float*>(V);
+    auto o = static_cast<float*>(O);
+    if (D == 128)
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
+                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs);
+    else if (D == 64)
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
+                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs);
+    else if (D == 32)
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
+                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs);
+    else
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dash

@@ -1,0 +1,275 @@
+// C ABI of the DASH prefill path: argument validation, workspace sizing,
+// error reporting and kernel dispatch.  Every entry point validates its
+// arguments with plain host code before any HIP call, so invalid calls
+// enqueue nothing (and can be exercised without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <exception>
+#include <string>
+
+#include "../../include/dash.h"
+#include "dash_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Ctx {
+  int device;
+  int cu_count;
+};
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DASH_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ---- shape checks shared by the attention entry points ---------------------
+int check_shape(const dash_shape* s, bool need_b1) {
+  if (!s) return fail(DASH_E_INVAL, "shape is NULL");
+  if (s->dtype != DASH_F32 && s->dtype != DASH_BF16) return fail(DASH_E_DTYPE, "dtype %d unsupported", s->dtype);
+  if (s->B < 1 || s->S < 1 || s->Hq < 1 || s->Hkv < 1 || s->D < 1 || s->hidden < 1)
+    return fail(DASH_E_SHAPE, "B, S, Hq, Hkv, D and hidden must be >= 1");
+  if (need_b1 && s->B != 1) return fail(DASH_E_SHAPE, "this call supports B == 1 only");
+  if (s->Hq % s->Hkv != 0) return fail(DASH_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", s->Hq, s->Hkv);
+  if (s->S > (1 << 24)) return fail(DASH_E_SHAPE, "S above 2^24 unsupported");
+  if (static_cast<int64_t>(s->B) * s->S > (1ll << 26)) return fail(DASH_E_SHAPE, "B*S above 2^26 unsupported");
+  if (s->Hq > 1024 || s->D > 1024 || s->hidden > (1 << 20)) return fail(DASH_E_SHAPE, "head count or width too large");
+  if (s->dtype == DASH_BF16) {
+    if (s->D != 64 && s->D != 128) return fail(DASH_E_SHAPE, "bf16 path supports D in {64, 128}, got %d", s->D);
+    if (s->hidden % 8 != 0) return fail(DASH_E_SHAPE, "bf16 path needs hidden %% 8 == 0, got %d", s->hidden);
+  } else {
+    if (s->D != 32 && s->D != 64 && s->D != 128)
+      return fail(DASH_E_SHAPE, "fp32 path supports D in {32, 64, 128}, got %d", s->D);
+    if (s->hidden % 4 != 0) return fail(DASH_E_SHAPE, "fp32 path needs hidden %% 4 == 0, got %d", s->hidden);
+  }
+  return DASH_OK;
+}
+
+size_t score_ws_bytes(const dash_shape* s, int64_t rows) {
+  return align_up(static_cast<size_t>(dash::wo_gemm_parts(s->dtype, s->hidden)) * static_cast<size_t>(rows) *
+                  sizeof(float));
+}
+
+int check_ptrs(std::initializer_list<std::pair<const void*, const char*>> ps) {
+  for (auto& p : ps) {
+    if (!p.first) return fail(DASH_E_INVAL, "%s is NULL", p.second);
+    if (!aligned16(p.first)) return fail(DASH_E_ALIGN, "%s is not 16-byte aligned", p.second);
+  }
+  return DASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dash_last_error(void) { return g_last_error.c_str(); }
+
+const char* dash_version(void) { return "dash-mi355x 0.1.0 (gfx950)"; }
+
+int dash_create(void** ctx, int device) {
+  try {
+    if (!ctx) return fail(DASH_E_INVAL, "ctx is NULL");
+    *ctx = nullptr;
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (device < 0 || device >= n) return fail(DASH_E_HIP, "device %d not present (%d devices)", device, n);
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    *ctx = new Ctx{device, cus};
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+void dash_destroy(void* ctx) { delete static_cast<Ctx*>(ctx); }
+
+size_t dash_workspace_size(void* /*ctx*/, int op, const dash_shape* s, int n_max) {
+  try {
+    switch (op) {
+      case DASH_OP_ATTN_LAYER:
+        if (check_shape(s, false) != DASH_OK) return 0;
+        return score_ws_bytes(s, static_cast<int64_t>(s->B) * s->S);
+      case DASH_OP_ATTN_ACTIVE:
+        if (check_shape(s, true) != DASH_OK || n_max < 0) return 0;
+        return score_ws_bytes(s, n_max);
+      case DASH_OP_SELECT:
+        return 0;  // selection keeps its state in LDS
+      default:
+        return 0;
+    }
+  } catch (...) {
+    return 0;
+  }
+}
+
+int dash_attn_layer(void* /*ctx*/, const dash_shape* s, const void* Q, const void* K, const void* V,
+                    const void* Wo, void* O, void* U, float* score, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    rc = check_ptrs({{Q, "Q"}, {K, "K"}, {V, "V"}, {Wo, "Wo"}, {O, "O"}, {U, "U"}});
+    if (rc) return rc;
+    const int64_t rows = static_cast<int64_t>(s->B) * s->S;
+    if (score) {
+      if (!aligned16(score)) return fail(DASH_E_ALIGN, "score is not 16-byte aligned");
+      const size_t need = score_ws_bytes(s, rows);
+      if (!ws || ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+      if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
+    const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
+    hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Q, K, V, O, nullptr, nullptr, s->S, s->S, s->Hq,
+                                          s->Hkv, s->S * qd, s->S * kvd, s->S * qd, st);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    e = dash::launch_wo_gemm(s->dtype, O, Wo, U, score, static_cast<float*>(ws), nullptr, static_cast<int>(rows),
+                             s->hidden, static_cast<int>(qd), st);
+    if (e != hipSuccess) return hip_fail(e, "projection launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int32_t* pos, const int32_t* n_dev,
+                int n_max, int rows, int32_t* idx, int32_t* n_out_dev, float* tau_out, void* /*ws*/,
+                size_t /*ws_bytes*/, void* stream) {
+  try {
+    if (!p) return fail(DASH_E_INVAL, "selection parameters are NULL");
+    if (p->keep_first != 0 || p->keep_last != 0)
+      return fail(DASH_E_INVAL, "keep_first / keep_last are reserved and must be 0");
+    if (n_max < 0 || n_max > (1 << 30)) return fail(DASH_E_INVAL, "n_max %d out of range", n_max);
+    if (rows < 1 || rows > (1 << 20)) return fail(DASH_E_INVAL, "rows %d out of range", rows);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    switch (p->mode) {
+      case DASH_SEL_TOPK: {
+        if (p->k < 0 || p->k > n_max) return fail(DASH_E_INVAL, "k = %d outside [0, %d]", p->k, n_max);
+        if (n_dev) return fail(DASH_E_INVAL, "top-k takes its length from n_max (n_dev must be NULL)");
+        if (pos && rows != 1) return fail(DASH_E_INVAL, "pos is supported for a single row only");
+        if (static_cast<int64_t>(rows) * n_max > (1ll << 31) - 1)
+          return fail(DASH_E_INVAL, "rows * n_max too large");
+        if (p->k == 0) return DASH_OK;
+        if (!score) return fail(DASH_E_INVAL, "score is NULL");
+        if (!idx) return fail(DASH_E_INVAL, "idx is NULL");
+        e = dash::launch_topk(score, rows, n_max, p->k, pos, idx, st);
+        break;
+      }
+      case DASH_SEL_ORDER_STAT: {
+        if (rows != 1) return fail(DASH_E_INVAL, "order statistic supports one row");
+        if (!score || !tau_out) return fail(DASH_E_INVAL, "score and tau_out are required");
+        if (p->rank < 1) return fail(DASH_E_INVAL, "rank must be >= 1");
+        if (!n_dev && p->rank > n_max) return fail(DASH_E_INVAL, "rank %d exceeds n %d", p->rank, n_max);
+        e = dash::launch_order_stat(score, n_dev, n_max, p->rank, tau_out, st);
+        break;
+      }
+      case DASH_SEL_THRESHOLD: {
+        if (rows != 1) return fail(DASH_E_INVAL, "threshold selection supports one row");
+        if (!p->tau || !p->counters) return fail(DASH_E_INVAL, "tau and counters are required");
+        if (p->patience < 1 || p->patience > 255) return fail(DASH_E_INVAL, "patience must be in [1, 255]");
+        if (!idx || !n_out_dev) return fail(DASH_E_INVAL, "idx and n_out_dev are required");
+        if (n_max > 0 && !score) return fail(DASH_E_INVAL, "score is NULL");
+        if (pos && static_cast<const void*>(pos) == static_cast<const void*>(idx))
+          return fail(DASH_E_INVAL, "idx must not alias pos");
+        e = dash::launch_threshold(score, pos, n_dev, n_max, p->tau, p->patience, p->counters, idx, n_out_dev, st);
+        break;
+      }
+      default:
+        return fail(DASH_E_INVAL, "selection mode %d unknown", p->mode);
+    }
+    if (e != hipSuccess) return hip_fail(e, "selection launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_compact(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_max, const void* X, int S,
+                 size_t row_bytes, void* Xa, void* stream) {
+  try {
+    if (n_max < 0) return fail(DASH_E_INVAL, "n_max must be >= 0");
+    if (S < 0) return fail(DASH_E_INVAL, "S must be >= 0");
+    if (row_bytes == 0 || row_bytes % 16 != 0) return fail(DASH_E_ALIGN, "row_bytes must be a positive multiple of 16");
+    if (n_max == 0) return DASH_OK;
+    int rc = check_ptrs({{X, "X"}, {Xa, "Xa"}});
+    if (rc) return rc;
+    if (!idx) return fail(DASH_E_INVAL, "idx is NULL");
+    if (static_cast<uint64_t>(n_max) * (row_bytes / 16) >= (1ull << 31))
+      return fail(DASH_E_INVAL, "n_max * row_bytes too large");
+    hipError_t e = dash::launch_compact(idx, n_dev, n_max, X, S, row_bytes, Xa, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "compaction launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const int32_t* q_pos,
+                     const int32_t* n_dev, int n_max, const void* K, const void* V, int kv_mode, void* Oa,
+                     const void* Wo, void* Ua, float* score, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    if (kv_mode != DASH_KV_ACTIVE && kv_mode != DASH_KV_ALL) return fail(DASH_E_INVAL, "kv_mode %d unknown", kv_mode);
+    if (n_max < 0 || n_max > s->S) return fail(DASH_E_INVAL, "n_max %d outside [0, S=%d]", n_max, s->S);
+    if (n_max == 0) return DASH_OK;
+    rc = check_ptrs({{Qa, "Qa"}, {K, "K"}, {V, "V"}, {Oa, "Oa"}});
+    if (rc) return rc;
+    if (kv_mode == DASH_KV_ALL && !q_pos) return fail(DASH_E_INVAL, "kv_mode ALL needs q_pos");
+    if (Wo) {
+      rc = check_ptrs({{Wo, "Wo"}, {Ua, "Ua"}});
+      if (rc) return rc;
+      if (score) {
+        if (!aligned16(score)) return fail(DASH_E_ALIGN, "score is not 16-byte aligned");
+        const size_t need = score_ws_bytes(s, n_max);
+        if (!ws || ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+        if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
+      }
+    } else if (Ua || score) {
+      return fail(DASH_E_INVAL, "Ua / score need Wo");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
+    const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
+    // ACTIVE: keys are the compacted rows aligned with the queries (their count
+    // follows the query count, -1); ALL: the layer's S rows at their positions.
+    const int n_kv = kv_mode == DASH_KV_ACTIVE ? (n_dev ? -1 : n_max) : s->S;
+    const int32_t* qp = kv_mode == DASH_KV_ALL ? q_pos : nullptr;
+    hipError_t e = dash::launch_attention(s->dtype, 1, s->D, Qa, K, V, Oa, qp, n_dev, n_max, n_kv, s->Hq, s->Hkv,
+                                          0, 0, 0, st);
+    (void)kvd;
+    (void)qd;
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (Wo) {
+      e = dash::launch_wo_gemm(s->dtype, Oa, Wo, Ua, score, static_cast<float*>(ws), n_dev, n_max, s->hidden,
+                               static_cast<int>(qd), st);
+      if (e != hipSuccess) return hip_fail(e, "projection launch");
+    }
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+}  // extern "C"

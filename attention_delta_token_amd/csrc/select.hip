@@ -1,0 +1,274 @@
+// Selection kernels of the DASH prefill path (gfx950).
+//
+// * Top-k:  the k tokens with the largest Δattn score, written in ascending
+//   position order — the single-shot halting decision of the CSDN explainer
+//   "DASH：基于注意力增量的Transformer令牌压缩，实现长序列推理高效加速", §2.3 and
+//   §3.1 step 3 (sort descending, keep the top K; active indices kept sorted,
+//   §3.3).  Equal scores go to the lower position.
+// * Order statistic: the rank-th smallest score, used as the halting
+//   threshold of the selective-halting policy.
+// * Threshold step: consecutive-layer counters and halting, from the forum
+//   summary "DASH：通过注意力动态监测实现长上下文高效预填充", sections
+//   层间更新动态监测 and 选择性停止机制.
+//
+// One workgroup of 1024 threads owns one row of scores.  Scores map to
+// order-preserving 32-bit keys; a three-pass radix select (11, 11 and 10 bits,
+// most significant first) over LDS histograms finds the cut key T and how many
+// keys equal to T must be taken.  A final pass with a workgroup prefix scan of
+// (greater-than-T, equal-to-T) counts emits the survivors in ascending order,
+// so ties resolve to the lower position without any sort.  Everything lives
+// in one launch: no host round trip, no global atomics, deterministic.
+#include "dash_common.h"
+#include "dash_kernels.h"
+
+namespace dash {
+
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kBins = 2048;
+
+// Order-preserving key: larger score -> larger key.  NaN -> 0 (below every
+// number, including -inf whose key is 0x007fffff); -0 and +0 share one key.
+// Integer-only, so the result does not depend on the denormal mode.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  const uint32_t mag = b & 0x7fffffffu;
+  if (mag > 0x7f800000u) return 0u;  // NaN
+  if (mag == 0u) b = 0u;             // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  if (k == 0u) return __uint_as_float(0x7fc00000u);
+  const uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(b);
+}
+
+// Inclusive wave scan (64 lanes) of a 64-bit value.
+__device__ __forceinline__ uint64_t wave_incl_scan(uint64_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint64_t o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive workgroup scan of a 64-bit value; also returns the block total.
+__device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* sh_waves, uint64_t& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const uint64_t incl = wave_incl_scan(v);
+  if (lane == kWave - 1) sh_waves[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    uint64_t w = (lane < kSelWaves) ? sh_waves[lane] : 0ull;
+    const uint64_t wi = wave_incl_scan(w);
+    if (lane < kSelWaves) sh_waves[kSelWaves + lane] = wi - w;  // exclusive wave offsets
+    if (lane == kSelWaves - 1) sh_waves[2 * kSelWaves] = wi;
+  }
+  __syncthreads();
+  const uint64_t res = sh_waves[kSelWaves + wid] + incl - v;
+  total = sh_waves[2 * kSelWaves];
+  __syncthreads();
+  return res;
+}
+
+// Find the key of the kk-th largest (1-based) among `n` keys of `row`.
+// Returns the cut key; *take_eq = how many keys equal to it are ranked within
+// the top kk (the kk - #greater lowest-position ones).
+__device__ uint32_t radix_cut(const float* __restrict__ row, int n, uint32_t kk, uint32_t* hist,
+                              uint64_t* sh_scan, uint32_t* sh_cut, uint32_t* take_eq) {
+  uint32_t prefix = 0u, pmask = 0u;
+  const int shifts[3] = {21, 10, 0};
+  const uint32_t dmask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = shifts[pass];
+    const uint32_t dm = dmask[pass];
+    for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[b] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kSelThreads) {
+      const uint32_t key = score_key(row[i]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
+    }
+    __syncthreads();
+    // Suffix sums over bins (from the top): each thread owns 2 consecutive bins.
+    const int nb = static_cast<int>(dm) + 1;
+    const int b0 = 2 * threadIdx.x;
+    uint32_t c0 = (b0 < nb) ? hist[b0] : 0u;
+    uint32_t c1 = (b0 + 1 < nb) ? hist[b0 + 1] : 0u;
+    uint64_t tot;
+    const uint32_t mine = c0 + c1;
+    // Exclusive prefix over bins below 2t; keys strictly above bin 2t+1 = total - prefix - mine.
+    const uint64_t excl = block_excl_scan(mine, sh_scan, tot);
+    const uint32_t above1 = static_cast<uint32_t>(tot - excl - mine);  // keys in bins > 2t+1
+    const uint32_t above0 = above1 + c1;                               // keys in bins > 2t
+    // The cut bin b satisfies above(b) < kk <= above(b) + hist[b].
+    if (b0 + 1 < nb && above1 < kk && kk <= above1 + c1) {
+      sh_cut[0] = static_cast<uint32_t>(b0 + 1);
+      sh_cut[1] = kk - above1;
+    }
+    if (b0 < nb && above0 < kk && kk <= above0 + c0) {
+      sh_cut[0] = static_cast<uint32_t>(b0);
+      sh_cut[1] = kk - above0;
+    }
+    __syncthreads();
+    const uint32_t bin = sh_cut[0];
+    kk = sh_cut[1];
+    prefix |= bin << sh;
+    pmask |= dm << sh;
+    __syncthreads();
+  }
+  *take_eq = kk;
+  return prefix;
+}
+
+// Emit, in ascending position order, every i with key > cut plus the first
+// `take_eq` positions with key == cut.  out_map != nullptr maps i -> out_map[i].
+__device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut, uint32_t take_eq,
+                              const int32_t* __restrict__ out_map, int32_t* __restrict__ out,
+                              uint64_t* sh_scan) {
+  constexpr int E = 8;  // consecutive elements per thread per chunk
+  uint32_t eq_before = 0u, sel_before = 0u;
+  for (int base = 0; base < n; base += kSelThreads * E) {
+    const int i0 = base + threadIdx.x * E;
+    uint32_t gt = 0u, eq = 0u;
+    uint32_t flags = 0u;  // bit e: gt, bit 8+e: eq
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = i0 + e;
+      if (i < n) {
+        const uint32_t key = score_key(row[i]);
+        if (key > cut) { ++gt; flags |= 1u << e; }
+        else if (key == cut) { ++eq; flags |= 1u << (8 + e); }
+      }
+    }
+    uint64_t tot;
+    const uint64_t mine = (static_cast<uint64_t>(gt) << 32) | eq;
+    const uint64_t excl = block_excl_scan(mine, sh_scan, tot);
+    uint32_t eq_rank = eq_before + static_cast<uint32_t>(excl & 0xffffffffu);
+    const uint32_t gt_rank = static_cast<uint32_t>(excl >> 32);
+    uint32_t eq_taken_before = eq_rank < take_eq ? eq_rank : take_eq;
+    uint32_t o = sel_before + gt_rank + (eq_taken_before - (eq_before < take_eq ? eq_before : take_eq));
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = i0 + e;
+      bool take = false;
+      if (flags & (1u << e)) take = true;
+      else if (flags & (1u << (8 + e))) { take = eq_rank < take_eq; ++eq_rank; }
+      if (take) {
+        out[o] = out_map ? out_map[i] : i;
+        ++o;
+      }
+    }
+    const uint32_t tot_gt = static_cast<uint32_t>(tot >> 32);
+    const uint32_t tot_eq = static_cast<uint32_t>(tot & 0xffffffffu);
+    const uint32_t eq_after = eq_before + tot_eq;
+    const uint32_t took = (eq_after < take_eq ? eq_after : take_eq) - (eq_before < take_eq ? eq_before : take_eq);
+    sel_before += tot_gt + took;
+    eq_before = eq_after;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads, 1)
+void topk_kernel(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ pos,
+                 int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
+  __shared__ uint32_t sh_cut[2];
+  const int row = blockIdx.x;
+  const float* r = score + static_cast<size_t>(row) * n;
+  int32_t* out = idx + static_cast<size_t>(row) * k;
+  if (k == 0) return;
+  uint32_t take_eq;
+  const uint32_t cut = radix_cut(r, n, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
+  emit_selected(r, n, cut, take_eq, pos, out, sh_scan);
+}
+
+__global__ __launch_bounds__(kSelThreads, 1)
+void order_stat_kernel(const float* __restrict__ score, const int32_t* __restrict__ n_dev, int n_max,
+                       int rank, float* __restrict__ tau_out) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
+  __shared__ uint32_t sh_cut[2];
+  int n = n_dev ? *n_dev : n_max;
+  if (n > n_max) n = n_max;
+  if (rank < 1 || rank > n) {
+    if (threadIdx.x == 0) *tau_out = __uint_as_float(0x7fc00000u);
+    return;
+  }
+  uint32_t take_eq;
+  // rank-th smallest == (n - rank + 1)-th largest under the same total order.
+  const uint32_t cut = radix_cut(score, n, static_cast<uint32_t>(n - rank + 1), hist, sh_scan, sh_cut,
+                                 &take_eq);
+  if (threadIdx.x == 0) *tau_out = key_score(cut);
+}
+
+__global__ __launch_bounds__(kSelThreads, 1)
+void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict__ pos,
+                      const int32_t* __restrict__ n_dev, int n_max, const float* __restrict__ tau_p,
+                      int patience, uint8_t* __restrict__ counters, int32_t* __restrict__ out,
+                      int32_t* __restrict__ n_out) {
+  __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
+  int n = n_dev ? *n_dev : n_max;
+  if (n > n_max) n = n_max;
+  if (n < 0) n = 0;
+  const float tau = *tau_p;
+  constexpr int E = 4;
+  uint32_t before = 0u;
+  for (int base = 0; base < n; base += kSelThreads * E) {
+    const int i0 = base + threadIdx.x * E;
+    uint32_t keep_bits = 0u, cnt = 0u;
+    int32_t p[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = i0 + e;
+      p[e] = -1;
+      if (i < n) {
+        const int32_t q = pos ? pos[i] : i;
+        p[e] = q;
+        const uint32_t c = (score[i] < tau) ? static_cast<uint32_t>(counters[q]) + 1u : 0u;
+        counters[q] = static_cast<uint8_t>(c > 255u ? 255u : c);
+        if (c < static_cast<uint32_t>(patience)) { keep_bits |= 1u << e; ++cnt; }
+      }
+    }
+    uint64_t tot;
+    const uint64_t excl = block_excl_scan(cnt, sh_scan, tot);
+    uint32_t o = before + static_cast<uint32_t>(excl);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (keep_bits & (1u << e)) out[o++] = p[e];
+    before += static_cast<uint32_t>(tot);
+  }
+  if (threadIdx.x == 0) *n_out = static_cast<int32_t>(before);
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* score, int rows, int n, int k, const int32_t* pos, int32_t* idx,
+                       hipStream_t stream) {
+  if (rows == 0 || k == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_order_stat(const float* score, const int32_t* n_dev, int n_max, int rank, float* tau_out,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(order_stat_kernel, dim3(1), dim3(kSelThreads), 0, stream, score, n_dev, n_max, rank,
+                     tau_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,
+                            const float* tau, int patience, uint8_t* counters, int32_t* out,
+                            int32_t* n_out, hipStream_t stream) {
+  hipLaunchKernelGGL(threshold_kernel, dim3(1), dim3(kSelThreads), 0, stream, score, pos, n_dev, n_max, tau,
+                     patience, counters, out, n_out);
+  return hipGetLastError();
+}
+
+}  // namespace dash

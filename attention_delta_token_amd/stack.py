@@ -1,0 +1,161 @@
+"""Drivers that chain the four C-ABI calls into the DASH prefill stacks.
+
+Only orchestration lives here (which call, on which buffers, in which
+order); every step runs inside libdash.so.  Buffers are allocated once, up
+front, so a step enqueues kernels only and never synchronises with the host.
+
+* One-shot policy (single-shot halting): layers 0..hl run at full length, the
+  score of layer hl picks the k tokens to keep once, and layers hl+1..L-1 run
+  on that active set — CSDN explainer "DASH：基于注意力增量的Transformer令牌压缩，
+  实现长序列推理高效加速", §2.3 and §3.1.
+* Threshold policy (selective halting): tau is an order statistic of the
+  layer-0 scores; after every layer each active token's consecutive-below-tau
+  counter is updated and tokens reaching `patience` stop being queries while
+  keeping their K/V — forum summary "DASH：通过注意力动态监测实现长上下文高效预填充",
+  sections 层间更新动态监测 and 选择性停止机制.
+* Dense baseline: every layer at full length, no score/select/compact.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class LayerTensors:
+    """One layer's device inputs: Q [S,Hq,D], K and V [S,Hkv,D], Wo [hidden, Hq*D]."""
+    Q: torch.Tensor
+    K: torch.Tensor
+    V: torch.Tensor
+    Wo: torch.Tensor
+
+
+def _shape_of(layer: LayerTensors):
+    S, Hq, D = layer.Q.shape
+    return S, Hq, layer.K.shape[1], D, layer.Wo.shape[0]
+
+
+class OneShotStack:
+    """Layers 0..hl full length, top-k at hl, layers hl+1..L-1 on the kept rows."""
+
+    def __init__(self, layers: list[LayerTensors], halt_layer: int, k: int, kv_mode: int = L.DASH_KV_ACTIVE):
+        self.layers = layers
+        self.hl = halt_layer
+        self.k = k
+        self.kv_mode = kv_mode
+        S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        dev, dt = layers[0].Q.device, layers[0].Q.dtype
+        self.S, self.Hq, self.Hkv, self.D, self.hidden = S, Hq, Hkv, D, hidden
+        self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
+        self.U = torch.empty(S, hidden, device=dev, dtype=dt)
+        self.score = torch.empty(S, device=dev, dtype=torch.float32)
+        self.idx = torch.empty(max(k, 1), device=dev, dtype=torch.int32)
+        self.Qa = torch.empty(max(k, 1), Hq, D, device=dev, dtype=dt)
+        self.Ka = torch.empty(max(k, 1), Hkv, D, device=dev, dtype=dt)
+        self.Va = torch.empty(max(k, 1), Hkv, D, device=dev, dtype=dt)
+        self.Oa = torch.empty(max(k, 1), Hq * D, device=dev, dtype=dt)
+        self.Ua = torch.empty(max(k, 1), hidden, device=dev, dtype=dt)
+        dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
+        self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
+
+    def full_layer(self, l: int, with_score: bool) -> None:
+        x = self.layers[l]
+        L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.score if with_score else None, self.ws)
+
+    def select(self) -> None:
+        L.dash_select(self.score, self.idx, mode=L.DASH_SEL_TOPK, k=self.k)
+
+    def post_layer(self, l: int) -> None:
+        x = self.layers[l]
+        k = self.k
+        if k == 0:
+            return
+        L.dash_compact(self.idx, x.Q, self.Qa, n_max=k)
+        if self.kv_mode == L.DASH_KV_ACTIVE:
+            L.dash_compact(self.idx, x.K, self.Ka, n_max=k)
+            L.dash_compact(self.idx, x.V, self.Va, n_max=k)
+            L.dash_attn_active(self.Qa, self.Ka, self.Va, L.DASH_KV_ACTIVE, self.Oa, n_max=k, Wo=x.Wo,
+                               Ua=self.Ua)
+        else:
+            L.dash_attn_active(self.Qa, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=self.idx, n_max=k, Wo=x.Wo,
+                               Ua=self.Ua, S=self.S)
+
+    def run(self) -> None:
+        for l in range(len(self.layers)):
+            if l <= self.hl:
+                self.full_layer(l, with_score=(l == self.hl))
+                if l == self.hl:
+                    self.select()
+            else:
+                self.post_layer(l)
+
+
+class ThresholdStack:
+    """Layer 0 full length fixes tau (rank-th smallest score); every layer then
+    updates the counters and compacts the surviving queries; keys and values
+    stay full length (halted tokens keep their K/V)."""
+
+    def __init__(self, layers: list[LayerTensors], tau_rank: int, patience: int = 2, record: bool = False):
+        self.layers = layers
+        self.rank = tau_rank
+        self.patience = patience
+        S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        dev, dt = layers[0].Q.device, layers[0].Q.dtype
+        self.S = S
+        self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
+        self.U = torch.empty(S, hidden, device=dev, dtype=dt)
+        self.score = torch.empty(S, device=dev, dtype=torch.float32)
+        self.tau = torch.empty(4, device=dev, dtype=torch.float32)
+        self.counters = torch.zeros(S, device=dev, dtype=torch.uint8)
+        self.pos = [torch.empty(S, device=dev, dtype=torch.int32) for _ in range(2)]
+        self.n = torch.zeros(2, 4, device=dev, dtype=torch.int32)
+        self.Qa = torch.empty(S, Hq, D, device=dev, dtype=dt)
+        self.Oa = torch.empty(S, Hq * D, device=dev, dtype=dt)
+        dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
+        self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
+        self.record = record
+        self.trace = []
+
+    def run(self) -> None:
+        S = self.S
+        self.counters.zero_()
+        x = self.layers[0]
+        L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.score, self.ws)
+        L.dash_select(self.score, mode=L.DASH_SEL_ORDER_STAT, rank=self.rank, n_max=S, tau_out=self.tau)
+        L.dash_select(self.score, self.pos[0], mode=L.DASH_SEL_THRESHOLD, tau=self.tau, patience=self.patience,
+                      counters=self.counters, n_max=S, n_out=self.n[0])
+        if self.record:
+            self.trace.append((None, self.score.clone()))
+        cur = 0
+        for l in range(1, len(self.layers)):
+            x = self.layers[l]
+            pos, n = self.pos[cur], self.n[cur]
+            L.dash_compact(pos, x.Q, self.Qa, n_dev=n, n_max=S)
+            L.dash_attn_active(self.Qa, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=pos, n_dev=n, n_max=S, Wo=x.Wo,
+                               Ua=self.U, score=self.score, ws=self.ws, S=S)
+            if self.record:
+                self.trace.append((pos.clone(), n.clone(), self.score.clone(), self.U.clone()))
+            nxt = cur ^ 1
+            L.dash_select(self.score, self.pos[nxt], mode=L.DASH_SEL_THRESHOLD, tau=self.tau,
+                          patience=self.patience, counters=self.counters, pos=pos, n_dev=n, n_max=S,
+                          n_out=self.n[nxt])
+            cur = nxt
+        self.final = cur
+
+
+class DenseStack:
+    """Every layer at full length (the comparison baseline)."""
+
+    def __init__(self, layers: list[LayerTensors]):
+        self.layers = layers
+        S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        dev, dt = layers[0].Q.device, layers[0].Q.dtype
+        self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
+        self.U = torch.empty(S, hidden, device=dev, dtype=dt)
+
+    def run(self) -> None:
+        for x in self.layers:
+            L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U)

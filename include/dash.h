@@ -1,0 +1,170 @@
+/*
+ * dash.h — C ABI of the DASH (Delta Attention Selective Halting) prefill path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (web pages describing the method, cited by title
+ * and section):
+ *   [P1] "DASH：基于注意力增量的Transformer令牌压缩，实现长序列推理高效加速"
+ *        (CSDN blog explainer): §2.1 Δattn definition, §2.3 single-shot
+ *        decision, §3.1 algorithm steps, §3.2 parameters, §3.3 prefill loop
+ *        sketch, §5.1/§5.2 engineering notes (no host/device syncs, efficient
+ *        gathers).
+ *   [P2] "DASH：通过注意力动态监测实现长上下文高效预填充" (zingnex forum):
+ *        sections 层间更新动态监测 and 选择性停止机制 (threshold halting over
+ *        consecutive layers; halted tokens keep their K/V).
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers, 16-byte aligned, owned by the
+ *     caller.  The library never allocates or frees device memory; scratch
+ *     space comes from the caller's workspace (size from dash_workspace_size).
+ *   - Every call is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) and returns without waiting.  Counts that depend on
+ *     the data stay on the device (n_dev / n_out_dev), so no call performs a
+ *     hidden host<->device synchronisation.
+ *   - Arguments are validated before anything is enqueued.  An invalid call
+ *     returns a nonzero dash_status, enqueues nothing, and leaves a message
+ *     readable through dash_last_error().  A failed launch returns DASH_E_HIP.
+ *     Faults during execution surface at the caller's next synchronisation.
+ *     No C++ exception crosses this boundary.
+ *   - `ctx` may be NULL (the current HIP device is used).
+ *   - Layouts are dense and row-major:
+ *       Q  [B, S, Hq,  D]      K, V [B, S, Hkv, D]   (token-major)
+ *       O  [B, S, Hq*D]        (head h in columns h*D .. h*D+D-1)
+ *       Wo [hidden, Hq*D]      out-major, like a linear layer's weight:
+ *                              U[t][c] = sum_e O[t][e] * Wo[c][e]
+ *       U  [B, S, hidden]      score [B, S] fp32
+ *     Element type of Q, K, V, O, Wo and U is `dtype` (fp32 or bf16);
+ *     arithmetic accumulates in fp32.
+ *   - q-head h reads kv-head h / (Hq / Hkv); softmax scale is 1/sqrt(D).
+ */
+#ifndef DASH_H
+#define DASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_E_INVAL = 1,      /* null pointer, bad enum, out-of-range count */
+  DASH_E_SHAPE = 2,      /* inconsistent or unsupported shape */
+  DASH_E_DTYPE = 3,      /* unsupported element type for this call */
+  DASH_E_ALIGN = 4,      /* pointer or row size not 16-byte aligned */
+  DASH_E_WORKSPACE = 5,  /* workspace missing or too small */
+  DASH_E_HIP = 6         /* HIP runtime error (launch, device query) */
+} dash_status;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+typedef enum { DASH_KV_ACTIVE = 0, DASH_KV_ALL = 1 } dash_kv_mode;
+typedef enum { DASH_SEL_TOPK = 0, DASH_SEL_THRESHOLD = 1, DASH_SEL_ORDER_STAT = 2 } dash_sel_mode;
+typedef enum { DASH_OP_ATTN_LAYER = 0, DASH_OP_SELECT = 1, DASH_OP_ATTN_ACTIVE = 2 } dash_op;
+
+/* Problem shape.  hidden is the width of U; Hq*D is the width of O. */
+typedef struct {
+  int B, S, Hq, Hkv, D, hidden;
+  int dtype; /* dash_dtype */
+} dash_shape;
+
+/* Selection parameters.
+ *   TOPK:        k kept per row.
+ *   ORDER_STAT:  rank (1-based) of the order statistic among ascending scores.
+ *   THRESHOLD:   tau (DEVICE pointer to one float), patience (consecutive
+ *                layers below tau before a token halts), counters (DEVICE
+ *                uint8 array indexed by original position, length >= every
+ *                position that appears).
+ *   keep_first / keep_last: forced retention of the first / last tokens; must
+ *                be 0 (reserved). */
+typedef struct {
+  int mode; /* dash_sel_mode */
+  int k;
+  int rank;
+  const float* tau;
+  int patience;
+  uint8_t* counters;
+  int keep_first, keep_last;
+} dash_sel;
+
+/* Library context: remembers the device and its compute-unit count.
+ * dash_create returns DASH_E_HIP when no device is usable. */
+int dash_create(void** ctx, int device);
+void dash_destroy(void* ctx);
+
+/* Message of the last failed call on this host thread (library-owned). */
+const char* dash_last_error(void);
+
+/* Library version string. */
+const char* dash_version(void);
+
+/* Workspace bytes needed by `op` (dash_op) for shape s with up to n_max rows
+ * (n_max is the sequence length for DASH_OP_ATTN_LAYER and the row capacity
+ * for the others; for DASH_OP_SELECT the shape's B is the number of rows of
+ * scores).  Returns 0 for an invalid request. */
+size_t dash_workspace_size(void* ctx, int op, const dash_shape* s, int n_max);
+
+/* a1 + a2: one full-length layer ([P1] §2.1, §3.1 steps 1-2).
+ *   O = causal GQA softmax attention of Q, K, V          [B, S, Hq*D]
+ *   U = O · Wo^T                                         [B, S, hidden]
+ *   score[t] = ||U_t||_2 (fp32), taken from the fp32 accumulators before U is
+ *   rounded to dtype.  score == NULL skips the score.
+ * Supported: dtype bf16 with D in {64, 128}; dtype fp32 with D <= 128 and
+ * D % 4 == 0 (reference-speed kernels).  hidden % 4 == 0; Hq % Hkv == 0.
+ * Workspace: dash_workspace_size(DASH_OP_ATTN_LAYER, s, S). */
+int dash_attn_layer(void* ctx, const dash_shape* s,
+                    const void* Q, const void* K, const void* V, const void* Wo,
+                    void* O, void* U, float* score,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* a3 / a3': selection ([P1] §2.3 and §3.1 step 3; [P2] 层间更新动态监测).
+ *   TOPK:       score [rows, n_max] → idx [rows, k]: the k positions with the
+ *               largest score, ties to the lower position, NaN below every
+ *               number, -0 == +0, written in ascending order.  If pos != NULL
+ *               (rows == 1 only) the kept entries are pos[i] instead of i.
+ *               n_dev must be NULL (n = n_max).
+ *   ORDER_STAT: rows == 1; n = *n_dev (or n_max); *tau_out (device) = the
+ *               rank-th smallest of score[0..n) under the same order (NaN
+ *               lowest), a zero returned as +0.  rank <= n is required when n
+ *               comes from the device; otherwise tau_out is set to NaN.
+ *   THRESHOLD:  rows == 1; n = *n_dev (or n_max); row i belongs to position
+ *               p = pos[i] (pos == NULL ⇒ p = i; pos ascending).  For each row:
+ *               counters[p] = score[i] < *tau ? counters[p] + 1 : 0 and the row
+ *               stays active iff counters[p] < patience.  Surviving positions
+ *               are written ascending to idx (capacity n_max) and their number
+ *               to *n_out_dev (device int).  idx must not alias pos.
+ * Workspace: dash_workspace_size(DASH_OP_SELECT, {B = rows, ...}, n_max). */
+int dash_select(void* ctx, const dash_sel* p, const float* score, const int32_t* pos,
+                const int32_t* n_dev, int n_max, int rows,
+                int32_t* idx, int32_t* n_out_dev, float* tau_out,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* a4: compaction ([P1] §3.1 step 4, §3.3): Xa[r, :] = X[idx[r], :] for
+ * r < n, n = *n_dev (or n_max).  X has S rows of row_bytes bytes (a multiple
+ * of 16).  A row whose idx[r] lies outside [0, S) is not copied (its Xa row is
+ * left as it was).  Rows of Xa at or beyond n are left untouched.  No
+ * workspace. */
+int dash_compact(void* ctx, const int32_t* idx, const int32_t* n_dev, int n_max,
+                 const void* X, int S, size_t row_bytes, void* Xa, void* stream);
+
+/* a5: post-halt attention ([P1] §3.1 step 4 and §5.1; [P2] 选择性停止机制).
+ *   Qa [n, Hq, D] are the active queries (n = *n_dev or n_max, s->B == 1),
+ *   q_pos [n] their ascending original positions.
+ *   DASH_KV_ACTIVE: K, V are [n, Hkv, D], compacted at the same positions
+ *     (pruned tokens left the KV cache); q_pos may be NULL.
+ *   DASH_KV_ALL: K, V are the full [S, Hkv, D] of this layer (halted tokens
+ *     keep their K/V); q_pos is required.
+ *   Key r is visible to query i iff pos(r) <= q_pos[i].
+ *   Oa [n, Hq*D].  If Wo != NULL: Ua = Oa · Wo^T [n, hidden], and score[i] =
+ *   ||Ua_i||_2 when score != NULL.  Rows at or beyond n are left untouched.
+ * Workspace: dash_workspace_size(DASH_OP_ATTN_ACTIVE, s, n_max). */
+int dash_attn_active(void* ctx, const dash_shape* s, const void* Qa, const int32_t* q_pos,
+                     const int32_t* n_dev, int n_max, const void* K, const void* V, int kv_mode,
+                     void* Oa, const void* Wo, void* Ua, float* score,
+                     void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H */

@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every symbol include/dash.h declares, and
+rejects invalid arguments before touching the GPU.  CPU only: no call here
+reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_delta_token_amd as dash
+from attention_delta_token_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dash.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dash.LIB_PATH):
+        pytest.fail("libdash.so is not built (run __graft_entry__.build())")
+    return dash.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dash_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("dash_attn_layer", "dash_select", "dash_compact", "dash_attn_active"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    assert "gfx950" in dash.version()
+
+
+def _shape(**kw):
+    d = dict(B=1, S=64, Hq=4, Hkv=2, D=128, hidden=512, dtype=L.DASH_BF16)
+    d.update(kw)
+    return L.DashShape(d["B"], d["S"], d["Hq"], d["Hkv"], d["D"], d["hidden"], d["dtype"])
+
+
+def _last(lib):
+    return lib.dash_last_error().decode()
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def test_attn_layer_validation(lib):
+    f = lib.dash_attn_layer
+    p = [FAKE] * 6
+    assert f(None, None, *p, None, None, 0, None) == L.DASH_E_INVAL
+    assert f(None, ctypes.byref(_shape(Hq=6, Hkv=4)), *p, None, None, 0, None) == L.DASH_E_SHAPE
+    assert "multiple" in _last(lib)
+    assert f(None, ctypes.byref(_shape(D=96)), *p, None, None, 0, None) == L.DASH_E_SHAPE
+    assert f(None, ctypes.byref(_shape(dtype=7)), *p, None, None, 0, None) == L.DASH_E_DTYPE
+    assert f(None, ctypes.byref(_shape(S=0)), *p, None, None, 0, None) == L.DASH_E_SHAPE
+    assert f(None, ctypes.byref(_shape()), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
+    assert "Q is NULL" in _last(lib)
+    assert f(None, ctypes.byref(_shape()), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == L.DASH_E_ALIGN
+    # score requested with a missing or short workspace
+    assert f(None, ctypes.byref(_shape()), *p, FAKE, None, 0, None) == L.DASH_E_WORKSPACE
+    need = lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(_shape()), 64)
+    assert need >= 64 * 4 * 4  # 4 column tiles of 128 for hidden 512
+    assert f(None, ctypes.byref(_shape()), *p, FAKE, FAKE, need - 1, None) == L.DASH_E_WORKSPACE
+
+
+def test_select_validation(lib):
+    f = lib.dash_select
+    sel = L.DashSel(L.DASH_SEL_TOPK, 5, 0, None, 2, None, 0, 0)
+    assert f(None, None, FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    assert f(None, ctypes.byref(sel), FAKE, None, None, 4, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    assert "outside" in _last(lib)
+    assert f(None, ctypes.byref(sel), FAKE, None, FAKE, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    assert f(None, ctypes.byref(sel), FAKE, FAKE, None, 10, 2, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    assert f(None, ctypes.byref(sel), None, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    sel0 = L.DashSel(L.DASH_SEL_TOPK, 0, 0, None, 2, None, 0, 0)
+    assert f(None, ctypes.byref(sel0), None, None, None, 10, 1, None, None, None, None, 0, None) == L.DASH_OK
+    forced = L.DashSel(L.DASH_SEL_TOPK, 5, 0, None, 2, None, 64, 0)
+    assert f(None, ctypes.byref(forced), FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    os_ = L.DashSel(L.DASH_SEL_ORDER_STAT, 0, 11, None, 2, None, 0, 0)
+    assert f(None, ctypes.byref(os_), FAKE, None, None, 10, 1, None, None, FAKE, None, 0, None) == L.DASH_E_INVAL
+    th = L.DashSel(L.DASH_SEL_THRESHOLD, 0, 0, FAKE, 0, FAKE, 0, 0)
+    assert f(None, ctypes.byref(th), FAKE, None, None, 10, 1, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
+    th = L.DashSel(L.DASH_SEL_THRESHOLD, 0, 0, FAKE, 2, FAKE, 0, 0)
+    assert f(None, ctypes.byref(th), FAKE, FAKE, None, 10, 1, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
+    assert "alias" in _last(lib)
+    bad = L.DashSel(9, 0, 0, None, 2, None, 0, 0)
+    assert f(None, ctypes.byref(bad), FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+
+
+def test_compact_validation(lib):
+    f = lib.dash_compact
+    assert f(None, FAKE, None, 10, FAKE, 10, 24, FAKE, None) == L.DASH_E_ALIGN
+    assert f(None, FAKE, None, 10, FAKE, 10, 0, FAKE, None) == L.DASH_E_ALIGN
+    assert f(None, None, None, 10, FAKE, 10, 32, FAKE, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, None, -1, FAKE, 10, 32, FAKE, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, None, 10, FAKE + 8, 10, 32, FAKE, None) == L.DASH_E_ALIGN
+    assert f(None, FAKE, None, 0, None, 10, 32, None, None) == L.DASH_OK  # nothing to do
+
+
+def test_attn_active_validation(lib):
+    f = lib.dash_attn_active
+    s = _shape()
+    args = lambda **kw: dict(dict(Qa=FAKE, q_pos=None, n_dev=None, n_max=32, K=FAKE, V=FAKE, mode=L.DASH_KV_ACTIVE,
+                                  Oa=FAKE, Wo=None, Ua=None, score=None, ws=None, wsb=0), **kw)
+    call = lambda shape, a: f(None, ctypes.byref(shape), a["Qa"], a["q_pos"], a["n_dev"], a["n_max"], a["K"], a["V"],
+                               a["mode"], a["Oa"], a["Wo"], a["Ua"], a["score"], a["ws"], a["wsb"], None)
+    assert call(_shape(B=2), args()) == L.DASH_E_SHAPE
+    assert call(s, args(mode=5)) == L.DASH_E_INVAL
+    assert call(s, args(n_max=65)) == L.DASH_E_INVAL
+    assert call(s, args(mode=L.DASH_KV_ALL)) == L.DASH_E_INVAL
+    assert "q_pos" in _last(lib)
+    assert call(s, args(Ua=FAKE)) == L.DASH_E_INVAL
+    assert call(s, args(Wo=FAKE, Ua=FAKE, score=FAKE)) == L.DASH_E_WORKSPACE
+    assert call(s, args(Qa=None)) == L.DASH_E_INVAL
+    assert call(s, args(n_max=0, Qa=None)) == L.DASH_OK
+
+
+def test_workspace_size(lib):
+    s = _shape(hidden=3584, S=8192, Hq=28, Hkv=4)
+    n = lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(s), 8192)
+    assert n >= 28 * 8192 * 4
+    assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(s), 8192) == 0
+    assert lib.dash_workspace_size(None, 17, ctypes.byref(s), 8192) == 0
+    assert lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(_shape(D=33)), 8192) == 0
