@@ -8,5 +8,5 @@ from ._lib import (  # noqa: F401
     DASH_BF16, DASH_F32, DASH_KV_ACTIVE, DASH_KV_ALL, DASH_OP_ATTN_ACTIVE, DASH_OP_ATTN_LAYER, DASH_OP_SELECT,
     DASH_SEL_ORDER_STAT, DASH_SEL_THRESHOLD, DASH_SEL_TOPK, DashError, EXPORTED, LIB_PATH,
     dash_attn_active, dash_attn_layer, dash_compact, dash_select, dash_workspace_size, load, make_shape, version,
-    workspace,
+    workspace, trace_start, trace_stop, trace_read,
 )

@@ -23,7 +23,9 @@ DASH_SEL_TOPK, DASH_SEL_THRESHOLD, DASH_SEL_ORDER_STAT = 0, 1, 2
 DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE = 0, 1, 2
 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
-            "dash_attn_layer", "dash_select", "dash_compact", "dash_attn_active")
+            "dash_attn_layer", "dash_select", "dash_compact", "dash_attn_active",
+            "dash_trace_start", "dash_trace_stop", "dash_trace_read")
+TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact")
 
 
 class DashShape(Structure):
@@ -76,6 +78,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]
     lib.dash_attn_active.restype = c_int
+    lib.dash_trace_start.argtypes = [c_int]
+    lib.dash_trace_start.restype = c_int
+    lib.dash_trace_stop.argtypes = []
+    lib.dash_trace_stop.restype = c_int
+    lib.dash_trace_read.argtypes = [POINTER(c_int), POINTER(ctypes.c_float), c_int, POINTER(c_int)]
+    lib.dash_trace_read.restype = c_int
     _lib = lib
     return lib
 
@@ -176,3 +184,21 @@ def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: 
     _check(load().dash_attn_active(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(n_dev), n_max, _ptr(K),
                                    _ptr(V), kv_mode, _ptr(Oa), _ptr(Wo), _ptr(Ua), _ptr(score), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def trace_start(capacity: int) -> None:
+    """Start bracketing every library launch with HIP events (measurement only)."""
+    _check(load().dash_trace_start(capacity))
+
+
+def trace_stop() -> None:
+    _check(load().dash_trace_stop())
+
+
+def trace_read(max_records: int = 1 << 16) -> list[tuple[str, float]]:
+    """Wait for the recorded events; return [(op name, milliseconds)] in launch order."""
+    ops = (c_int * max_records)()
+    ms = (ctypes.c_float * max_records)()
+    n = c_int(0)
+    _check(load().dash_trace_read(ops, ms, max_records, ctypes.byref(n)))
+    return [(TRACE_OPS[ops[i]], float(ms[i])) for i in range(n.value)]

@@ -8,7 +8,9 @@
 #include <cstdint>
 #include <cstdio>
 #include <exception>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/dash.h"
 #include "dash_kernels.h"
@@ -76,9 +78,88 @@ int check_ptrs(std::initializer_list<std::pair<const void*, const char*>> ps) {
   return DASH_OK;
 }
 
+// ---- launch tracing ----------------------------------------------------------
+std::mutex g_tr_mu;
+std::vector<hipEvent_t> g_tr_ev;  // 2 per record
+std::vector<int> g_tr_op;
+int g_tr_n = 0;
+bool g_tr_on = false;
+
+void trace_release() {
+  for (hipEvent_t e : g_tr_ev) (void)hipEventDestroy(e);
+  g_tr_ev.clear();
+  g_tr_op.clear();
+  g_tr_n = 0;
+}
+
+// Records the opening event of a traced kernel group; returns its slot or -1.
+int trace_open(int op, hipStream_t st) {
+  if (!g_tr_on) return -1;
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  if (!g_tr_on || g_tr_n >= static_cast<int>(g_tr_op.size())) return -1;
+  const int slot = g_tr_n++;
+  g_tr_op[slot] = op;
+  (void)hipEventRecord(g_tr_ev[2 * slot], st);
+  return slot;
+}
+
+void trace_close(int slot, hipStream_t st) {
+  if (slot >= 0) (void)hipEventRecord(g_tr_ev[2 * slot + 1], st);
+}
+
 }  // namespace
 
 extern "C" {
+
+int dash_trace_start(int capacity) {
+  try {
+    if (capacity < 1 || capacity > (1 << 20)) return fail(DASH_E_INVAL, "trace capacity %d out of range", capacity);
+    std::lock_guard<std::mutex> lk(g_tr_mu);
+    g_tr_on = false;
+    trace_release();
+    g_tr_ev.resize(2 * static_cast<size_t>(capacity));
+    for (size_t i = 0; i < g_tr_ev.size(); ++i) {
+      hipError_t e = hipEventCreate(&g_tr_ev[i]);
+      if (e != hipSuccess) {
+        g_tr_ev.resize(i);
+        trace_release();
+        return hip_fail(e, "hipEventCreate");
+      }
+    }
+    g_tr_op.assign(static_cast<size_t>(capacity), -1);
+    g_tr_on = true;
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_trace_stop(void) {
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  g_tr_on = false;
+  return DASH_OK;
+}
+
+int dash_trace_read(int* ops, float* ms, int max, int* n) {
+  try {
+    if (!n || max < 0 || (max > 0 && (!ops || !ms))) return fail(DASH_E_INVAL, "bad trace_read arguments");
+    std::lock_guard<std::mutex> lk(g_tr_mu);
+    const int m = g_tr_n < max ? g_tr_n : max;
+    for (int i = 0; i < m; ++i) {
+      hipError_t e = hipEventSynchronize(g_tr_ev[2 * i + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, g_tr_ev[2 * i], g_tr_ev[2 * i + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      ops[i] = g_tr_op[i];
+      ms[i] = t;
+    }
+    *n = m;
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
 
 const char* dash_last_error(void) { return g_last_error.c_str(); }
 
@@ -140,11 +221,15 @@ int dash_attn_layer(void* /*ctx*/, const dash_shape* s, const void* Q, const voi
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
     const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
+    int tr = trace_open(DASH_TR_ATTN_LAYER, st);
     hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Q, K, V, O, nullptr, nullptr, s->S, s->S, s->Hq,
                                           s->Hkv, s->S * qd, s->S * kvd, s->S * qd, st);
+    trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
+    tr = trace_open(DASH_TR_PROJ_LAYER, st);
     e = dash::launch_wo_gemm(s->dtype, O, Wo, U, score, static_cast<float*>(ws), nullptr, static_cast<int>(rows),
                              s->hidden, static_cast<int>(qd), st);
+    trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "projection launch");
     return DASH_OK;
   } catch (...) {
@@ -163,6 +248,7 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
     if (rows < 1 || rows > (1 << 20)) return fail(DASH_E_INVAL, "rows %d out of range", rows);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+    int tr = -1;
     switch (p->mode) {
       case DASH_SEL_TOPK: {
         if (p->k < 0 || p->k > n_max) return fail(DASH_E_INVAL, "k = %d outside [0, %d]", p->k, n_max);
@@ -173,6 +259,7 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
         if (p->k == 0) return DASH_OK;
         if (!score) return fail(DASH_E_INVAL, "score is NULL");
         if (!idx) return fail(DASH_E_INVAL, "idx is NULL");
+        tr = trace_open(DASH_TR_SELECT, st);
         e = dash::launch_topk(score, rows, n_max, p->k, pos, idx, st);
         break;
       }
@@ -181,6 +268,7 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
         if (!score || !tau_out) return fail(DASH_E_INVAL, "score and tau_out are required");
         if (p->rank < 1) return fail(DASH_E_INVAL, "rank must be >= 1");
         if (!n_dev && p->rank > n_max) return fail(DASH_E_INVAL, "rank %d exceeds n %d", p->rank, n_max);
+        tr = trace_open(DASH_TR_SELECT, st);
         e = dash::launch_order_stat(score, n_dev, n_max, p->rank, tau_out, st);
         break;
       }
@@ -192,12 +280,14 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
         if (n_max > 0 && !score) return fail(DASH_E_INVAL, "score is NULL");
         if (pos && static_cast<const void*>(pos) == static_cast<const void*>(idx))
           return fail(DASH_E_INVAL, "idx must not alias pos");
+        tr = trace_open(DASH_TR_SELECT, st);
         e = dash::launch_threshold(score, pos, n_dev, n_max, p->tau, p->patience, p->counters, idx, n_out_dev, st);
         break;
       }
       default:
         return fail(DASH_E_INVAL, "selection mode %d unknown", p->mode);
     }
+    trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "selection launch");
     return DASH_OK;
   } catch (...) {
@@ -217,7 +307,10 @@ int dash_compact(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_
     if (!idx) return fail(DASH_E_INVAL, "idx is NULL");
     if (static_cast<uint64_t>(n_max) * (row_bytes / 16) >= (1ull << 31))
       return fail(DASH_E_INVAL, "n_max * row_bytes too large");
-    hipError_t e = dash::launch_compact(idx, n_dev, n_max, X, S, row_bytes, Xa, static_cast<hipStream_t>(stream));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int tr = trace_open(DASH_TR_COMPACT, st);
+    hipError_t e = dash::launch_compact(idx, n_dev, n_max, X, S, row_bytes, Xa, st);
+    trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "compaction launch");
     return DASH_OK;
   } catch (...) {
@@ -251,19 +344,20 @@ int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const i
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
-    const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
     // ACTIVE: keys are the compacted rows aligned with the queries (their count
     // follows the query count, -1); ALL: the layer's S rows at their positions.
     const int n_kv = kv_mode == DASH_KV_ACTIVE ? (n_dev ? -1 : n_max) : s->S;
     const int32_t* qp = kv_mode == DASH_KV_ALL ? q_pos : nullptr;
+    int tr = trace_open(DASH_TR_ATTN_ACTIVE, st);
     hipError_t e = dash::launch_attention(s->dtype, 1, s->D, Qa, K, V, Oa, qp, n_dev, n_max, n_kv, s->Hq, s->Hkv,
                                           0, 0, 0, st);
-    (void)kvd;
-    (void)qd;
+    trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (Wo) {
+      tr = trace_open(DASH_TR_PROJ_ACTIVE, st);
       e = dash::launch_wo_gemm(s->dtype, Oa, Wo, Ua, score, static_cast<float*>(ws), n_dev, n_max, s->hidden,
                                static_cast<int>(qd), st);
+      trace_close(tr, st);
       if (e != hipSuccess) return hip_fail(e, "projection launch");
     }
     return DASH_OK;

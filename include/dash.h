@@ -163,6 +163,28 @@ int dash_attn_active(void* ctx, const dash_shape* s, const void* Qa, const int32
                      void* Oa, const void* Wo, void* Ua, float* score,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Launch tracing (measurement support, not on the hot path).
+ * dash_trace_start(capacity) creates 2*capacity HIP events on the current
+ * device and starts recording: every kernel group the library enqueues is
+ * bracketed by an event pair on its launch stream, until `capacity` groups
+ * have been recorded or dash_trace_stop() is called.  dash_trace_read waits
+ * for the recorded events and copies out, for up to `max` groups, the group
+ * kind (dash_trace_op) and its elapsed milliseconds into host arrays; *n gets
+ * the number copied.  Starting again discards earlier records.  Not
+ * thread-safe with concurrent launches from several host threads. */
+typedef enum {
+  DASH_TR_ATTN_LAYER = 0,   /* attention kernel of dash_attn_layer */
+  DASH_TR_PROJ_LAYER = 1,   /* W_o GEMM (+ score finalize) of dash_attn_layer */
+  DASH_TR_ATTN_ACTIVE = 2,  /* attention kernel of dash_attn_active */
+  DASH_TR_PROJ_ACTIVE = 3,  /* W_o GEMM (+ score finalize) of dash_attn_active */
+  DASH_TR_SELECT = 4,       /* selection kernel of dash_select */
+  DASH_TR_COMPACT = 5       /* gather kernel of dash_compact */
+} dash_trace_op;
+
+int dash_trace_start(int capacity);
+int dash_trace_stop(void);
+int dash_trace_read(int* ops, float* ms, int max, int* n);
+
 #ifdef __cplusplus
 }
 #endif
