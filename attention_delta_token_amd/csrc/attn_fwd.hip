@@ -21,9 +21,11 @@
 // one exchange with the partner half-wave.  The output is accumulated
 // transposed too, O^T += V^T · P^T, where P^T is fed straight from the score
 // accumulators (rounded to bf16) as the B operand and V^T is read from an LDS
-// copy of the V tile stored transposed with an XOR swizzle on 8-byte granules
-// (conflict-free operand reads).  K and V tiles are double-buffered in LDS
-// with register prefetch one tile ahead; one barrier per step.  Workgroups
+// copy of the V tile stored transposed, keys permuted within groups of 16 so
+// each MFMA operand is one 16-byte read, rows padded so the reads are free of
+// bank conflicts.  K and V tiles arrive through buffer loads (rows past the
+// key count read as zeros), are double-buffered in LDS with register prefetch
+// one tile ahead, and one barrier separates steps.  Workgroups
 // are ordered heaviest-first (causal work grows with the query position) and
 // the q-heads that share a kv-head are placed on the same XCD so they share
 // its L2.
@@ -63,63 +65,76 @@ __device__ __forceinline__ void attn_tile_of(int bid, int n_qt, int Hkv, int g, 
 
 template <int D>
 struct AttnLds {
-  static constexpr int kKRow = D + 8;                   // padded K row (bf16)
+  static constexpr int kKRow = D + 8;          // padded K row, bf16 elements (272 B for D=128)
   static constexpr int kKElems = kBKV * kKRow;
-  static constexpr int kVtElems = D * kBKV;             // V^T [D][64], swizzled
+  static constexpr int kVtRow = kBKV + 8;      // padded V^T row, bf16 elements (144 B)
+  static constexpr int kVtElems = D * kVtRow;
   static constexpr int kStage = kKElems + kVtElems;
   static constexpr int kTotal = 2 * kStage;
-  static constexpr int kORow = D + 8;                   // output staging row
+  static constexpr int kORow = D + 8;          // output staging row
+};
+
+// Buffer resource over `bytes` bytes from `base`: loads past the end return 0,
+// which is how rows beyond the key count read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Within each group of 16 keys, V^T stores key r at position
+// 8*((r>>2)&1) + 4*(r>>3) + (r&3): the 8 keys one half-wave feeds to a 16-key
+// MFMA step (r = 4h..4h+3 and 8+4h..8+4h+3) are then 16 contiguous bytes.
+__device__ __forceinline__ int vt_dword_of_pair(int kp) {
+  const int r = (2 * kp) & 15;
+  const int p = 8 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+  return (kp >> 3) * 8 + (p >> 1);
+}
+
+// Per-thread global offsets (bytes, relative to the tile's first key row).
+template <int D>
+struct KvLoadPlan {
+  uint32_t k_off[D / 32];
+  uint32_t v_off[D / 64];
+  __device__ __forceinline__ void init(int kv_ld) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int c = tid + i * kAttnThreads;
+      k_off[i] = static_cast<uint32_t>((c / (D / 8)) * kv_ld + (c % (D / 8)) * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+      const int c = tid + i * kAttnThreads;
+      v_off[i] = static_cast<uint32_t>((2 * (c & 31)) * kv_ld + (c >> 5) * 8) * 2u;
+    }
+  }
 };
 
 template <int D>
-__device__ __forceinline__ void load_kv(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                        int k0, int n_kv, int kv_ld, u32x4 (&rk)[D / 32],
-                                        u32x4 (&rv)[D / 64][2]) {
-  const int tid = threadIdx.x;
-  // K: 64 rows x D/8 chunks; thread takes chunks tid + i*256.
+__device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk_src, __amdgpu_buffer_rsrc_t rv_src,
+                                        const KvLoadPlan<D>& pl, uint32_t tile_off, uint32_t row_bytes,
+                                        u32x4 (&rk)[D / 32], u32x4 (&rv)[D / 64][2]) {
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int c = tid + i * kAttnThreads;
-    const int key = c / (D / 8);
-    const int dc = c % (D / 8);
-    const int row = k0 + key;
-    rk[i] = (row < n_kv) ? *reinterpret_cast<const u32x4*>(K + static_cast<size_t>(row) * kv_ld + dc * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-  }
-  // V: pairs of keys x D/8 chunks; item c: key pair c % 32, chunk c / 32.
+  for (int i = 0; i < D / 32; ++i)
+    rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk_src, pl.k_off[i], tile_off, 0);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
-    const int c = tid + i * kAttnThreads;
-    const int kp = c & 31;
-    const int dc = c >> 5;
-    const int row = k0 + 2 * kp;
-    rv[i][0] = (row < n_kv) ? *reinterpret_cast<const u32x4*>(V + static_cast<size_t>(row) * kv_ld + dc * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
-    rv[i][1] = (row + 1 < n_kv)
-                   ? *reinterpret_cast<const u32x4*>(V + static_cast<size_t>(row + 1) * kv_ld + dc * 8)
-                   : u32x4{0u, 0u, 0u, 0u};
+    rv[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rv_src, pl.v_off[i], tile_off, 0);
+    rv[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rv_src, pl.v_off[i] + row_bytes, tile_off, 0);
   }
-}
-
-// Byte offset inside the V^T tile of the 8-byte granule holding keys
-// [4*gran, 4*gran+4) of row d.
-__device__ __forceinline__ int vt_granule_offset(int d, int gran) {
-  return d * (kBKV * 2) + ((gran ^ ((d >> 1) & 15)) << 3);
 }
 
 template <int D>
 __device__ __forceinline__ void store_kv(uint16_t* __restrict__ stage, const u32x4 (&rk)[D / 32],
                                          const u32x4 (&rv)[D / 64][2]) {
+  using L = AttnLds<D>;
   const int tid = threadIdx.x;
-  uint16_t* ks = stage;
-  unsigned char* vt = reinterpret_cast<unsigned char*>(stage + AttnLds<D>::kKElems);
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     const int c = tid + i * kAttnThreads;
-    const int key = c / (D / 8);
-    const int dc = c % (D / 8);
-    *reinterpret_cast<u32x4*>(ks + key * AttnLds<D>::kKRow + dc * 8) = rk[i];
+    *reinterpret_cast<u32x4*>(stage + (c / (D / 8)) * L::kKRow + (c % (D / 8)) * 8) = rk[i];
   }
+  uint32_t* vt = reinterpret_cast<uint32_t*>(stage + L::kKElems);
   const int flip = (tid >> 5) & 1;  // half-waves write rows of opposite parity
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
@@ -128,17 +143,14 @@ __device__ __forceinline__ void store_kv(uint16_t* __restrict__ stage, const u32
     const int dc = c >> 5;
     const u32x4 a = rv[i][0];  // 8 bf16 of key 2kp   (element e in word e/2, half e%2)
     const u32x4 b = rv[i][1];  // 8 bf16 of key 2kp+1
+    uint32_t* col = vt + dc * 8 * (L::kVtRow / 2) + vt_dword_of_pair(kp);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      // Elements 2w and 2w+1; half-waves with flip set write them in swapped order.
-      const uint32_t a_lo = a[w] & 0xffffu, a_hi = a[w] >> 16;
-      const uint32_t b_lo = b[w] & 0xffffu, b_hi = b[w] >> 16;
-      const uint32_t first = flip ? (a_hi | (b_hi << 16)) : (a_lo | (b_lo << 16));
-      const uint32_t second = flip ? (a_lo | (b_lo << 16)) : (a_hi | (b_hi << 16));
-      const int d0 = dc * 8 + 2 * w + flip;
-      const int d1 = dc * 8 + 2 * w + (flip ^ 1);
-      *reinterpret_cast<uint32_t*>(vt + vt_granule_offset(d0, kp >> 1) + ((kp & 1) << 2)) = first;
-      *reinterpret_cast<uint32_t*>(vt + vt_granule_offset(d1, kp >> 1) + ((kp & 1) << 2)) = second;
+      const uint32_t lo = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);  // (a.lo, b.lo)
+      const uint32_t hi = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);  // (a.hi, b.hi)
+      const int e0 = 2 * w + flip, e1 = 2 * w + (flip ^ 1);
+      col[e0 * (L::kVtRow / 2)] = flip ? hi : lo;
+      col[e1 * (L::kVtRow / 2)] = flip ? lo : hi;
     }
   }
 }
@@ -169,6 +181,11 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   V += b * kv_bs + static_cast<int64_t>(kvh) * D;
   const int q_ld = Hq * D;
   const int kv_ld = Hkv * D;
+  const uint32_t row_bytes = static_cast<uint32_t>(kv_ld) * 2u;
+  // bytes from this kv-head's first element to the end of the last key row
+  const uint32_t kv_bytes = n_kv > 0 ? static_cast<uint32_t>(n_kv - 1) * row_bytes + D * 2u : 0u;
+  const __amdgpu_buffer_rsrc_t k_src = make_rsrc(K, kv_bytes);
+  const __amdgpu_buffer_rsrc_t v_src = make_rsrc(V, kv_bytes);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -204,19 +221,28 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
+  KvLoadPlan<D> plan;
+  plan.init(kv_ld);
+  const uint32_t tile_bytes = static_cast<uint32_t>(kBKV) * row_bytes;
   u32x4 rk[D / 32];
   u32x4 rv[D / 64][2];
-  load_kv<D>(K, V, 0, n_kv, kv_ld, rk, rv);
+  load_kv<D>(k_src, v_src, plan, 0u, row_bytes, rk, rv);
   store_kv<D>(lds, rk, rv);
-  if (n_tiles > 1) load_kv<D>(K, V, kBKV, n_kv, kv_ld, rk, rv);
+  // Drain every outstanding global load (the query registers included) before
+  // the loop, so the only loads in flight inside it are the tile prefetches and
+  // no wait for them lands ahead of the score MFMAs.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (n_tiles > 1) load_kv<D>(k_src, v_src, plan, tile_bytes, row_bytes, rk, rv);
   __syncthreads();
+
+  // LDS operand addresses (bytes) for this lane; per-step offsets are immediates.
+  const int k_lane = (l32 * L::kKRow + hi * 8) * 2;
+  const int vt_lane = (l32 * L::kVtRow + hi * 8) * 2 + L::kKElems * 2;
 
   for (int j = 0; j < n_tiles; ++j) {
     const int k0 = j * kBKV;
-    const uint16_t* st = lds + (j & 1) * L::kStage;
+    const unsigned char* st = reinterpret_cast<const unsigned char*>(lds + (j & 1) * L::kStage);
     if (k0 <= wave_pmax) {
-      const uint16_t* ks_lds = st;
-      const unsigned char* vt = reinterpret_cast<const unsigned char*>(st + L::kKElems);
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -227,7 +253,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(ks_lds + (kb * 32 + l32) * L::kKRow + ks * 16 + hi * 8);
+              *reinterpret_cast<const bf16x8*>(st + k_lane + (kb * 32 * L::kKRow + ks * 16) * 2);
           s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
         }
       }
@@ -237,7 +263,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            if (key > my_pos) s[kb][r] = -__builtin_inff();
+            s[kb][r] = key > my_pos ? -__builtin_inff() : s[kb][r];
           }
       }
       float mx = s[0][0];
@@ -260,10 +286,13 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
           psum += p;
         }
       l_run = fmaf(l_run, alpha, psum);
+      // Rescale the accumulators only when some query of the wave saw a new maximum.
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i)
+        for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
 #pragma unroll
       for (int stp = 0; stp < 4; ++stp) {
         const int kb = stp >> 1;
@@ -274,16 +303,15 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const int d = db * 32 + l32;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + vt_granule_offset(d, 4 * stp + hi));
-          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vt + vt_granule_offset(d, 4 * stp + 2 + hi));
-          const u32x4 av = {lo[0], lo[1], hi2[0], hi2[1]};
-          o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), pb, o[db]);
+          const bf16x8 av =
+              *reinterpret_cast<const bf16x8*>(st + vt_lane + (db * 32 * L::kVtRow + stp * 16) * 2);
+          o[db] = mfma32x32x16(av, pb, o[db]);
         }
       }
     }
     if (j + 1 < n_tiles) store_kv<D>(lds + ((j + 1) & 1) * L::kStage, rk, rv);
-    if (j + 2 < n_tiles) load_kv<D>(K, V, (j + 2) * kBKV, n_kv, kv_ld, rk, rv);
+    if (j + 2 < n_tiles)
+      load_kv<D>(k_src, v_src, plan, static_cast<uint32_t>(j + 2) * tile_bytes, row_bytes, rk, rv);
     __syncthreads();
   }
 
