@@ -39,6 +39,7 @@ namespace {
 constexpr int kAttnThreads = 256;
 constexpr int kBQ = 128;  // queries per workgroup
 constexpr int kBKV = 64;  // keys per step
+constexpr float kLazyLog2 = 8.0f;  // slack of the lazily updated softmax maximum
 
 // Logical (query tile, q-head) of workgroup `bid`: pairs (query tile, kv-head)
 // are enumerated heaviest query tile first; the g q-heads of a pair land on
@@ -135,7 +136,8 @@ __device__ __forceinline__ void store_kv(uint16_t* __restrict__ stage, const u32
     *reinterpret_cast<u32x4*>(stage + (c / (D / 8)) * L::kKRow + (c % (D / 8)) * 8) = rk[i];
   }
   uint32_t* vt = reinterpret_cast<uint32_t*>(stage + L::kKElems);
-  const int flip = (tid >> 5) & 1;  // half-waves write rows of opposite parity
+  // Lanes 32-63 write rows 8 below lanes 0-31 (a 288-dword offset), so a wave's
+  // 4-byte writes land in distinct banks.
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
     const int c = tid + i * kAttnThreads;
@@ -148,9 +150,8 @@ __device__ __forceinline__ void store_kv(uint16_t* __restrict__ stage, const u32
     for (int w = 0; w < 4; ++w) {
       const uint32_t lo = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);  // (a.lo, b.lo)
       const uint32_t hi = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);  // (a.hi, b.hi)
-      const int e0 = 2 * w + flip, e1 = 2 * w + (flip ^ 1);
-      col[e0 * (L::kVtRow / 2)] = flip ? hi : lo;
-      col[e1 * (L::kVtRow / 2)] = flip ? lo : hi;
+      col[(2 * w) * (L::kVtRow / 2)] = lo;
+      col[(2 * w + 1) * (L::kVtRow / 2)] = hi;
     }
   }
 }
@@ -219,6 +220,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
   float m_run = -__builtin_inff();
+  float mc = -__builtin_inff();  // m_run * c_log2
   float l_run = 0.f;
 
   KvLoadPlan<D> plan;
@@ -272,10 +274,22 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-      const float mc = m_new * c_log2;
-      m_run = m_new;
+      // Lazy reference maximum: m_run only moves when the tile's maximum
+      // exceeds it by more than 2^kLazyLog2 in exp2 units, so the accumulators
+      // are rescaled rarely; meanwhile P may reach 2^kLazyLog2 (exact in fp32,
+      // a plain scale factor for bf16).
+      const bool grow = (mx - m_run) * c_log2 > kLazyLog2;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+        m_run = m_new;
+        mc = m_new * c_log2;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -285,14 +299,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
           s[kb][r] = p;
           psum += p;
         }
-      l_run = fmaf(l_run, alpha, psum);
-      // Rescale the accumulators only when some query of the wave saw a new maximum.
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      }
+      l_run += psum;
 #pragma unroll
       for (int stp = 0; stp < 4; ++stp) {
         const int kb = stp >> 1;
