@@ -6,9 +6,12 @@
 // 实现长序列推理高效加速", §2.1 (U and Δattn) and §2.2 (the norm costs next to
 // nothing once U is produced).
 //
-// bf16 path: 128x128 output tile per 256-thread workgroup, K stepped by 64,
-// operands double-buffered in LDS, v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation.  The tile is computed transposed (C^T = Wo_tile · O_tile^T) so
+// bf16 path: 256x256 output tile per 512-thread workgroup (8 waves of 64x128),
+// K stepped by 64, operands streamed into a double-buffered LDS ring by direct
+// global->LDS loads (no register staging) one step ahead of the MFMAs
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation); rows are XOR-swizzled so the
+// operand reads are free of bank conflicts, and tiles are grouped so the
+// workgroups running together share their A rows and W slices in L2.  The tile is computed transposed (C^T = Wo_tile · O_tile^T) so
 // that every lane holds a single output row: the row's sum of squares is then
 // accumulated in registers straight from the fp32 accumulators, before U is
 // rounded to bf16.  Each (row, 128-column tile) partial is written to the
@@ -21,50 +24,78 @@ namespace dash {
 
 namespace {
 
-constexpr int kGemmThreads = 256;
-constexpr int kBM = 128;           // rows of U (tokens)
-constexpr int kBN = 128;           // columns of U (hidden channels)
-constexpr int kBK = 64;            // contraction step
-constexpr int kLdsRow = kBK + 8;   // padded LDS row (bf16 elements): 144 bytes
-constexpr int kTileElems = kBM * kLdsRow;
+constexpr int kGemmThreads = 512;                       // 8 waves
+constexpr int kBM = 256;                                // rows of U (tokens) per tile
+constexpr int kBN = 256;                                // columns of U (hidden channels) per tile
+constexpr int kBK = 64;                                 // contraction step: one 128-byte LDS row
+constexpr int kStages = 2;                              // LDS ring depth (loads run 1 step ahead)
+constexpr int kRowBytes = kBK * 2;
+constexpr int kRowChunks = kRowBytes / 16;              // 16-byte chunks per row
+constexpr int kRowsPerLine = 256 / kRowBytes;           // rows sharing one 64-bank line
+constexpr int kATileBytes = kBM * kRowBytes;            // 32 KiB
+constexpr int kWTileBytes = kBN * kRowBytes;            // 32 KiB
+constexpr int kStageBytes = kATileBytes + kWTileBytes;  // 64 KiB
+constexpr int kChunksPerStage = kStageBytes / 1024;     // 1 KiB per wave-wide direct load
+constexpr int kLoadsPerWave = kChunksPerStage / (kGemmThreads / 64);  // 8
+constexpr int kGroupM = 4;                              // m-tiles per L2-sharing group
+constexpr int kNB = 4;                                  // 32-column blocks per wave (128 columns)
+constexpr int kMB = 2;                                  // 32-row blocks per wave (64 rows)
 
-__device__ __forceinline__ void gemm_load_tile(const uint16_t* __restrict__ base, int rows_valid, int ld,
-                                               int k0, u32x4 (&r)[4]) {
-  // 128 rows x 64 bf16 = 1024 chunks of 16 bytes; thread t takes chunks t, t+256, ...
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + i * kGemmThreads;
-    const int row = c >> 3;
-    const int kc = c & 7;
-    if (row < rows_valid)
-      r[i] = *reinterpret_cast<const u32x4*>(base + static_cast<size_t>(row) * ld + k0 + kc * 8);
-    else
-      r[i] = u32x4{0u, 0u, 0u, 0u};
-  }
+// Row r keeps its 16-byte chunk c at slot c ^ ((r / kRowsPerLine) % kRowChunks):
+// the 16 lanes of one 16-byte operand read (16 consecutive rows) then hit
+// distinct banks of the 64-bank LDS.
+__device__ __forceinline__ int gemm_slot(int row, int chunk) {
+  return chunk ^ ((row / kRowsPerLine) % kRowChunks);
 }
 
-__device__ __forceinline__ void gemm_store_tile(uint16_t* lds, const u32x4 (&r)[4]) {
+struct GemmLoadPlan {
+  const uint16_t* src[kLoadsPerWave];  // row start + swizzled chunk, at k = 0
+  __device__ __forceinline__ void init(const uint16_t* A, const uint16_t* W, int m0, int n0, int M, int N, int K) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int kRowsPerKiB = 1024 / kRowBytes;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + i * kGemmThreads;
-    const int row = c >> 3;
-    const int kc = c & 7;
-    *reinterpret_cast<u32x4*>(lds + row * kLdsRow + kc * 8) = r[i];
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int q = wave + 8 * i;  // 1 KiB chunk of the stage
+      const int is_a = q < kATileBytes / 1024;
+      const int local_row = (is_a ? q : q - kATileBytes / 1024) * kRowsPerKiB + lane / kRowChunks;
+      const int chunk = gemm_slot(local_row, lane % kRowChunks);
+      // rows past the matrix edge re-read the last row (their results are never stored)
+      const int grow = is_a ? min(m0 + local_row, M - 1) : min(n0 + local_row, N - 1);
+      src[i] = (is_a ? A : W) + static_cast<size_t>(grow) * K + chunk * 8;
+    }
   }
-}
+  __device__ __forceinline__ void issue(unsigned char* stage, int k0) const {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int q = wave + 8 * i;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + k0),
+                                       (__attribute__((address_space(3))) void*)(stage + q * 1024), 16, 0, 0);
+    }
+  }
+};
 
-__global__ __launch_bounds__(kGemmThreads, 2)
+__device__ __forceinline__ void wait_vmcnt_0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ void wait_lgkm_0() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+
+__global__ __launch_bounds__(kGemmThreads, 1)
 void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                          uint16_t* __restrict__ U, float* __restrict__ part,
                          const int32_t* __restrict__ m_dev, int M_max, int N, int K, int n_tiles_n,
                          int part_ld) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kTileElems];  // [stage][A|W]
+  static_assert(kLoadsPerWave * (kGemmThreads / 64) == kChunksPerStage, "stage split");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * kStageBytes];
   int M = m_dev ? *m_dev : M_max;
   if (M > M_max) M = M_max;
   const int n_tiles_m = (M_max + kBM - 1) / kBM;
   const int lid = xcd_remap(blockIdx.x, n_tiles_m * n_tiles_n);
-  const int tn = lid % n_tiles_n;
-  const int tm = lid / n_tiles_n;
+  // Groups of kGroupM m-tiles sweep all n-tiles together (shared A rows and W
+  // k-slices stay in L2 while the group runs).
+  const int group = lid / (kGroupM * n_tiles_n);
+  const int gm = min(kGroupM, n_tiles_m - group * kGroupM);
+  const int within = lid - group * kGroupM * n_tiles_n;
+  const int tm = group * kGroupM + within % gm;
+  const int tn = within / gm;
   const int m0 = tm * kBM;
   const int n0 = tn * kBN;
   if (m0 >= M) return;
@@ -74,114 +105,123 @@ void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int wn = wave >> 1;  // 0..1 : 64-column half of the tile
-  const int wm = wave & 1;   // 0..1 : 64-row half of the tile
+  const int wm = wave & 3;   // 64-row slice of the tile
+  const int wn = wave >> 2;  // 128-column slice of the tile
 
-  const uint16_t* Ab = A + static_cast<size_t>(m0) * K;
-  const uint16_t* Wb = W + static_cast<size_t>(n0) * K;
-  const int rows_a = min(kBM, M - m0);
-  const int rows_w = min(kBN, N - n0);
+  GemmLoadPlan plan;
+  plan.init(A, W, m0, n0, M, N, K);
 
-  f32x16 acc[2][2];
+  // Per-lane byte offsets of the 16-byte operand chunk for each 16-wide k-step.
+  int koff[kBK / 16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int ks = 0; ks < kBK / 16; ++ks) koff[ks] = 16 * gemm_slot(l32, 2 * ks + hi);
+  const int a_row = (wm * 64 + l32) * kRowBytes;                  // O rows (B operand)
+  const int w_row = kATileBytes + (wn * 128 + l32) * kRowBytes;   // W rows (A operand)
+
+  f32x16 acc[kNB][kMB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < kNB; ++i)
+#pragma unroll
+    for (int j = 0; j < kMB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ra[4], rw[4];
-  gemm_load_tile(Ab, rows_a, K, 0, ra);
-  gemm_load_tile(Wb, rows_w, K, 0, rw);
-  gemm_store_tile(lds, ra);
-  gemm_store_tile(lds + kTileElems, rw);
-  __syncthreads();
-
   const int KT = K / kBK;
+  plan.issue(lds, 0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      gemm_load_tile(Ab, rows_a, K, (kt + 1) * kBK, ra);
-      gemm_load_tile(Wb, rows_w, K, (kt + 1) * kBK, rw);
-    }
-    const uint16_t* la = lds + cur * 2 * kTileElems;
-    const uint16_t* lw = la + kTileElems;
+    wait_vmcnt_0();                 // this wave's part of step kt has landed
+    __builtin_amdgcn_s_barrier();   // ... and every wave's; step kt-1 is done
+    if (kt + 1 < KT) plan.issue(lds + ((kt + 1) & 1) * kStageBytes, (kt + 1) * kBK);
+    const unsigned char* st = lds + (kt & 1) * kStageBytes;
+    bf16x8 opw[2][kNB], opa[2][kMB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+      opw[0][nb] = *reinterpret_cast<const bf16x8*>(st + w_row + nb * 32 * kRowBytes + koff[0]);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+      opa[0][mb] = *reinterpret_cast<const bf16x8*>(st + a_row + mb * 32 * kRowBytes + koff[0]);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 opw[2], opa[2];
+      const int cur = ks & 1;
+      if (ks + 1 < kBK / 16) {  // operands of the next 16-wide step are read while this one multiplies
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        opw[nb] = *reinterpret_cast<const bf16x8*>(lw + (wn * 64 + nb * 32 + l32) * kLdsRow + ks * 16 + hi * 8);
+        for (int nb = 0; nb < kNB; ++nb)
+          opw[cur ^ 1][nb] = *reinterpret_cast<const bf16x8*>(st + w_row + nb * 32 * kRowBytes + koff[ks + 1]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        opa[mb] = *reinterpret_cast<const bf16x8*>(la + (wm * 64 + mb * 32 + l32) * kLdsRow + ks * 16 + hi * 8);
+        for (int mb = 0; mb < kMB; ++mb)
+          opa[cur ^ 1][mb] = *reinterpret_cast<const bf16x8*>(st + a_row + mb * 32 * kRowBytes + koff[ks + 1]);
+      }
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma32x32x16(opw[nb], opa[mb], acc[nb][mb]);
+        for (int mb = 0; mb < kMB; ++mb) acc[nb][mb] = mfma32x32x16(opw[cur][nb], opa[cur][mb], acc[nb][mb]);
     }
-    if (more) {
-      uint16_t* nx = lds + (cur ^ 1) * 2 * kTileElems;
-      gemm_store_tile(nx, ra);
-      gemm_store_tile(nx + kTileElems, rw);
-    }
-    __syncthreads();
   }
 
   // ---- epilogue -----------------------------------------------------------
   // acc[nb][mb][r] = U[m][n] with m = m0 + wm*64 + mb*32 + l32,
-  //                  n = n0 + wn*64 + nb*32 + (r/4)*8 + hi*4 + (r%4).
-  float* red = reinterpret_cast<float*>(lds);            // [2 wn][128 m] partial sums
-  uint16_t* ct = lds + 2 * kTileElems;                    // staging tile [128 m][kLdsC]
+  //                  n = n0 + wn*128 + nb*32 + (r/4)*8 + hi*4 + (r%4).
+  wait_lgkm_0();
+  __builtin_amdgcn_s_barrier();  // every wave is done with the ring before it is reused
+  float* red = reinterpret_cast<float*>(lds);                // [2 wn][256 m] partial sums
+  uint16_t* ct = reinterpret_cast<uint16_t*>(lds + 4096);    // staging [128 m][kLdsC], one half at a time
   constexpr int kLdsC = kBN + 8;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < kMB; ++mb) {
     float ss = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int nl = wn * 64 + nb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+        const int nl = wn * 128 + nb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
         const float v = (n0 + nl < N) ? acc[nb][mb][r] : 0.f;
         ss += v * v;
       }
     ss += __shfl_xor(ss, 32, 64);
-    const int ml = wm * 64 + mb * 32 + l32;
-    if (hi == 0) red[wn * kBM + ml] = ss;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn * 64 + nb * 32 + g * 8 + hi * 4;
-        u32x2 pk;
-        pk[0] = pack_bf16x2(acc[nb][mb][g * 4 + 0], acc[nb][mb][g * 4 + 1]);
-        pk[1] = pack_bf16x2(acc[nb][mb][g * 4 + 2], acc[nb][mb][g * 4 + 3]);
-        *reinterpret_cast<u32x2*>(ct + ml * kLdsC + nl) = pk;
-      }
+    if (hi == 0) red[wn * kBM + wm * 64 + mb * 32 + l32] = ss;
   }
-  __syncthreads();
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((wm >> 1) == half) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) {
+        const int ml = (wm & 1) * 64 + mb * 32 + l32;  // row within this half
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int nl = wn * 128 + nb * 32 + g * 8 + hi * 4;
+            u32x2 pk;
+            pk[0] = pack_bf16x2(acc[nb][mb][g * 4 + 0], acc[nb][mb][g * 4 + 1]);
+            pk[1] = pack_bf16x2(acc[nb][mb][g * 4 + 2], acc[nb][mb][g * 4 + 3]);
+            *reinterpret_cast<u32x2*>(ct + ml * kLdsC + nl) = pk;
+          }
+      }
+    }
+    __syncthreads();
+    // Coalesced store of 128 rows x 32 chunks of 16 bytes.
+#pragma unroll
+    for (int i = 0; i < (128 * kBN / 8) / kGemmThreads; ++i) {
+      const int c = tid + i * kGemmThreads;
+      const int row = c >> 5;
+      const int cc = c & 31;
+      const int m = m0 + half * 128 + row;
+      const int n = n0 + cc * 8;
+      if (m < M && n < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ct + row * kLdsC + cc * 8);
+        if (n + 8 <= N) {
+          *reinterpret_cast<u32x4*>(U + static_cast<size_t>(m) * N + n) = v;
+        } else {
+          for (int j = 0; j < N - n; ++j)
+            U[static_cast<size_t>(m) * N + n + j] = static_cast<uint16_t>(v[j >> 1] >> (16 * (j & 1)));
+        }
+      }
+    }
+    __syncthreads();
+  }
   if (part && tid < kBM) {
     const int m = m0 + tid;
     if (m < M) part[static_cast<size_t>(tn) * part_ld + m] = red[tid] + red[kBM + tid];
-  }
-  // Coalesced store of the bf16 tile: 128 rows x 16 chunks of 16 bytes.
-#pragma unroll
-  for (int i = 0; i < (kBM * kBN / 8) / kGemmThreads; ++i) {
-    const int c = tid + i * kGemmThreads;
-    const int row = c >> 4;
-    const int cc = c & 15;
-    const int m = m0 + row;
-    const int n = n0 + cc * 8;
-    if (m < M && n < N) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ct + row * kLdsC + cc * 8);
-      if (n + 8 <= N) {
-        *reinterpret_cast<u32x4*>(U + static_cast<size_t>(m) * N + n) = v;
-      } else {
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
-        for (int j = 0; j < N - n; ++j) U[static_cast<size_t>(m) * N + n + j] = e[j];
-      }
-    }
   }
 }
 
@@ -249,15 +289,24 @@ void wo_gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W
   }
 }
 
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(64)
 void score_finalize_kernel(const float* __restrict__ part, int n_parts, int part_ld,
                            const int32_t* __restrict__ m_dev, int M_max, float* __restrict__ score) {
   int M = m_dev ? *m_dev : M_max;
   if (M > M_max) M = M_max;
-  const int m = blockIdx.x * 256 + threadIdx.x;
+  const int m = blockIdx.x * 64 + threadIdx.x;
   if (m >= M) return;
+  // Partials are added in tile order; the loads of a group of 8 are issued together.
   float s = 0.f;
-  for (int t = 0; t < n_parts; ++t) s += part[static_cast<size_t>(t) * part_ld + m];
+  int t = 0;
+  for (; t + 8 <= n_parts; t += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[static_cast<size_t>(t + u) * part_ld + m];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; t < n_parts; ++t) s += part[static_cast<size_t>(t) * part_ld + m];
   score[m] = sqrtf(s);
 }
 
@@ -284,7 +333,7 @@ hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, floa
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !score) return e;
-  hipLaunchKernelGGL(score_finalize_kernel, dim3((M_max + 255) / 256), dim3(256), 0, stream, part, parts, M_max,
+  hipLaunchKernelGGL(score_finalize_kernel, dim3((M_max + 63) / 64), dim3(64), 0, stream, part, parts, M_max,
                      m_dev, M_max, score);
   return hipGetLastError();
 }

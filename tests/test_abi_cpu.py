@@ -72,7 +72,7 @@ def test_attn_layer_validation(lib):
     # score requested with a missing or short workspace
     assert f(None, ctypes.byref(_shape()), *p, FAKE, None, 0, None) == L.DASH_E_WORKSPACE
     need = lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(_shape()), 64)
-    assert need >= 64 * 4 * 4  # 4 column tiles of 128 for hidden 512
+    assert need >= 64 * 4  # at least one fp32 partial per row
     assert f(None, ctypes.byref(_shape()), *p, FAKE, FAKE, need - 1, None) == L.DASH_E_WORKSPACE
 
 
@@ -131,7 +131,7 @@ def test_attn_active_validation(lib):
 def test_workspace_size(lib):
     s = _shape(hidden=3584, S=8192, Hq=28, Hkv=4)
     n = lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(s), 8192)
-    assert n >= 28 * 8192 * 4
+    assert n >= 8192 * 4
     assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(s), 8192) == 0
     assert lib.dash_workspace_size(None, 17, ctypes.byref(s), 8192) == 0
     assert lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(_shape(D=33)), 8192) == 0
