@@ -64,17 +64,6 @@ __device__ __forceinline__ void attn_tile_of(int bid, int n_qt, int Hkv, int g, 
   h = kvh * g + j;
 }
 
-template <int D>
-struct AttnLds {
-  static constexpr int kKRow = D + 8;          // padded K row, bf16 elements (272 B for D=128)
-  static constexpr int kKElems = kBKV * kKRow;
-  static constexpr int kVtRow = kBKV + 8;      // padded V^T row, bf16 elements (144 B)
-  static constexpr int kVtElems = D * kVtRow;
-  static constexpr int kStage = kKElems + kVtElems;
-  static constexpr int kTotal = 2 * kStage;
-  static constexpr int kORow = D + 8;          // output staging row
-};
-
 // Buffer resource over `bytes` bytes from `base`: loads past the end return 0,
 // which is how rows beyond the key count read as zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -82,78 +71,68 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-// Within each group of 16 keys, V^T stores key r at position
-// 8*((r>>2)&1) + 4*(r>>3) + (r&3): the 8 keys one half-wave feeds to a 16-key
-// MFMA step (r = 4h..4h+3 and 8+4h..8+4h+3) are then 16 contiguous bytes.
-__device__ __forceinline__ int vt_dword_of_pair(int kp) {
-  const int r = (2 * kp) & 15;
-  const int p = 8 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-  return (kp >> 3) * 8 + (p >> 1);
+template <int D>
+struct AttnCfg {
+  static constexpr int kRowBytes = D * 2;               // K and V rows in LDS (unpadded, swizzled)
+  static constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
+  static constexpr int kRowsPerLine = 256 / kRowBytes;  // rows per 64-bank line
+  static constexpr int kTileBytes = kBKV * kRowBytes;   // one K or V tile
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / (kAttnThreads / 64);
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;
+  static constexpr int kTotal = 4 * kTileBytes;         // K[2] + V[2]
+  static constexpr int kORow = D + 8;                   // output staging row (bf16 elements)
+};
+
+// K rows: chunk c of row r sits at slot c ^ ((r / kRowsPerLine) % kChunks), so
+// the 16 consecutive rows of one 16-byte operand read hit distinct banks.
+template <int D>
+__device__ __forceinline__ int k_slot(int r, int c) {
+  using C = AttnCfg<D>;
+  return c ^ ((r / C::kRowsPerLine) % C::kChunks);
 }
 
-// Per-thread global offsets (bytes, relative to the tile's first key row).
+// V rows: chunk c of row r sits at slot c ^ (4 * ((r / kRowsPerLine) % (kChunks / 4))),
+// so the four rows x 64 bytes that 32 lanes fetch in one transposing read
+// (ds_read_b64_tr_b16) hit distinct banks.
 template <int D>
-struct KvLoadPlan {
-  uint32_t k_off[D / 32];
-  uint32_t v_off[D / 64];
+__device__ __forceinline__ int v_slot(int r, int c) {
+  using C = AttnCfg<D>;
+  return c ^ (4 * ((r / C::kRowsPerLine) % (C::kChunks / 4)));
+}
+
+// Direct global->LDS loads of one K or V tile: each wave moves kLoadsPerWave
+// KiB; lane l of a 1 KiB load lands at byte 16*l, i.e. row l / kChunks, slot
+// l % kChunks, and fetches the chunk the swizzle puts there.
+template <int D, bool IsV>
+struct TileLoader {
+  using C = AttnCfg<D>;
+  uint32_t voff[C::kLoadsPerWave];
   __device__ __forceinline__ void init(int kv_ld) {
-    const int tid = threadIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      const int c = tid + i * kAttnThreads;
-      k_off[i] = static_cast<uint32_t>((c / (D / 8)) * kv_ld + (c % (D / 8)) * 8) * 2u;
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      const int q = wave + (kAttnThreads / 64) * i;
+      const int row = q * C::kRowsPerKiB + lane / C::kChunks;
+      const int slot = lane % C::kChunks;
+      const int chunk = IsV ? v_slot<D>(row, slot) : k_slot<D>(row, slot);
+      voff[i] = static_cast<uint32_t>(row * kv_ld * 2 + chunk * 16);
     }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, unsigned char* tile, uint32_t tile_off) const {
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-      const int c = tid + i * kAttnThreads;
-      v_off[i] = static_cast<uint32_t>((2 * (c & 31)) * kv_ld + (c >> 5) * 8) * 2u;
+    for (int i = 0; i < C::kLoadsPerWave; ++i) {
+      const int q = wave + (kAttnThreads / 64) * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(tile + q * 1024), 16,
+                                               voff[i], tile_off, 0, 0);
     }
   }
 };
 
-template <int D>
-__device__ __forceinline__ void load_kv(__amdgpu_buffer_rsrc_t rk_src, __amdgpu_buffer_rsrc_t rv_src,
-                                        const KvLoadPlan<D>& pl, uint32_t tile_off, uint32_t row_bytes,
-                                        u32x4 (&rk)[D / 32], u32x4 (&rv)[D / 64][2]) {
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-    rk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk_src, pl.k_off[i], tile_off, 0);
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    rv[i][0] = __builtin_amdgcn_raw_buffer_load_b128(rv_src, pl.v_off[i], tile_off, 0);
-    rv[i][1] = __builtin_amdgcn_raw_buffer_load_b128(rv_src, pl.v_off[i] + row_bytes, tile_off, 0);
-  }
-}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
-__device__ __forceinline__ void store_kv(uint16_t* __restrict__ stage, const u32x4 (&rk)[D / 32],
-                                         const u32x4 (&rv)[D / 64][2]) {
-  using L = AttnLds<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int c = tid + i * kAttnThreads;
-    *reinterpret_cast<u32x4*>(stage + (c / (D / 8)) * L::kKRow + (c % (D / 8)) * 8) = rk[i];
-  }
-  uint32_t* vt = reinterpret_cast<uint32_t*>(stage + L::kKElems);
-  // Lanes 32-63 write rows 8 below lanes 0-31 (a 288-dword offset), so a wave's
-  // 4-byte writes land in distinct banks.
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const int c = tid + i * kAttnThreads;
-    const int kp = c & 31;
-    const int dc = c >> 5;
-    const u32x4 a = rv[i][0];  // 8 bf16 of key 2kp   (element e in word e/2, half e%2)
-    const u32x4 b = rv[i][1];  // 8 bf16 of key 2kp+1
-    uint32_t* col = vt + dc * 8 * (L::kVtRow / 2) + vt_dword_of_pair(kp);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);  // (a.lo, b.lo)
-      const uint32_t hi = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);  // (a.hi, b.hi)
-      col[(2 * w) * (L::kVtRow / 2)] = lo;
-      col[(2 * w + 1) * (L::kVtRow / 2)] = hi;
-    }
-  }
+__device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
 template <int D>
@@ -162,8 +141,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_dev, int n_q_max,
                           int n_kv, int Hq, int Hkv, float c_log2, int64_t q_bs, int64_t kv_bs, int64_t o_bs) {
-  using L = AttnLds<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[L::kTotal];
+  using C = AttnCfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kTotal];
 
   int n_q = n_dev ? *n_dev : n_q_max;
   if (n_q > n_q_max) n_q = n_q_max;
@@ -183,7 +162,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int q_ld = Hq * D;
   const int kv_ld = Hkv * D;
   const uint32_t row_bytes = static_cast<uint32_t>(kv_ld) * 2u;
-  // bytes from this kv-head's first element to the end of the last key row
+  // bytes from this kv-head's first element to the end of the last key row;
+  // loads past it (rows beyond the key count) return zeros
   const uint32_t kv_bytes = n_kv > 0 ? static_cast<uint32_t>(n_kv - 1) * row_bytes + D * 2u : 0u;
   const __amdgpu_buffer_rsrc_t k_src = make_rsrc(K, kv_bytes);
   const __amdgpu_buffer_rsrc_t v_src = make_rsrc(V, kv_bytes);
@@ -205,6 +185,25 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int block_pmax = q_pos ? q_pos[b_last] : b_last;
   const int kv_end = min(n_kv, block_pmax + 1);
   const int n_tiles = (kv_end + kBKV - 1) / kBKV;
+  // Tiles this wave computes (keys k0 <= wave_pmax) and the first one that
+  // holds a key past some query of the wave (needs the causal mask).
+  const int n_w = min(n_tiles, wave_pmax / kBKV + 1);
+  const int j_mask = min(n_w, (wave_pmin + 1) / kBKV);
+
+  unsigned char* kbuf0 = lds;
+  unsigned char* vbuf0 = lds + 2 * C::kTileBytes;
+  auto kbuf = [&](int i) { return kbuf0 + (i & 1) * C::kTileBytes; };
+  auto vbuf = [&](int i) { return vbuf0 + (i & 1) * C::kTileBytes; };
+  TileLoader<D, false> kload;
+  TileLoader<D, true> vload;
+  kload.init(kv_ld);
+  vload.init(kv_ld);
+  const uint32_t tile_bytes = static_cast<uint32_t>(kBKV) * row_bytes;
+
+  // Prologue loads: K(0), K(1), V(0).
+  kload.issue(k_src, kbuf(0), 0u);
+  if (n_tiles > 1) kload.issue(k_src, kbuf(1), tile_bytes);
+  vload.issue(v_src, vbuf(0), 0u);
 
   // This lane's query as the B operand of S^T = K Q^T: 8 dims per k-step.
   bf16x8 qreg[D / 16];
@@ -223,109 +222,145 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   float mc = -__builtin_inff();  // m_run * c_log2
   float l_run = 0.f;
 
-  KvLoadPlan<D> plan;
-  plan.init(kv_ld);
-  const uint32_t tile_bytes = static_cast<uint32_t>(kBKV) * row_bytes;
-  u32x4 rk[D / 32];
-  u32x4 rv[D / 64][2];
-  load_kv<D>(k_src, v_src, plan, 0u, row_bytes, rk, rv);
-  store_kv<D>(lds, rk, rv);
-  // Drain every outstanding global load (the query registers included) before
-  // the loop, so the only loads in flight inside it are the tile prefetches and
-  // no wait for them lands ahead of the score MFMAs.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (n_tiles > 1) load_kv<D>(k_src, v_src, plan, tile_bytes, row_bytes, rk, rv);
-  __syncthreads();
+  // K operand offsets: row kb*32 + l32, chunk 2*ks + hi (the kb term is an immediate).
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * C::kRowBytes + 16 * k_slot<D>(l32, 2 * ks + hi);
+  // V^T operand (transposing reads): 16-lane group grp = (l32 / 16) covers d = db*32 + 16*grp .. +15;
+  // source lane j = lane % 16 reads key row kb0 + j/4, d chunk db*32 + 16*grp + 4*(j%4).
+  const int tj = lane & 15;
+  const int tgrp = (lane >> 4) & 1;
+  int voffs[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int row = (tj >> 2) + 4 * hi;  // row within the tile for key step 0, part 0
+    const int e = db * 32 + 16 * tgrp + 4 * (tj & 3);  // first d element read
+    voffs[db] = row * C::kRowBytes + 16 * v_slot<D>(row, e >> 3) + 2 * (e & 7);
+  }
 
-  // LDS operand addresses (bytes) for this lane; per-step offsets are immediates.
-  const int k_lane = (l32 * L::kKRow + hi * 8) * 2;
-  const int vt_lane = (l32 * L::kVtRow + hi * 8) * 2 + L::kKElems * 2;
+  // S^T for one key tile: 2 blocks of 32 keys x this wave's 32 queries.
+  auto qk = [&](const unsigned char* kst, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + koff[ks] + kb * 32 * C::kRowBytes);
+        s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
+      }
+  };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int k0 = j * kBKV;
-    const unsigned char* st = reinterpret_cast<const unsigned char*>(lds + (j & 1) * L::kStage);
-    if (k0 <= wave_pmax) {
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(st + k_lane + (kb * 32 * L::kKRow + ks * 16) * 2);
-          s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
-        }
-      }
-      if (k0 + kBKV - 1 > wave_pmin) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            s[kb][r] = key > my_pos ? -__builtin_inff() : s[kb][r];
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy reference maximum: m_run only moves when the tile's maximum
-      // exceeds it by more than 2^kLazyLog2 in exp2 units, so the accumulators
-      // are rescaled rarely; meanwhile P may reach 2^kLazyLog2 (exact in fp32,
-      // a plain scale factor for bf16).
-      const bool grow = (mx - m_run) * c_log2 > kLazyLog2;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-        m_run = m_new;
-        mc = m_new * c_log2;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      }
-      float psum = 0.f;
+  // Softmax numerator of a tile in place, with the lazy running maximum; returns
+  // alpha (the accumulator rescale, 1 unless the reference maximum moved).
+  auto softmax = [&](f32x16 (&s)[2], int k0, bool masked) -> float {
+    if (masked) {
+      const int lim = my_pos - k0 - hi * 4;  // key offset c is visible iff c <= lim
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -mc));
-          s[kb][r] = p;
-          psum += p;
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          s[kb][r] = c > lim ? -__builtin_inff() : s[kb][r];
         }
-      l_run += psum;
+    }
+    float mx = s[0][0];
 #pragma unroll
-      for (int stp = 0; stp < 4; ++stp) {
-        const int kb = stp >> 1;
-        const int sub = stp & 1;
-        u32x4 pw;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) pw[t] = pack_bf16x2(s[kb][8 * sub + 2 * t], s[kb][8 * sub + 2 * t + 1]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // The reference maximum only moves when the tile's maximum exceeds it by
+    // more than 2^kLazyLog2 in exp2 units (P then stays <= 2^kLazyLog2).
+    const bool grow = (mx - m_run) * c_log2 > kLazyLog2;
+    const float m_new = grow ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+    m_run = m_new;
+    mc = m_new * c_log2;
+    float psum = 0.f;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 av =
-              *reinterpret_cast<const bf16x8*>(st + vt_lane + (db * 32 * L::kVtRow + stp * 16) * 2);
-          o[db] = mfma32x32x16(av, pb, o[db]);
-        }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -mc));
+        s[kb][r] = p;
+        psum += p;
+      }
+    l_run = fmaf(l_run, alpha, psum);
+    return alpha;
+  };
+
+  // O^T += V^T P^T for one tile: P rounded to bf16 as the B operand; the V^T
+  // operand (8 keys of one d per lane) comes from two transposing reads.
+  auto pv = [&](const f32x16 (&s)[2], const unsigned char* vst) {
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp) {
+      const int kb = stp >> 1;
+      const int sub = stp & 1;
+      u32x4 pw;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pw[t] = pack_bf16x2(s[kb][8 * sub + 2 * t], s[kb][8 * sub + 2 * t + 1]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        // keys 16*stp + 4*hi + (0..3) and 16*stp + 8 + 4*hi + (0..3)
+        const i16x4 lo = lds_read_tr16(vst + voffs[db] + (16 * stp) * C::kRowBytes);
+        const i16x4 up = lds_read_tr16(vst + voffs[db] + (16 * stp + 8) * C::kRowBytes);
+        const u32x4 av = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                          __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]};
+        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), pb, o[db]);
       }
     }
-    if (j + 1 < n_tiles) store_kv<D>(lds + ((j + 1) & 1) * L::kStage, rk, rv);
-    if (j + 2 < n_tiles)
-      load_kv<D>(k_src, v_src, plan, static_cast<uint32_t>(j + 2) * tile_bytes, row_bytes, rk, rv);
-    __syncthreads();
+  };
+
+  auto rescale = [&](float alpha) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+  };
+
+  // Step j: wait for K(j+1) and V(j), then refill the freed buffers with K(j+2)
+  // and V(j+1) while the scores of tile j+1 (MFMA) and the softmax of tile j
+  // (vector ALU) run side by side, then O += P V for tile j.
+  auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of K(j+1), V(j)
+    __builtin_amdgcn_s_barrier();        // everyone's; and everyone is past step j-1
+    if (j + 2 < n_tiles) kload.issue(k_src, kbuf(j), static_cast<uint32_t>(j + 2) * tile_bytes);
+    if (j + 1 < n_tiles) vload.issue(v_src, vbuf(j + 1), static_cast<uint32_t>(j + 1) * tile_bytes);
+    float alpha = 1.0f;
+    if (j + 1 < j_mask) {  // steady state: both tiles fully visible, one basic block
+      qk(kbuf(j + 1), s_nxt);
+      alpha = softmax(s_cur, j * kBKV, false);
+    } else {
+      if (j + 1 < n_w) qk(kbuf(j + 1), s_nxt);
+      if (j < n_w) alpha = softmax(s_cur, j * kBKV, j >= j_mask);
+    }
+    if (j < n_w) {
+      if (__any(alpha != 1.0f)) rescale(alpha);
+      pv(s_cur, vbuf(j));
+    }
+  };
+
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query registers and prologue tiles
+  __builtin_amdgcn_s_barrier();
+  f32x16 sa[2], sb[2];
+  if (n_w > 0) qk(kbuf(0), sa);
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, sa, sb);
+    step(j + 1, sb, sa);
   }
+  if (j < n_tiles) step(j, sa, sb);
 
   // Normalise and stage the 128 x D output tile through LDS for 16-byte stores.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
-  uint16_t* ot = lds;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __syncthreads();                     // every wave is done with the K/V buffers
+  uint16_t* ot = reinterpret_cast<uint16_t*>(lds);
   const int ql = wave * 32 + l32;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -335,19 +370,19 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       u32x2 pk;
       pk[0] = pack_bf16x2(o[db][gq * 4 + 0] * inv, o[db][gq * 4 + 1] * inv);
       pk[1] = pack_bf16x2(o[db][gq * 4 + 2] * inv, o[db][gq * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(ot + ql * L::kORow + d) = pk;
+      *reinterpret_cast<u32x2*>(ot + ql * C::kORow + d) = pk;
     }
   __syncthreads();
-  constexpr int kChunks = kBQ * D / 8;
+  constexpr int kOutChunks = kBQ * D / 8;
 #pragma unroll
-  for (int i = 0; i < kChunks / kAttnThreads; ++i) {
+  for (int i = 0; i < kOutChunks / kAttnThreads; ++i) {
     const int c = tid + i * kAttnThreads;
     const int row = c / (D / 8);
     const int dc = c % (D / 8);
     const int q = q0 + row;
     if (q < n_q)
       *reinterpret_cast<u32x4*>(O + static_cast<size_t>(q) * q_ld + h * D + dc * 8) =
-          *reinterpret_cast<const u32x4*>(ot + row * L::kORow + dc * 8);
+          *reinterpret_cast<const u32x4*>(ot + row * C::kORow + dc * 8);
   }
 }
 
