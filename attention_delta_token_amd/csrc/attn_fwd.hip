@@ -253,32 +253,45 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       }
   };
 
-  // Softmax numerator of a tile in place, with the lazy running maximum; returns
-  // alpha (the accumulator rescale, 1 unless the reference maximum moved).
-  auto softmax = [&](f32x16 (&s)[2], int k0, bool masked) -> float {
-    if (masked) {
-      const int lim = my_pos - k0 - hi * 4;  // key offset c is visible iff c <= lim
+  // Causal mask of a tile: keys past this lane's query position get -inf.
+  auto mask = [&](f32x16 (&s)[2], int k0) {
+    const int lim = my_pos - k0 - hi * 4;  // key offset c is visible iff c <= lim
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-          s[kb][r] = c > lim ? -__builtin_inff() : s[kb][r];
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+        s[kb][r] = c > lim ? -__builtin_inff() : s[kb][r];
+      }
+  };
+
+  // Maximum of a (masked) score tile; moves the lazy reference maximum when the
+  // tile exceeds it by more than 2^kLazyLog2 in exp2 units (P then stays below
+  // 2^kLazyLog2) and rescales the accumulators for it.  Called on tile j+1 at
+  // the end of step j, so step j+1 itself needs no branch.
+  auto update_max = [&](const f32x16 (&s)[2]) {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // The reference maximum only moves when the tile's maximum exceeds it by
-    // more than 2^kLazyLog2 in exp2 units (P then stays <= 2^kLazyLog2).
     const bool grow = (mx - m_run) * c_log2 > kLazyLog2;
-    const float m_new = grow ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-    m_run = m_new;
-    mc = m_new * c_log2;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+      m_run = m_new;
+      mc = m_new * c_log2;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+  };
+
+  // Softmax numerator of a tile in place against the current reference maximum.
+  auto softmax = [&](f32x16 (&s)[2]) {
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -288,8 +301,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         s[kb][r] = p;
         psum += p;
       }
-    l_run = fmaf(l_run, alpha, psum);
-    return alpha;
+    l_run += psum;
   };
 
   // O^T += V^T P^T for one tile: P rounded to bf16 as the B operand; the V^T
@@ -315,39 +327,42 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
   };
 
-  auto rescale = [&](float alpha) {
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-  };
-
-  // Step j: wait for K(j+1) and V(j), then refill the freed buffers with K(j+2)
-  // and V(j+1) while the scores of tile j+1 (MFMA) and the softmax of tile j
-  // (vector ALU) run side by side, then O += P V for tile j.
+  // Step j: wait for K(j+1) and V(j), refill the freed buffers with K(j+2) and
+  // V(j+1); then, in one basic block, the scores of tile j+1 (MFMA) run beside
+  // the softmax of tile j (vector ALU) and O += P V for tile j follows while the
+  // maximum of tile j+1 is taken.  Tile j+1's reference maximum (and any
+  // accumulator rescale) is settled at the end of the step.
   auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of K(j+1), V(j)
     __builtin_amdgcn_s_barrier();        // everyone's; and everyone is past step j-1
     if (j + 2 < n_tiles) kload.issue(k_src, kbuf(j), static_cast<uint32_t>(j + 2) * tile_bytes);
     if (j + 1 < n_tiles) vload.issue(v_src, vbuf(j + 1), static_cast<uint32_t>(j + 1) * tile_bytes);
-    float alpha = 1.0f;
-    if (j + 1 < j_mask) {  // steady state: both tiles fully visible, one basic block
+    if (j + 1 < j_mask) {  // steady state: tile j+1 fully visible
       qk(kbuf(j + 1), s_nxt);
-      alpha = softmax(s_cur, j * kBKV, false);
+      softmax(s_cur);
+      pv(s_cur, vbuf(j));
+      update_max(s_nxt);
     } else {
       if (j + 1 < n_w) qk(kbuf(j + 1), s_nxt);
-      if (j < n_w) alpha = softmax(s_cur, j * kBKV, j >= j_mask);
-    }
-    if (j < n_w) {
-      if (__any(alpha != 1.0f)) rescale(alpha);
-      pv(s_cur, vbuf(j));
+      if (j < n_w) {
+        softmax(s_cur);
+        pv(s_cur, vbuf(j));
+      }
+      if (j + 1 < n_w) {
+        if (j + 1 >= j_mask) mask(s_nxt, (j + 1) * kBKV);
+        update_max(s_nxt);
+      }
     }
   };
 
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query registers and prologue tiles
   __builtin_amdgcn_s_barrier();
   f32x16 sa[2], sb[2];
-  if (n_w > 0) qk(kbuf(0), sa);
+  if (n_w > 0) {
+    qk(kbuf(0), sa);
+    if (j_mask == 0) mask(sa, 0);
+    update_max(sa);
+  }
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
     step(j, sa, sb);
