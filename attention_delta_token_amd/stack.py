@@ -98,7 +98,8 @@ class ThresholdStack:
     updates the counters and compacts the surviving queries; keys and values
     stay full length (halted tokens keep their K/V)."""
 
-    def __init__(self, layers: list[LayerTensors], tau_rank: int, patience: int = 2, record: bool = False):
+    def __init__(self, layers: list[LayerTensors], tau_rank: int, patience: int = 2, record: bool = False,
+                 record_outputs: bool = True):
         self.layers = layers
         self.rank = tau_rank
         self.patience = patience
@@ -116,7 +117,8 @@ class ThresholdStack:
         self.Oa = torch.empty(S, Hq * D, device=dev, dtype=dt)
         dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
         self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
-        self.record = record
+        self.record = record                  # keep per-layer host-visible copies (tests, measurement)
+        self.record_outputs = record_outputs  # ... including scores and U, not only the active sets
         self.trace = []
 
     def run(self) -> None:
@@ -128,7 +130,7 @@ class ThresholdStack:
         L.dash_select(self.score, self.pos[0], mode=L.DASH_SEL_THRESHOLD, tau=self.tau, patience=self.patience,
                       counters=self.counters, n_max=S, n_out=self.n[0])
         if self.record:
-            self.trace.append((None, self.score.clone()))
+            self.trace.append((None, self.score.clone() if self.record_outputs else None))
         cur = 0
         for l in range(1, len(self.layers)):
             x = self.layers[l]
@@ -137,7 +139,10 @@ class ThresholdStack:
             L.dash_attn_active(self.Qa, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=pos, n_dev=n, n_max=S, Wo=x.Wo,
                                Ua=self.U, score=self.score, ws=self.ws, S=S)
             if self.record:
-                self.trace.append((pos.clone(), n.clone(), self.score.clone(), self.U.clone()))
+                if self.record_outputs:
+                    self.trace.append((pos.clone(), n.clone(), self.score.clone(), self.U.clone()))
+                else:
+                    self.trace.append((pos.clone(), n.clone()))
             nxt = cur ^ 1
             L.dash_select(self.score, self.pos[nxt], mode=L.DASH_SEL_THRESHOLD, tau=self.tau,
                           patience=self.patience, counters=self.counters, pos=pos, n_dev=n, n_max=S,
