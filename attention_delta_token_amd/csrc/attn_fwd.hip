@@ -40,6 +40,9 @@ constexpr int kAttnThreads = 256;
 constexpr int kBQ = 128;  // queries per workgroup
 constexpr int kBKV = 64;  // keys per step
 constexpr float kLazyLog2 = 8.0f;  // slack of the lazily updated softmax maximum
+#ifndef DASH_ATTN_SCHED
+#define DASH_ATTN_SCHED 1
+#endif
 
 // Logical (query tile, q-head) of workgroup `bid`: pairs (query tile, kv-head)
 // are enumerated heaviest query tile first; the g q-heads of a pair land on
@@ -341,6 +344,23 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       qk(kbuf(j + 1), s_nxt);
       softmax(s_cur);
       pv(s_cur, vbuf(j));
+#if DASH_ATTN_SCHED
+      // Interleave: operand reads run a few MFMAs ahead; each score MFMA is
+      // followed by softmax vector work, each PV MFMA by its next operand reads.
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // 6 LDS reads up front
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // 6 VALU or transcendental
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);  // 2 VALU or transcendental
+      }
+#endif
       update_max(s_nxt);
     } else {
       if (j + 1 < n_w) qk(kbuf(j + 1), s_nxt);
