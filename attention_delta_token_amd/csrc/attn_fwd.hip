@@ -40,9 +40,6 @@ constexpr int kAttnThreads = 256;
 constexpr int kBQ = 128;  // queries per workgroup
 constexpr int kBKV = 64;  // keys per step
 constexpr float kLazyLog2 = 8.0f;  // slack of the lazily updated softmax maximum
-#ifndef DASH_ATTN_SCHED
-#define DASH_ATTN_SCHED 1
-#endif
 
 // Logical (query tile, q-head) of workgroup `bid`: pairs (query tile, kv-head)
 // are enumerated heaviest query tile first; the g q-heads of a pair land on
@@ -208,12 +205,18 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   if (n_tiles > 1) kload.issue(k_src, kbuf(1), tile_bytes);
   vload.issue(v_src, vbuf(0), 0u);
 
-  // This lane's query as the B operand of S^T = K Q^T: 8 dims per k-step.
+  // This lane's query as the B operand of S^T = K Q^T: 8 dims per k-step,
+  // pre-multiplied by log2(e)/sqrt(D) (rounded to bf16) so the scores come out
+  // in exp2 units.
   bf16x8 qreg[D / 16];
   {
     const uint16_t* qp = Q + static_cast<size_t>(qrow_c) * q_ld + h * D + hi * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[ks][e] = static_cast<__bf16>(static_cast<float>(raw[e]) * c_log2);
+    }
   }
 
   f32x16 o[D / 32];
@@ -221,8 +224,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   for (int i = 0; i < D / 32; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  float m_run = -__builtin_inff();
-  float mc = -__builtin_inff();  // m_run * c_log2
+  float m_run = 0.f;  // reference maximum (exp2 units); score tiles hold S - m_run
   float l_run = 0.f;
 
   // K operand offsets: row kb*32 + l32, chunk 2*ks + hi (the kb term is an immediate).
@@ -241,12 +243,14 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     voffs[db] = row * C::kRowBytes + 16 * v_slot<D>(row, e >> 3) + 2 * (e & 7);
   }
 
-  // S^T for one key tile: 2 blocks of 32 keys x this wave's 32 queries.
-  auto qk = [&](const unsigned char* kst, f32x16 (&s)[2]) {
+  // S^T - m for one key tile: 2 blocks of 32 keys x this wave's 32 queries; the
+  // accumulators start at -m (m = this lane's reference maximum), so the
+  // softmax numerator is a bare exp2.
+  auto qk = [&](const unsigned char* kst, f32x16 (&s)[2], float init) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[kb][r] = init;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
@@ -272,20 +276,24 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // tile exceeds it by more than 2^kLazyLog2 in exp2 units (P then stays below
   // 2^kLazyLog2) and rescales the accumulators for it.  Called on tile j+1 at
   // the end of step j, so step j+1 itself needs no branch.
-  auto update_max = [&](const f32x16 (&s)[2]) {
+  // The tile holds S - m_run; `first` marks the first tile (m_run not set yet).
+  auto update_max = [&](f32x16 (&s)[2], bool first) {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool grow = (mx - m_run) * c_log2 > kLazyLog2;
+    const bool grow = first || mx > kLazyLog2;
     if (__any(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-      m_run = m_new;
-      mc = m_new * c_log2;
+      const float delta = grow ? mx : 0.f;
+      const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-delta);
+      m_run = first ? mx : m_run + delta;
       l_run *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
@@ -293,30 +301,33 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
   };
 
-  // Softmax numerator of a tile in place against the current reference maximum.
+  // Softmax numerator of a tile in place: P = exp2(S - m_run).
   auto softmax = [&](f32x16 (&s)[2]) {
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -mc));
-        s[kb][r] = p;
-        psum += p;
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r]);
   };
 
   // O^T += V^T P^T for one tile: P rounded to bf16 as the B operand; the V^T
-  // operand (8 keys of one d per lane) comes from two transposing reads.
+  // operand (8 keys of one d per lane) comes from two transposing reads.  The
+  // softmax denominator adds the same rounded P (two at a time with a bf16 dot).
   auto pv = [&](const f32x16 (&s)[2], const unsigned char* vst) {
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float psum = 0.f;
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp) {
       const int kb = stp >> 1;
       const int sub = stp & 1;
       u32x4 pw;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) pw[t] = pack_bf16x2(s[kb][8 * sub + 2 * t], s[kb][8 * sub + 2 * t + 1]);
+      for (int t = 0; t < 4; ++t) {
+        bf16x2 pr;
+        pr[0] = static_cast<__bf16>(s[kb][8 * sub + 2 * t]);
+        pr[1] = static_cast<__bf16>(s[kb][8 * sub + 2 * t + 1]);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+        pw[t] = __builtin_bit_cast(uint32_t, pr);
+      }
       const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
@@ -328,6 +339,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), pb, o[db]);
       }
     }
+    l_run += psum;
   };
 
   // Step j: wait for K(j+1) and V(j), refill the freed buffers with K(j+2) and
@@ -341,36 +353,19 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     if (j + 2 < n_tiles) kload.issue(k_src, kbuf(j), static_cast<uint32_t>(j + 2) * tile_bytes);
     if (j + 1 < n_tiles) vload.issue(v_src, vbuf(j + 1), static_cast<uint32_t>(j + 1) * tile_bytes);
     if (j + 1 < j_mask) {  // steady state: tile j+1 fully visible
-      qk(kbuf(j + 1), s_nxt);
+      qk(kbuf(j + 1), s_nxt, -m_run);
       softmax(s_cur);
       pv(s_cur, vbuf(j));
-#if DASH_ATTN_SCHED
-      // Interleave: operand reads run a few MFMAs ahead; each score MFMA is
-      // followed by softmax vector work, each PV MFMA by its next operand reads.
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // 6 LDS reads up front
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // 6 VALU or transcendental
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);  // 2 VALU or transcendental
-      }
-#endif
-      update_max(s_nxt);
+      update_max(s_nxt, false);
     } else {
-      if (j + 1 < n_w) qk(kbuf(j + 1), s_nxt);
+      if (j + 1 < n_w) qk(kbuf(j + 1), s_nxt, -m_run);
       if (j < n_w) {
         softmax(s_cur);
         pv(s_cur, vbuf(j));
       }
       if (j + 1 < n_w) {
         if (j + 1 >= j_mask) mask(s_nxt, (j + 1) * kBKV);
-        update_max(s_nxt);
+        update_max(s_nxt, false);
       }
     }
   };
@@ -379,9 +374,9 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   __builtin_amdgcn_s_barrier();
   f32x16 sa[2], sb[2];
   if (n_w > 0) {
-    qk(kbuf(0), sa);
+    qk(kbuf(0), sa, 0.f);
     if (j_mask == 0) mask(sa, 0);
-    update_max(sa);
+    update_max(sa, true);
   }
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
