@@ -28,6 +28,10 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 2048;
+// Each histogram is kept in kCopies copies, lane l counting into copy l % kCopies:
+// scores cluster in a few top-digit bins, and the copies cut the same-address
+// LDS atomic conflicts of one wave by that factor.
+constexpr int kCopies = 8;
 
 // Order-preserving key: larger score -> larger key.  NaN -> 0 (below every
 // number, including -inf whose key is 0x007fffff); -0 and +0 share one key.
@@ -77,11 +81,13 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* sh_wav
   return res;
 }
 
-// Find the key of the kk-th largest (1-based) among `n` keys of `row`.
-// Returns the cut key; *take_eq = how many keys equal to it are ranked within
-// the top kk (the kk - #greater lowest-position ones).
-__device__ uint32_t radix_cut(const float* __restrict__ row, int n, uint32_t kk, uint32_t* hist,
-                              uint64_t* sh_scan, uint32_t* sh_cut, uint32_t* take_eq) {
+// Find the key of the kk-th largest (1-based) among the keys visited by
+// `for_keys(f)` (which calls f(key) for each of this thread's keys).  Returns
+// the cut key; *take_eq = how many keys equal to it are ranked within the top
+// kk (the kk - #greater lowest-position ones).
+template <class ForKeys>
+__device__ uint32_t radix_cut(ForKeys for_keys, uint32_t kk, uint32_t* hist, uint64_t* sh_scan, uint32_t* sh_cut,
+                              uint32_t* take_eq) {
   uint32_t prefix = 0u, pmask = 0u;
   const int shifts[3] = {21, 10, 0};
   const uint32_t dmask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
@@ -89,18 +95,24 @@ __device__ uint32_t radix_cut(const float* __restrict__ row, int n, uint32_t kk,
   for (int pass = 0; pass < 3; ++pass) {
     const int sh = shifts[pass];
     const uint32_t dm = dmask[pass];
-    for (int b = threadIdx.x; b < kBins; b += kSelThreads) hist[b] = 0u;
+    for (int b = threadIdx.x; b < kCopies * kBins; b += kSelThreads) hist[b] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-      const uint32_t key = score_key(row[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1u);
-    }
+    uint32_t* my_hist = hist + (threadIdx.x % kCopies) * kBins;
+    for_keys([&](uint32_t key) {
+      if ((key & pmask) == prefix) atomicAdd(&my_hist[(key >> sh) & dm], 1u);
+    });
     __syncthreads();
     // Suffix sums over bins (from the top): each thread owns 2 consecutive bins.
     const int nb = static_cast<int>(dm) + 1;
     const int b0 = 2 * threadIdx.x;
-    uint32_t c0 = (b0 < nb) ? hist[b0] : 0u;
-    uint32_t c1 = (b0 + 1 < nb) ? hist[b0 + 1] : 0u;
+    uint32_t c0 = 0u, c1 = 0u;
+    if (b0 < nb) {
+#pragma unroll
+      for (int c = 0; c < kCopies; ++c) {
+        c0 += hist[c * kBins + b0];
+        c1 += hist[c * kBins + b0 + 1];
+      }
+    }
     uint64_t tot;
     const uint32_t mine = c0 + c1;
     // Exclusive prefix over bins below 2t; keys strictly above bin 2t+1 = total - prefix - mine.
@@ -126,6 +138,16 @@ __device__ uint32_t radix_cut(const float* __restrict__ row, int n, uint32_t kk,
   *take_eq = kk;
   return prefix;
 }
+
+// Keys of one score row read from global memory on every pass.
+struct RowKeys {
+  const float* row;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void operator()(F&& f) const {
+    for (int i = threadIdx.x; i < n; i += kSelThreads) f(score_key(row[i]));
+  }
+};
 
 // Emit, in ascending position order, every i with key > cut plus the first
 // `take_eq` positions with key == cut.  out_map != nullptr maps i -> out_map[i].
@@ -177,7 +199,7 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
 __global__ __launch_bounds__(kSelThreads, 1)
 void topk_kernel(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ pos,
                  int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   __shared__ uint32_t sh_cut[2];
   const int row = blockIdx.x;
@@ -185,14 +207,66 @@ void topk_kernel(const float* __restrict__ score, int n, int k, const int32_t* _
   int32_t* out = idx + static_cast<size_t>(row) * k;
   if (k == 0) return;
   uint32_t take_eq;
-  const uint32_t cut = radix_cut(r, n, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
+  const uint32_t cut = radix_cut(RowKeys{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
   emit_selected(r, n, cut, take_eq, pos, out, sh_scan);
+}
+
+// Rows of up to kSelThreads * ITEMS scores: each thread loads its ITEMS
+// consecutive scores once, keeps their keys in registers for the three radix
+// passes, and emits its survivors after one workgroup scan (thread order is
+// position order).
+template <int ITEMS>
+__global__ __launch_bounds__(kSelThreads, 1)
+void topk_reg_kernel(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ pos,
+                     int32_t* __restrict__ idx) {
+  static_assert(ITEMS <= 32, "masks are 32-bit");
+  __shared__ uint32_t hist[kCopies * kBins];
+  __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
+  __shared__ uint32_t sh_cut[2];
+  const int rowi = blockIdx.x;
+  const float* r = score + static_cast<size_t>(rowi) * n;
+  int32_t* out = idx + static_cast<size_t>(rowi) * k;
+  if (k == 0) return;
+  const int i0 = threadIdx.x * ITEMS;
+  uint32_t keys[ITEMS];
+#pragma unroll
+  for (int e = 0; e < ITEMS; ++e) keys[e] = (i0 + e < n) ? score_key(r[i0 + e]) : 0u;
+  const int valid = n - i0;  // keys e < valid exist
+  auto for_keys = [&](auto&& f) {
+#pragma unroll
+    for (int e = 0; e < ITEMS; ++e)
+      if (e < valid) f(keys[e]);
+  };
+  uint32_t take_eq;
+  const uint32_t cut = radix_cut(for_keys, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
+  uint32_t gt_mask = 0u, eq_mask = 0u;
+#pragma unroll
+  for (int e = 0; e < ITEMS; ++e) {
+    if (e < valid) {
+      if (keys[e] > cut) gt_mask |= 1u << e;
+      else if (keys[e] == cut) eq_mask |= 1u << e;
+    }
+  }
+  const uint32_t gt = __popc(gt_mask), eq = __popc(eq_mask);
+  uint64_t tot;
+  const uint64_t excl = block_excl_scan((static_cast<uint64_t>(gt) << 32) | eq, sh_scan, tot);
+  uint32_t eq_rank = static_cast<uint32_t>(excl & 0xffffffffu);
+  uint32_t o = static_cast<uint32_t>(excl >> 32) + (eq_rank < take_eq ? eq_rank : take_eq);
+#pragma unroll
+  for (int e = 0; e < ITEMS; ++e) {
+    bool take = (gt_mask >> e) & 1u;
+    if ((eq_mask >> e) & 1u) { take = eq_rank < take_eq; ++eq_rank; }
+    if (take) {
+      out[o] = pos ? pos[i0 + e] : i0 + e;
+      ++o;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads, 1)
 void order_stat_kernel(const float* __restrict__ score, const int32_t* __restrict__ n_dev, int n_max,
                        int rank, float* __restrict__ tau_out) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   __shared__ uint32_t sh_cut[2];
   int n = n_dev ? *n_dev : n_max;
@@ -203,7 +277,7 @@ void order_stat_kernel(const float* __restrict__ score, const int32_t* __restric
   }
   uint32_t take_eq;
   // rank-th smallest == (n - rank + 1)-th largest under the same total order.
-  const uint32_t cut = radix_cut(score, n, static_cast<uint32_t>(n - rank + 1), hist, sh_scan, sh_cut,
+  const uint32_t cut = radix_cut(RowKeys{score, n}, static_cast<uint32_t>(n - rank + 1), hist, sh_scan, sh_cut,
                                  &take_eq);
   if (threadIdx.x == 0) *tau_out = key_score(cut);
 }
@@ -252,7 +326,16 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
 hipError_t launch_topk(const float* score, int rows, int n, int k, const int32_t* pos, int32_t* idx,
                        hipStream_t stream) {
   if (rows == 0 || k == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+  if (n <= kSelThreads * 4)
+    hipLaunchKernelGGL(topk_reg_kernel<4>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+  else if (n <= kSelThreads * 8)
+    hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+  else if (n <= kSelThreads * 16)
+    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+  else if (n <= kSelThreads * 32)
+    hipLaunchKernelGGL(topk_reg_kernel<32>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+  else
+    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
   return hipGetLastError();
 }
 

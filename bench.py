@@ -255,10 +255,33 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.profile_only:
+        out["select_sweep"] = [select_sweep(dash, torch, dev, rows, n) for rows, n in ((2048, 8192), (256, 65536))]
+
     if not args.no_cpu_baseline and not args.profile_only:
         out["cpu_baseline"] = cpu_baseline(w, host_keep, step, k_rows)
 
     print(json.dumps(out), flush=True)
+
+
+def select_sweep(dash, torch, dev, rows=256, n=65536):
+    """Top-k over a batch of independent score rows (one workgroup per row), the
+    regime where selection is bandwidth-bound: 4 B read per score + 4 B written
+    per kept index."""
+    k = n // 2
+    g = torch.Generator(device=dev).manual_seed(0)
+    score = torch.rand(rows, n, device=dev, generator=g)
+    idx = torch.empty(rows, k, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        dash.dash_select(score, idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows)
+    dash.trace_start(16)
+    for _ in range(5):
+        dash.dash_select(score, idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows)
+    dash.trace_stop()
+    t = [ms for op, ms in dash.trace_read(16) if op == "select"]
+    ms = sum(t) / len(t)
+    gbps = rows * (4.0 * n + 4.0 * k) / (ms * 1e-3) / 1e9
+    return {"rows": rows, "n": n, "k": k, "ms": ms, "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS}
 
 
 def describe(w):

@@ -64,7 +64,7 @@ def selection_within_cut(gpu_idx, ref_score, k, rel=TOL_SCORE):
 # selection (bit-exact on identical score vectors)
 # ---------------------------------------------------------------------------
 
-SEL_SIZES = [1, 5, 64, 1000, 4097, 8192, 65536 + 17, 131072]
+SEL_SIZES = [1, 5, 64, 1000, 4096, 4097, 8192, 16383, 32768, 32769, 65536 + 17, 131072]
 
 
 @pytest.mark.parametrize("n", SEL_SIZES)
