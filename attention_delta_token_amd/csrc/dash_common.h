@@ -35,6 +35,10 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Map a linear workgroup id so that workgroups dispatched to the same XCD
 // (ids congruent mod 8 land on the same XCD under round-robin dispatch) get
 // consecutive logical tiles, which then share that XCD's L2.

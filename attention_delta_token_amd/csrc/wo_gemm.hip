@@ -17,6 +17,9 @@
 // rounded to bf16.  Each (row, 128-column tile) partial is written to the
 // workspace and a finalize kernel adds the partials in a fixed order and takes
 // the square root, so the score is bit-reproducible run to run (no atomics).
+#include <cstdlib>
+#include <cstring>
+
 #include "dash_common.h"
 #include "dash_kernels.h"
 
@@ -35,8 +38,6 @@ constexpr int kRowsPerLine = 256 / kRowBytes;           // rows sharing one 64-b
 constexpr int kATileBytes = kBM * kRowBytes;            // 32 KiB
 constexpr int kWTileBytes = kBN * kRowBytes;            // 32 KiB
 constexpr int kStageBytes = kATileBytes + kWTileBytes;  // 64 KiB
-constexpr int kChunksPerStage = kStageBytes / 1024;     // 1 KiB per wave-wide direct load
-constexpr int kLoadsPerWave = kChunksPerStage / (kGemmThreads / 64);  // 8
 constexpr int kGroupM = 4;                              // m-tiles per L2-sharing group
 constexpr int kNB = 4;                                  // 32-column blocks per wave (128 columns)
 constexpr int kMB = 2;                                  // 32-row blocks per wave (64 rows)
@@ -48,14 +49,20 @@ __device__ __forceinline__ int gemm_slot(int row, int chunk) {
   return chunk ^ ((row / kRowsPerLine) % kRowChunks);
 }
 
+template <int BN>
 struct GemmLoadPlan {
-  const uint16_t* src[kLoadsPerWave];  // row start + swizzled chunk, at k = 0
+  static constexpr int kWBytes = BN * kRowBytes;
+  static constexpr int kStage = kATileBytes + kWBytes;
+  static constexpr int kChunks = kStage / 1024;                              // 1 KiB per wave-wide load
+  static constexpr int kPerWave = (kChunks + kGemmThreads / 64 - 1) / (kGemmThreads / 64);
+  static_assert(kStage % 1024 == 0, "whole KiB per stage");
+  const uint16_t* src[kPerWave];  // row start + swizzled chunk, at k = 0
   __device__ __forceinline__ void init(const uint16_t* A, const uint16_t* W, int m0, int n0, int M, int N, int K) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     constexpr int kRowsPerKiB = 1024 / kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-      const int q = wave + 8 * i;  // 1 KiB chunk of the stage
+    for (int i = 0; i < kPerWave; ++i) {
+      const int q = min(wave + 8 * i, kChunks - 1);  // 1 KiB chunk of the stage
       const int is_a = q < kATileBytes / 1024;
       const int local_row = (is_a ? q : q - kATileBytes / 1024) * kRowsPerKiB + lane / kRowChunks;
       const int chunk = gemm_slot(local_row, lane % kRowChunks);
@@ -67,10 +74,11 @@ struct GemmLoadPlan {
   __device__ __forceinline__ void issue(unsigned char* stage, int k0) const {
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
+    for (int i = 0; i < kPerWave; ++i) {
       const int q = wave + 8 * i;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + k0),
-                                       (__attribute__((address_space(3))) void*)(stage + q * 1024), 16, 0, 0);
+      if (kChunks % 8 == 0 || q < kChunks)  // wave-uniform
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + k0),
+                                         (__attribute__((address_space(3))) void*)(stage + q * 1024), 16, 0, 0);
     }
   }
 };
@@ -83,7 +91,6 @@ void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
                          uint16_t* __restrict__ U, float* __restrict__ part,
                          const int32_t* __restrict__ m_dev, int M_max, int N, int K, int n_tiles_n,
                          int part_ld) {
-  static_assert(kLoadsPerWave * (kGemmThreads / 64) == kChunksPerStage, "stage split");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * kStageBytes];
   int M = m_dev ? *m_dev : M_max;
   if (M > M_max) M = M_max;
@@ -108,7 +115,7 @@ void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
   const int wm = wave & 3;   // 64-row slice of the tile
   const int wn = wave >> 2;  // 128-column slice of the tile
 
-  GemmLoadPlan plan;
+  GemmLoadPlan<kBN> plan;
   plan.init(A, W, m0, n0, M, N, K);
 
   // Per-lane byte offsets of the 16-byte operand chunk for each 16-wide k-step.
@@ -226,6 +233,149 @@ void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// bf16 path with 224-column tiles.  Same ring, loads and swizzle as above; the
+// 8 waves split the 256x224 tile as 4 (tokens) x 2 (channels), 64 x 112 each,
+// which is 4 x 7 blocks of v_mfma_f32_16x16x32_bf16.  224 divides the hidden
+// width 3584 (Qwen2.5-7B), so row counts that are multiples of 256 fill whole
+// waves of 256 workgroups where 256-column tiles leave part of the chip idle.
+// ---------------------------------------------------------------------------
+constexpr int kBN224 = 224;
+constexpr int kStage224 = kATileBytes + kBN224 * kRowBytes;  // 60 KiB
+constexpr int kTB = 4;  // 16-token blocks per wave (64 tokens)
+constexpr int kCB = 7;  // 16-channel blocks per wave (112 channels)
+
+__global__ __launch_bounds__(kGemmThreads, 1)
+void wo_gemm_bf16_n224_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                              uint16_t* __restrict__ U, float* __restrict__ part,
+                              const int32_t* __restrict__ m_dev, int M_max, int N, int K, int n_tiles_n,
+                              int part_ld) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kStages * kStage224];
+  int M = m_dev ? *m_dev : M_max;
+  if (M > M_max) M = M_max;
+  const int n_tiles_m = (M_max + kBM - 1) / kBM;
+  const int lid = xcd_remap(blockIdx.x, n_tiles_m * n_tiles_n);
+  const int group = lid / (kGroupM * n_tiles_n);
+  const int gm = min(kGroupM, n_tiles_m - group * kGroupM);
+  const int within = lid - group * kGroupM * n_tiles_n;
+  const int tm = group * kGroupM + within % gm;
+  const int tn = within / gm;
+  const int m0 = tm * kBM;
+  const int n0 = tn * kBN224;
+  if (m0 >= M) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;  // which 8-wide k slice of a 32-wide step this lane supplies
+  const int wm = wave & 3;   // 64-token slice of the tile
+  const int wn = wave >> 2;  // 112-channel slice of the tile
+
+  GemmLoadPlan<kBN224> plan;
+  plan.init(A, W, m0, n0, M, N, K);
+
+  // Operand rows start at multiples of 16, so a lane's swizzled chunk offset
+  // depends only on l16 and the k step.
+  int koff[kBK / 32];
+#pragma unroll
+  for (int ks = 0; ks < kBK / 32; ++ks) koff[ks] = 16 * gemm_slot(l16, 4 * ks + q4);
+  const int a_row = (wm * 64 + l16) * kRowBytes;                   // O rows (B operand)
+  const int w_row = kATileBytes + (wn * 112 + l16) * kRowBytes;    // W rows (A operand)
+
+  f32x4 acc[kCB][kTB];
+#pragma unroll
+  for (int i = 0; i < kCB; ++i)
+#pragma unroll
+    for (int j = 0; j < kTB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = K / kBK;
+  plan.issue(lds, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_vmcnt_0();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < KT) plan.issue(lds + ((kt + 1) & 1) * kStage224, (kt + 1) * kBK);
+    const unsigned char* st = lds + (kt & 1) * kStage224;
+    bf16x8 opw[2][kCB], opa[2][kTB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+      opw[0][cb] = *reinterpret_cast<const bf16x8*>(st + w_row + cb * 16 * kRowBytes + koff[0]);
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb)
+      opa[0][tb] = *reinterpret_cast<const bf16x8*>(st + a_row + tb * 16 * kRowBytes + koff[0]);
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+      opw[1][cb] = *reinterpret_cast<const bf16x8*>(st + w_row + cb * 16 * kRowBytes + koff[1]);
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb)
+      opa[1][tb] = *reinterpret_cast<const bf16x8*>(st + a_row + tb * 16 * kRowBytes + koff[1]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < kTB; ++tb) acc[cb][tb] = mfma16x16x32(opw[ks][cb], opa[ks][tb], acc[cb][tb]);
+  }
+
+  // ---- epilogue -----------------------------------------------------------
+  // acc[cb][tb][r] = U[m][n] with m = m0 + wm*64 + tb*16 + l16,
+  //                  n = n0 + wn*112 + cb*16 + q4*4 + r.
+  wait_lgkm_0();
+  __builtin_amdgcn_s_barrier();
+  float* red = reinterpret_cast<float*>(lds);              // [2 wn][256 m] partial sums
+  uint16_t* ct = reinterpret_cast<uint16_t*>(lds + 4096);  // staging [256 m][kLdsC]
+  constexpr int kLdsC = kBN224 + 8;
+  static_assert(4096 + kBM * kLdsC * 2 <= kStages * kStage224, "staging fits the ring");
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) {
+    float ss = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int nl = wn * 112 + cb * 16 + q4 * 4 + r;
+        const float v = (n0 + nl < N) ? acc[cb][tb][r] : 0.f;
+        ss += v * v;
+      }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    if (q4 == 0) red[wn * kBM + wm * 64 + tb * 16 + l16] = ss;
+    const int ml = wm * 64 + tb * 16 + l16;
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      const int nl = wn * 112 + cb * 16 + q4 * 4;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[cb][tb][0], acc[cb][tb][1]);
+      pk[1] = pack_bf16x2(acc[cb][tb][2], acc[cb][tb][3]);
+      *reinterpret_cast<u32x2*>(ct + ml * kLdsC + nl) = pk;
+    }
+  }
+  __syncthreads();
+  // Coalesced store of 256 rows x 28 chunks of 16 bytes.
+  constexpr int kChunksRow = kBN224 / 8;
+#pragma unroll 2
+  for (int i = 0; i < (kBM * kChunksRow) / kGemmThreads; ++i) {
+    const int c = tid + i * kGemmThreads;
+    const int row = c / kChunksRow;
+    const int cc = c - row * kChunksRow;
+    const int m = m0 + row;
+    const int n = n0 + cc * 8;
+    if (m < M && n < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ct + row * kLdsC + cc * 8);
+      if (n + 8 <= N) {
+        *reinterpret_cast<u32x4*>(U + static_cast<size_t>(m) * N + n) = v;
+      } else {
+        for (int j = 0; j < N - n; ++j)
+          U[static_cast<size_t>(m) * N + n + j] = static_cast<uint16_t>(v[j >> 1] >> (16 * (j & 1)));
+      }
+    }
+  }
+  if (part && tid < kBM) {
+    const int m = m0 + tid;
+    if (m < M) part[static_cast<size_t>(tn) * part_ld + m] = red[tid] + red[kBM + tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path (small workloads): 64x64 tile, 4x4 outputs per thread, VALU FMA.
 // ---------------------------------------------------------------------------
 constexpr int kF32Tile = 64;
@@ -312,21 +462,62 @@ void score_finalize_kernel(const float* __restrict__ part, int n_parts, int part
 
 }  // namespace
 
+namespace {
+
+int device_cus() {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  return cus;
+}
+
+// Column tile for the bf16 path: the width whose whole waves of workgroups
+// (one per CU) cost least, a wave of 224-wide tiles counting 224/256 of a
+// wave of 256-wide ones.
+// DASH_WO_TILE_N=224 or 256 in the environment forces one of the two (tests
+// use it to cover both kernels at small sizes).
+int bf16_tile_n(int M, int N) {
+  if (const char* f = std::getenv("DASH_WO_TILE_N")) {
+    if (std::strcmp(f, "224") == 0) return kBN224;
+    if (std::strcmp(f, "256") == 0) return kBN;
+  }
+  const long tm = (M + kBM - 1) / kBM;
+  const long cus = device_cus();
+  const long w256 = (tm * ((N + kBN - 1) / kBN) + cus - 1) / cus;
+  const long w224 = (tm * ((N + kBN224 - 1) / kBN224) + cus - 1) / cus;
+  return w224 * kBN224 < w256 * kBN ? kBN224 : kBN;
+}
+
+}  // namespace
+
 int wo_gemm_parts(int dtype, int N) {
-  const int bn = dtype == 1 ? kBN : kF32Tile;
-  return (N + bn - 1) / bn;
+  // Upper bound over the column tiles the launcher may pick (sizes the workspace).
+  if (dtype == 1) return (N + kBN224 - 1) / kBN224;
+  return (N + kF32Tile - 1) / kF32Tile;
 }
 
 hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, float* score, float* part,
                           const int32_t* m_dev, int M_max, int N, int K, hipStream_t stream) {
   if (M_max <= 0) return hipSuccess;
-  const int parts = wo_gemm_parts(dtype, N);
+  int parts;
   if (dtype == 1) {
+    const int bn = bf16_tile_n(M_max, N);
+    parts = (N + bn - 1) / bn;
     const int tm = (M_max + kBM - 1) / kBM;
-    hipLaunchKernelGGL(wo_gemm_bf16_kernel, dim3(tm * parts), dim3(kGemmThreads), 0, stream,
-                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
-                       static_cast<uint16_t*>(U), score ? part : nullptr, m_dev, M_max, N, K, parts, M_max);
+    if (bn == kBN224)
+      hipLaunchKernelGGL(wo_gemm_bf16_n224_kernel, dim3(tm * parts), dim3(kGemmThreads), 0, stream,
+                         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
+                         static_cast<uint16_t*>(U), score ? part : nullptr, m_dev, M_max, N, K, parts, M_max);
+    else
+      hipLaunchKernelGGL(wo_gemm_bf16_kernel, dim3(tm * parts), dim3(kGemmThreads), 0, stream,
+                         static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W),
+                         static_cast<uint16_t*>(U), score ? part : nullptr, m_dev, M_max, N, K, parts, M_max);
   } else {
+    parts = (N + kF32Tile - 1) / kF32Tile;
     hipLaunchKernelGGL(wo_gemm_f32_kernel, dim3(parts, (M_max + kF32Tile - 1) / kF32Tile), dim3(256), 0, stream,
                        static_cast<const float*>(A), static_cast<const float*>(W), static_cast<float*>(U),
                        score ? part : nullptr, m_dev, M_max, N, K, M_max);

@@ -111,6 +111,9 @@ size_t dash_workspace_size(void* ctx, int op, const dash_shape* s, int n_max);
  *   rounded to dtype.  score == NULL skips the score.
  * Supported: dtype bf16 with D in {64, 128}; dtype fp32 with D <= 128 and
  * D % 4 == 0 (reference-speed kernels).  hidden % 4 == 0; Hq % Hkv == 0.
+ * The bf16 W_o GEMM picks 224- or 256-column tiles, whichever fills the
+ * chip's compute units in fewer tile-widths of work; the environment variable
+ * DASH_WO_TILE_N=224 or =256 forces one (read at every launch; for tests).
  * Workspace: dash_workspace_size(DASH_OP_ATTN_LAYER, s, S). */
 int dash_attn_layer(void* ctx, const dash_shape* s,
                     const void* Q, const void* K, const void* V, const void* Wo,

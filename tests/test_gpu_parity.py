@@ -237,13 +237,17 @@ def _run_layer(dash, x, dtype=torch.bfloat16, with_score=True):
     return host(O), host(U), (host(score) if with_score else None)
 
 
+@pytest.mark.parametrize("tile_n", ["auto", "224", "256"])
 @pytest.mark.parametrize("S,Hq,Hkv,D,hidden", [
     (1, 2, 1, 128, 256), (77, 4, 2, 64, 128), (300, 8, 2, 128, 384), (640, 28, 4, 128, 3584),
     (1000, 32, 8, 128, 4096), (129, 7, 7, 64, 200),
 ])
-def test_attn_layer_bf16(dash, S, Hq, Hkv, D, hidden):
+def test_attn_layer_bf16(dash, monkeypatch, S, Hq, Hkv, D, hidden, tile_n):
+    """tile_n forces the W_o GEMM's 224- or 256-column tile kernel (auto: the launcher's choice)."""
+    if tile_n != "auto":
+        monkeypatch.setenv("DASH_WO_TILE_N", tile_n)
     x = _layer(S, Hq, Hkv, D, hidden, seed=S)
-    say("attn_layer bf16", S, Hq, Hkv, D, hidden)
+    say("attn_layer bf16", S, Hq, Hkv, D, hidden, "tile_n", tile_n)
     O, U, score = _run_layer(dash, x)
     O_ref, U_ref, s_ref = oracle.attention_layer(x["Q"], x["K"], x["V"], x["Wo"])
     assert maxrel(O, O_ref) <= TOL_BF16
