@@ -143,6 +143,37 @@ def select_topk(score, k: int) -> np.ndarray:
     return np.sort(order[:k]).astype(np.int32)
 
 
+def effective_keep_count(T: int, keep: float, keep_first: int, keep_last: int) -> int:
+    """K_eff = f + l + floor(keep * (T - f - l)) with f = keep_first, l =
+    keep_last and keep = 1 - ρ, [P1] §3.1 (forced retention of the first and
+    last tokens, and the resulting kept count) and §3.3 (the sketch's total
+    kept count).  Requires f + l <= T."""
+    if keep_first < 0 or keep_last < 0 or keep_first + keep_last > T:
+        raise ValueError("forced counts out of range")
+    return keep_first + keep_last + int(math.floor(keep * (T - keep_first - keep_last)))
+
+
+def select_topk_forced(score, k: int, keep_first: int, keep_last: int) -> np.ndarray:
+    """Top-k with forced retention, [P1] §3.1 and §3.3: positions
+    0..keep_first-1 and T-keep_last..T-1 are always kept, and the other
+    k - keep_first - keep_last kept positions are the top ones among the
+    middle positions keep_first..T-keep_last-1 (same order as select_topk:
+    larger score first, ties to the lower position).  The result is the
+    ascending union of the three sets (they are disjoint by construction).
+    keep_last = 0 forces no tail token (the prose's meaning; the sketch's
+    slice with 0 would mark every token)."""
+    s = np.asarray(score, dtype=np.float64)
+    n = s.shape[0]
+    f, l = keep_first, keep_last
+    if f < 0 or l < 0 or f + l > n or not f + l <= k <= n:
+        raise ValueError("k or forced counts out of range")
+    middle = s[f:n - l]
+    dyn = select_topk(middle, k - f - l).astype(np.int64) + f
+    head = np.arange(f)
+    tail = np.arange(n - l, n)
+    return np.concatenate([head, dyn, tail]).astype(np.int32)
+
+
 def order_statistic(score, r: int) -> float:
     """τ = the r-th smallest score (1-based, nearest rank), with NaN ranking
     below every number and a zero returned as +0.  Used for the threshold of

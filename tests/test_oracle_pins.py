@@ -238,6 +238,58 @@ def test_keep_counts(golden_dir):
     assert WORKLOADS[3].tau_rank == oracle.percentile_rank(WORKLOADS[3].S, 30) == 19661
 
 
+def brute_topk_forced(score, k, f, l):
+    """Position i is kept iff it is one of the first f or last l, or it lies in
+    the middle and fewer than k - f - l other middle positions beat it."""
+    n = len(score)
+    sel = []
+    for i in range(n):
+        if i < f or i >= n - l:
+            sel.append(i)
+            continue
+        beaten_by = sum(1 for j in range(f, n - l)
+                        if j != i and _beats(float(score[i]), float(score[j]), i, j))
+        if beaten_by < k - f - l:
+            sel.append(i)
+    return np.array(sel, dtype=np.int32)
+
+
+def test_forced_golden(golden_dir):
+    for c in json.load(open(os.path.join(golden_dir, "topk_ties.json")))["forced_cases"]:
+        s = np.array(c["score"], dtype=np.float32)
+        got = oracle.select_topk_forced(s, c["k"], c["f"], c["l"])
+        np.testing.assert_array_equal(got, np.array(c["idx"], dtype=np.int32))
+
+
+def test_forced_counts(golden_dir):
+    for e in json.load(open(os.path.join(golden_dir, "counts.json")))["forced"]:
+        assert oracle.effective_keep_count(e["T"], e["keep"], e["f"], e["l"]) == e["k"]
+    with pytest.raises(ValueError):
+        oracle.effective_keep_count(10, 0.5, 6, 5)
+
+
+@pytest.mark.parametrize("kind", SCORE_KINDS)
+@pytest.mark.parametrize("n", [1, 9, 70])
+def test_forced_brute_force(kind, n):
+    s = score_vector(kind, n, seed=3 * n + 1)
+    for f in sorted({0, 1, n // 4} & set(range(n + 1))):
+        for l in sorted({0, 2, n // 5} & set(range(n - f + 1))):
+            for k in sorted({f + l, f + l + 1, (n + f + l) // 2, n} & set(range(f + l, n + 1))):
+                got = oracle.select_topk_forced(s, k, f, l)
+                assert got.shape[0] == k
+                np.testing.assert_array_equal(got, brute_topk_forced(s, k, f, l))
+
+
+def test_forced_reduces_and_rejects():
+    s = score_vector("normal", 50, seed=4)
+    # no forced tokens: plain top-k; everything forced: the identity
+    np.testing.assert_array_equal(oracle.select_topk_forced(s, 20, 0, 0), brute_topk(s, 20))
+    np.testing.assert_array_equal(oracle.select_topk_forced(s, 50, 30, 20), np.arange(50))
+    for bad in ((10, 6, 5), (60, 0, 0), (3, 2, 2), (5, -1, 0)):
+        with pytest.raises(ValueError):
+            oracle.select_topk_forced(s, *bad)
+
+
 # ---------------------------------------------------------------------------
 # order statistic
 # ---------------------------------------------------------------------------
