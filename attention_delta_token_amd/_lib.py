@@ -8,6 +8,7 @@ is raised.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from ctypes import POINTER, Structure, c_char_p, c_int, c_size_t, c_void_p
 
@@ -150,13 +151,22 @@ def dash_attn_layer(Q, K, V, Wo, O, U, score=None, ws=None, stream=None) -> None
 
 def dash_select(score, idx=None, *, mode: int = DASH_SEL_TOPK, k: int = 0, rank: int = 0, tau=None,
                 patience: int = 2, counters=None, pos=None, n_dev=None, n_max: int | None = None, rows: int = 1,
-                n_out=None, tau_out=None, stream=None) -> None:
-    """Top-k / order statistic / threshold step (see include/dash.h)."""
+                n_out=None, tau_out=None, keep_first: int = 0, keep_last: int = 0, stream=None) -> None:
+    """Top-k / order statistic / threshold step (see include/dash.h).  For top-k
+    with forced retention, k is the total kept count (see effective_keep)."""
     if n_max is None:
         n_max = score.shape[-1] if score is not None else 0
-    sel = DashSel(mode, k, rank, _ptr(tau), patience, _ptr(counters), 0, 0)
+    sel = DashSel(mode, k, rank, _ptr(tau), patience, _ptr(counters), keep_first, keep_last)
     _check(load().dash_select(None, ctypes.byref(sel), _ptr(score), _ptr(pos), _ptr(n_dev), n_max, rows,
                               _ptr(idx), _ptr(n_out), _ptr(tau_out), None, 0, _stream(stream)))
+
+
+def effective_keep(T: int, keep: float, keep_first: int = 0, keep_last: int = 0) -> int:
+    """Kept count with forced retention: keep_first + keep_last plus floor(keep *
+    (T - keep_first - keep_last)) chosen by score (keep = 1 - pruning ratio)."""
+    if keep_first < 0 or keep_last < 0 or keep_first + keep_last > T:
+        raise ValueError("keep_first + keep_last must lie in [0, T]")
+    return keep_first + keep_last + int(math.floor(keep * (T - keep_first - keep_last)))
 
 
 def dash_compact(idx, X, Xa, n_dev=None, n_max: int | None = None, stream=None) -> None:

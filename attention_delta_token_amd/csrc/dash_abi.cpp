@@ -242,8 +242,8 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
                 size_t /*ws_bytes*/, void* stream) {
   try {
     if (!p) return fail(DASH_E_INVAL, "selection parameters are NULL");
-    if (p->keep_first != 0 || p->keep_last != 0)
-      return fail(DASH_E_INVAL, "keep_first / keep_last are reserved and must be 0");
+    if (p->mode != DASH_SEL_TOPK && (p->keep_first != 0 || p->keep_last != 0))
+      return fail(DASH_E_INVAL, "keep_first / keep_last apply to top-k only and must be 0 here");
     if (n_max < 0 || n_max > (1 << 30)) return fail(DASH_E_INVAL, "n_max %d out of range", n_max);
     if (rows < 1 || rows > (1 << 20)) return fail(DASH_E_INVAL, "rows %d out of range", rows);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -252,6 +252,10 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
     switch (p->mode) {
       case DASH_SEL_TOPK: {
         if (p->k < 0 || p->k > n_max) return fail(DASH_E_INVAL, "k = %d outside [0, %d]", p->k, n_max);
+        if (p->keep_first < 0 || p->keep_last < 0 ||
+            static_cast<int64_t>(p->keep_first) + p->keep_last > p->k)
+          return fail(DASH_E_INVAL, "forced counts keep_first %d + keep_last %d must lie in [0, k = %d]",
+                      p->keep_first, p->keep_last, p->k);
         if (n_dev) return fail(DASH_E_INVAL, "top-k takes its length from n_max (n_dev must be NULL)");
         if (pos && rows != 1) return fail(DASH_E_INVAL, "pos is supported for a single row only");
         if (static_cast<int64_t>(rows) * n_max > (1ll << 31) - 1)
@@ -260,7 +264,7 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
         if (!score) return fail(DASH_E_INVAL, "score is NULL");
         if (!idx) return fail(DASH_E_INVAL, "idx is NULL");
         tr = trace_open(DASH_TR_SELECT, st);
-        e = dash::launch_topk(score, rows, n_max, p->k, pos, idx, st);
+        e = dash::launch_topk(score, rows, n_max, p->k, p->keep_first, p->keep_last, pos, idx, st);
         break;
       }
       case DASH_SEL_ORDER_STAT: {

@@ -15,8 +15,8 @@ int wo_gemm_parts(int dtype, int N);
 hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, float* score, float* part,
                           const int32_t* m_dev, int M_max, int N, int K, hipStream_t stream);
 
-hipError_t launch_topk(const float* score, int rows, int n, int k, const int32_t* pos, int32_t* idx,
-                       hipStream_t stream);
+hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
+                       const int32_t* pos, int32_t* idx, hipStream_t stream);
 hipError_t launch_order_stat(const float* score, const int32_t* n_dev, int n_max, int rank, float* tau_out,
                              hipStream_t stream);
 hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,

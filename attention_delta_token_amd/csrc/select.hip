@@ -150,9 +150,10 @@ struct RowKeys {
 };
 
 // Emit, in ascending position order, every i with key > cut plus the first
-// `take_eq` positions with key == cut.  out_map != nullptr maps i -> out_map[i].
+// `take_eq` positions with key == cut, as first + i, or out_map[i] when
+// out_map != nullptr.
 __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut, uint32_t take_eq,
-                              const int32_t* __restrict__ out_map, int32_t* __restrict__ out,
+                              const int32_t* __restrict__ out_map, int first, int32_t* __restrict__ out,
                               uint64_t* sh_scan) {
   constexpr int E = 8;  // consecutive elements per thread per chunk
   uint32_t eq_before = 0u, sel_before = 0u;
@@ -183,7 +184,7 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
       if (flags & (1u << e)) take = true;
       else if (flags & (1u << (8 + e))) { take = eq_rank < take_eq; ++eq_rank; }
       if (take) {
-        out[o] = out_map ? out_map[i] : i;
+        out[o] = out_map ? out_map[i] : first + i;
         ++o;
       }
     }
@@ -196,19 +197,34 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
   }
 }
 
+// Forced retention: the first f and last l positions of a row of n_row
+// scores are written to the two ends of its k_total outputs; the caller then
+// selects k_total - f - l among the middle positions.
+__device__ __forceinline__ void emit_forced(int n_row, int k_total, int f, int l, const int32_t* __restrict__ pos,
+                                            int32_t* __restrict__ out) {
+  for (int i = threadIdx.x; i < f; i += kSelThreads) out[i] = pos ? pos[i] : i;
+  for (int j = threadIdx.x; j < l; j += kSelThreads) {
+    const int i = n_row - l + j;
+    out[k_total - l + j] = pos ? pos[i] : i;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads, 1)
-void topk_kernel(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ pos,
-                 int32_t* __restrict__ idx) {
+void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f, int l,
+                 const int32_t* __restrict__ pos, int32_t* __restrict__ idx) {
   __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   __shared__ uint32_t sh_cut[2];
   const int row = blockIdx.x;
-  const float* r = score + static_cast<size_t>(row) * n;
-  int32_t* out = idx + static_cast<size_t>(row) * k;
+  int32_t* out = idx + static_cast<size_t>(row) * k_total;
+  emit_forced(n_row, k_total, f, l, pos, out);
+  const int n = n_row - f - l;
+  const int k = k_total - f - l;
   if (k == 0) return;
+  const float* r = score + static_cast<size_t>(row) * n_row + f;
   uint32_t take_eq;
   const uint32_t cut = radix_cut(RowKeys{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
-  emit_selected(r, n, cut, take_eq, pos, out, sh_scan);
+  emit_selected(r, n, cut, take_eq, pos ? pos + f : nullptr, f, out + f, sh_scan);
 }
 
 // Rows of up to kSelThreads * ITEMS scores: each thread loads its ITEMS
@@ -217,16 +233,20 @@ void topk_kernel(const float* __restrict__ score, int n, int k, const int32_t* _
 // position order).
 template <int ITEMS>
 __global__ __launch_bounds__(kSelThreads, 1)
-void topk_reg_kernel(const float* __restrict__ score, int n, int k, const int32_t* __restrict__ pos,
-                     int32_t* __restrict__ idx) {
+void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, int f, int l,
+                     const int32_t* __restrict__ pos, int32_t* __restrict__ idx) {
   static_assert(ITEMS <= 32, "masks are 32-bit");
   __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   __shared__ uint32_t sh_cut[2];
   const int rowi = blockIdx.x;
-  const float* r = score + static_cast<size_t>(rowi) * n;
-  int32_t* out = idx + static_cast<size_t>(rowi) * k;
+  int32_t* out = idx + static_cast<size_t>(rowi) * k_total;
+  emit_forced(n_row, k_total, f, l, pos, out);
+  const int n = n_row - f - l;
+  const int k = k_total - f - l;
   if (k == 0) return;
+  const float* r = score + static_cast<size_t>(rowi) * n_row + f;
+  out += f;
   const int i0 = threadIdx.x * ITEMS;
   uint32_t keys[ITEMS];
 #pragma unroll
@@ -257,7 +277,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n, int k, const int32_
     bool take = (gt_mask >> e) & 1u;
     if ((eq_mask >> e) & 1u) { take = eq_rank < take_eq; ++eq_rank; }
     if (take) {
-      out[o] = pos ? pos[i0 + e] : i0 + e;
+      out[o] = pos ? pos[f + i0 + e] : f + i0 + e;
       ++o;
     }
   }
@@ -323,19 +343,21 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
 
 }  // namespace
 
-hipError_t launch_topk(const float* score, int rows, int n, int k, const int32_t* pos, int32_t* idx,
-                       hipStream_t stream) {
+hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
+                       const int32_t* pos, int32_t* idx, hipStream_t stream) {
   if (rows == 0 || k == 0) return hipSuccess;
-  if (n <= kSelThreads * 4)
-    hipLaunchKernelGGL(topk_reg_kernel<4>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
-  else if (n <= kSelThreads * 8)
-    hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
-  else if (n <= kSelThreads * 16)
-    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
-  else if (n <= kSelThreads * 32)
-    hipLaunchKernelGGL(topk_reg_kernel<32>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+  const int f = keep_first, l = keep_last;
+  const int n_mid = n - f - l;
+  if (n_mid <= kSelThreads * 4)
+    hipLaunchKernelGGL(topk_reg_kernel<4>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
+  else if (n_mid <= kSelThreads * 8)
+    hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
+  else if (n_mid <= kSelThreads * 16)
+    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
+  else if (n_mid <= kSelThreads * 32)
+    hipLaunchKernelGGL(topk_reg_kernel<32>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
   else
-    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, pos, idx);
+    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
   return hipGetLastError();
 }
 

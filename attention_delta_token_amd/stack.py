@@ -39,13 +39,16 @@ def _shape_of(layer: LayerTensors):
 
 
 class OneShotStack:
-    """Layers 0..hl full length, top-k at hl, layers hl+1..L-1 on the kept rows."""
+    """Layers 0..hl full length, top-k at hl (optionally forcing the first
+    keep_first and last keep_last tokens in), layers hl+1..L-1 on the kept rows."""
 
-    def __init__(self, layers: list[LayerTensors], halt_layer: int, k: int, kv_mode: int = L.DASH_KV_ACTIVE):
+    def __init__(self, layers: list[LayerTensors], halt_layer: int, k: int, kv_mode: int = L.DASH_KV_ACTIVE,
+                 keep_first: int = 0, keep_last: int = 0):
         self.layers = layers
         self.hl = halt_layer
-        self.k = k
+        self.k = k  # total kept, forced ends included
         self.kv_mode = kv_mode
+        self.keep_first, self.keep_last = keep_first, keep_last
         S, Hq, Hkv, D, hidden = _shape_of(layers[0])
         dev, dt = layers[0].Q.device, layers[0].Q.dtype
         self.S, self.Hq, self.Hkv, self.D, self.hidden = S, Hq, Hkv, D, hidden
@@ -66,7 +69,8 @@ class OneShotStack:
         L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.score if with_score else None, self.ws)
 
     def select(self) -> None:
-        L.dash_select(self.score, self.idx, mode=L.DASH_SEL_TOPK, k=self.k)
+        L.dash_select(self.score, self.idx, mode=L.DASH_SEL_TOPK, k=self.k, keep_first=self.keep_first,
+                      keep_last=self.keep_last)
 
     def post_layer(self, l: int) -> None:
         x = self.layers[l]

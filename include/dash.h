@@ -75,8 +75,11 @@ typedef struct {
  *                layers below tau before a token halts), counters (DEVICE
  *                uint8 array indexed by original position, length >= every
  *                position that appears).
- *   keep_first / keep_last: forced retention of the first / last tokens; must
- *                be 0 (reserved). */
+ *   keep_first / keep_last: TOPK only (0 for the other modes): forced
+ *                retention of the first f and last l positions of every row
+ *                ([P1] §3.1 and §3.2: keep_first_n / keep_last_n).  k stays
+ *                the total kept count (K_eff = f + l + floor(keep * (n - f - l))
+ *                in [P1]'s terms) and 0 <= f + l <= k is required. */
 typedef struct {
   int mode; /* dash_sel_mode */
   int k;
@@ -125,7 +128,10 @@ int dash_attn_layer(void* ctx, const dash_shape* s,
  *               largest score, ties to the lower position, NaN below every
  *               number, -0 == +0, written in ascending order.  If pos != NULL
  *               (rows == 1 only) the kept entries are pos[i] instead of i.
- *               n_dev must be NULL (n = n_max).
+ *               n_dev must be NULL (n = n_max).  With keep_first f and
+ *               keep_last l, positions 0..f-1 and n-l..n-1 are always kept and
+ *               the other k - f - l are the top ones among positions f..n-l-1
+ *               under the same order; the output is still ascending.
  *   ORDER_STAT: rows == 1; n = *n_dev (or n_max); *tau_out (device) = the
  *               rank-th smallest of score[0..n) under the same order (NaN
  *               lowest), a zero returned as +0.  rank <= n is required when n

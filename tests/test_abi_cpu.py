@@ -89,6 +89,14 @@ def test_select_validation(lib):
     assert f(None, ctypes.byref(sel0), None, None, None, 10, 1, None, None, None, None, 0, None) == L.DASH_OK
     forced = L.DashSel(L.DASH_SEL_TOPK, 5, 0, None, 2, None, 64, 0)
     assert f(None, ctypes.byref(forced), FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    # forced retention: f + l must not exceed k; negative counts rejected; top-k only
+    for kf, kl in ((3, 3), (-1, 0), (0, -2)):
+        bad_f = L.DashSel(L.DASH_SEL_TOPK, 5, 0, None, 2, None, kf, kl)
+        assert f(None, ctypes.byref(bad_f), FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    assert "keep_first" in _last(lib)
+    os_f = L.DashSel(L.DASH_SEL_ORDER_STAT, 0, 3, None, 2, None, 1, 0)
+    assert f(None, ctypes.byref(os_f), FAKE, None, None, 10, 1, None, None, FAKE, None, 0, None) == L.DASH_E_INVAL
+    assert "top-k only" in _last(lib)
     os_ = L.DashSel(L.DASH_SEL_ORDER_STAT, 0, 11, None, 2, None, 0, 0)
     assert f(None, ctypes.byref(os_), FAKE, None, None, 10, 1, None, None, FAKE, None, 0, None) == L.DASH_E_INVAL
     th = L.DashSel(L.DASH_SEL_THRESHOLD, 0, 0, FAKE, 0, FAKE, 0, 0)

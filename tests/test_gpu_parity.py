@@ -103,6 +103,50 @@ def test_topk_pos_map(dash):
     np.testing.assert_array_equal(idx.cpu().numpy(), pos[oracle.select_topk(s, k)])
 
 
+def _forced_cases(n):
+    """(keep_first, keep_last) pairs with f + l <= n, including the pages' defaults 64 / 32."""
+    pairs = [(0, 1), (1, 0), (64, 32), (5, 0), (0, 7), (n // 2, n - n // 2)]
+    return sorted({(f, l) for f, l in pairs if f + l <= n})
+
+
+@pytest.mark.parametrize("n", [1, 97, 4096 + 96, 8192, 32768 + 96, 65536 + 17, 131072])
+@pytest.mark.parametrize("kind", ["normal", "equal", "bf16ties", "special", "decreasing"])
+def test_topk_forced_bit_exact(dash, kind, n):
+    """Forced retention of the first/last tokens: bit-exact against the oracle for
+    k from f + l (nothing chosen by score) through the pages' K_eff to n."""
+    s = score_vector(kind, n, seed=7 * n + 3)
+    sd = torch.from_numpy(s).cuda()
+    for f, l in _forced_cases(n):
+        ks = {f + l, min(n, f + l + 1), dash.effective_keep(n, 0.333, f, l), n}
+        for k in sorted(ks):
+            say("topk forced", kind, n, f, l, k)
+            idx = torch.full((max(k, 1),), -7, dtype=torch.int32, device="cuda")
+            dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, keep_first=f, keep_last=l)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(idx.cpu().numpy()[:k], oracle.select_topk_forced(s, k, f, l))
+
+
+def test_topk_forced_batched_and_pos(dash):
+    rows, n, f, l = 24, 3000, 64, 32
+    k = dash.effective_keep(n, 0.333, f, l)
+    assert k == oracle.effective_keep_count(n, 0.333, f, l)
+    s = np.stack([score_vector("fewvalues" if r % 2 else "normal", n, seed=100 + r) for r in range(rows)])
+    idx = torch.empty(rows, k, dtype=torch.int32, device="cuda")
+    say("topk forced batched", rows, n, k)
+    dash.dash_select(torch.from_numpy(s).cuda(), idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows,
+                     keep_first=f, keep_last=l)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r in range(rows):
+        np.testing.assert_array_equal(got[r], oracle.select_topk_forced(s[r], k, f, l))
+    pos = np.sort(np.random.default_rng(1).choice(20000, n, replace=False)).astype(np.int32)
+    idx1 = torch.empty(k, dtype=torch.int32, device="cuda")
+    dash.dash_select(torch.from_numpy(s[0]).cuda(), idx1, mode=dash.DASH_SEL_TOPK, k=k, keep_first=f, keep_last=l,
+                     pos=torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx1.cpu().numpy(), pos[oracle.select_topk_forced(s[0], k, f, l)])
+
+
 @pytest.mark.parametrize("n", [1, 50, 4097, 65536])
 @pytest.mark.parametrize("kind", SCORE_KINDS)
 def test_order_statistic_bit_exact(dash, kind, n):
@@ -355,6 +399,25 @@ def test_tiny_fp32_one_shot_step(dash, seed):
     Oa = oracle.attn_active(hostl[1]["Q"], hostl[1]["K"], hostl[1]["V"], idx, "active")
     Ua = oracle.output_projection(Oa, hostl[1]["Wo"])
     assert maxrel(host(st.Oa), Oa) <= TOL_F32
+    assert maxrel(host(st.Ua), Ua) <= TOL_F32
+
+
+def test_tiny_fp32_one_shot_step_forced(dash):
+    """As above with the pages' forced retention (first 64, last 32 tokens) and
+    K_eff = 96 + floor(0.5 * (512 - 96)) = 304."""
+    from attention_delta_token_amd.stack import OneShotStack
+    w = WORKLOADS[0]
+    hostl, devl = _stack_inputs(w, 0, "f32")
+    k = oracle.effective_keep_count(w.S, w.keep, 64, 32)
+    assert k == dash.effective_keep(w.S, w.keep, 64, 32) == 304
+    st = OneShotStack(devl, halt_layer=0, k=k, keep_first=64, keep_last=32)
+    st.run()
+    torch.cuda.synchronize()
+    score, idx = host(st.score), st.idx.cpu().numpy()
+    np.testing.assert_array_equal(idx, oracle.select_topk_forced(score, k, 64, 32))
+    assert np.all(idx[:64] == np.arange(64)) and np.all(idx[-32:] == np.arange(w.S - 32, w.S))
+    Oa = oracle.attn_active(hostl[1]["Q"], hostl[1]["K"], hostl[1]["V"], idx, "active")
+    Ua = oracle.output_projection(Oa, hostl[1]["Wo"])
     assert maxrel(host(st.Ua), Ua) <= TOL_F32
 
 
