@@ -24,7 +24,7 @@ DASH_SEL_TOPK, DASH_SEL_THRESHOLD, DASH_SEL_ORDER_STAT = 0, 1, 2
 DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE = 0, 1, 2
 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
-            "dash_attn_layer", "dash_select", "dash_compact", "dash_attn_active",
+            "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_attn_active",
             "dash_trace_start", "dash_trace_stop", "dash_trace_read")
 TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact")
 
@@ -32,6 +32,10 @@ TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select",
 class DashShape(Structure):
     _fields_ = [("B", c_int), ("S", c_int), ("Hq", c_int), ("Hkv", c_int), ("D", c_int), ("hidden", c_int),
                 ("dtype", c_int)]
+
+
+class DashGather(Structure):
+    _fields_ = [("X", c_void_p), ("S", c_int), ("row_bytes", c_size_t), ("Xa", c_void_p)]
 
 
 class DashSel(Structure):
@@ -75,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_compact.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_int, c_size_t, c_void_p,
                                  c_void_p]
     lib.dash_compact.restype = c_int
+    lib.dash_compact_many.argtypes = [c_void_p, c_void_p, c_void_p, c_int, POINTER(DashGather), c_int, c_void_p]
+    lib.dash_compact_many.restype = c_int
     lib.dash_attn_active.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_int,
                                      c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]
@@ -177,6 +183,19 @@ def dash_compact(idx, X, Xa, n_dev=None, n_max: int | None = None, stream=None) 
         n_max = idx.shape[0]
     _check(load().dash_compact(None, _ptr(idx), _ptr(n_dev), n_max, _ptr(X), S, row_bytes, _ptr(Xa),
                                _stream(stream)))
+
+
+def dash_compact_many(idx, pairs, n_dev=None, n_max: int | None = None, stream=None) -> None:
+    """One launch gathering several tensors at the same rows: for each (X, Xa)
+    in pairs, Xa[r] = X[idx[r]] for r < n (at most 4 pairs)."""
+    if n_max is None:
+        n_max = idx.shape[0]
+    arr = (DashGather * len(pairs))()
+    for j, (X, Xa) in enumerate(pairs):
+        S = X.shape[0]
+        row_bytes = X[0].numel() * X.element_size() if S > 0 else Xa[0].numel() * Xa.element_size()
+        arr[j] = DashGather(_ptr(X), S, row_bytes, _ptr(Xa))
+    _check(load().dash_compact_many(None, _ptr(idx), _ptr(n_dev), n_max, arr, len(pairs), _stream(stream)))
 
 
 def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: int | None = None, Wo=None,

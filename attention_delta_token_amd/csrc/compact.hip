@@ -18,51 +18,102 @@ namespace {
 constexpr int kCompactThreads = 256;
 constexpr int kCompactItems = 4;
 
+// Up to kMaxGather tensors gathered at the same rows.  Row r of the flattened
+// space holds the 16-byte chunks of row r of tensor 0, then of tensor 1, ...;
+// lo[j] is the first chunk of tensor j within a flattened row, w[j] its chunks
+// per row and cpr the flattened row length.  Unused slots have lo = cpr.
+struct GatherSet {
+  const u32x4* X[kMaxGather];
+  u32x4* Xa[kMaxGather];
+  int S[kMaxGather];
+  uint32_t lo[kMaxGather];
+  uint32_t w[kMaxGather];
+  uint32_t cpr;
+};
+
+template <class T>
+__device__ __forceinline__ T pick(const T (&a)[kMaxGather], int j) {
+  // compile-time selects (no indexing of the argument block at run time)
+  T v = a[0];
+#pragma unroll
+  for (int t = 1; t < kMaxGather; ++t)
+    if (j == t) v = a[t];
+  return v;
+}
+
 __global__ __launch_bounds__(kCompactThreads)
-void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_dev, int n_max,
-                    const u32x4* __restrict__ X, int S, uint32_t cpr, u32x4* __restrict__ Xa) {
+void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_dev, int n_max, GatherSet g) {
   int n = n_dev ? *n_dev : n_max;
   if (n > n_max) n = n_max;
+  const uint32_t cpr = g.cpr;
   // The host guarantees n_max * cpr < 2^31, so 32-bit indexing is exact.
   const uint32_t total = static_cast<uint32_t>(n < 0 ? 0 : n) * cpr;
   const uint32_t base = blockIdx.x * (kCompactItems * kCompactThreads) + threadIdx.x;
   u32x4 v[kCompactItems];
-  uint32_t dst[kCompactItems];
-  bool ok[kCompactItems];
+  u32x4* dst[kCompactItems];
 #pragma unroll
   for (int it = 0; it < kCompactItems; ++it) {
     const uint32_t e = base + static_cast<uint32_t>(it) * kCompactThreads;
-    ok[it] = false;
+    dst[it] = nullptr;
     if (e < total) {
       const uint32_t r = e / cpr;
       const uint32_t c = e - r * cpr;
+      int j = 0;
+#pragma unroll
+      for (int t = 1; t < kMaxGather; ++t)
+        if (c >= g.lo[t]) j = t;
+      const uint32_t cj = c - pick(g.lo, j);
+      const uint32_t w = pick(g.w, j);
       const int32_t src = idx[r];
-      if (src >= 0 && src < S) {
-        v[it] = __builtin_nontemporal_load(X + static_cast<uint64_t>(src) * cpr + c);
-        dst[it] = e;
-        ok[it] = true;
+      if (src >= 0 && src < pick(g.S, j)) {
+        v[it] = __builtin_nontemporal_load(pick(g.X, j) + static_cast<uint64_t>(src) * w + cj);
+        dst[it] = pick(g.Xa, j) + static_cast<uint64_t>(r) * w + cj;
       }
     }
   }
 #pragma unroll
   for (int it = 0; it < kCompactItems; ++it)
-    if (ok[it]) Xa[dst[it]] = v[it];
+    if (dst[it]) *dst[it] = v[it];
 }
 
 }  // namespace
 
-hipError_t launch_compact(const int32_t* idx, const int32_t* n_dev, int n_max, const void* X, int S,
-                          size_t row_bytes, void* Xa, hipStream_t stream) {
-  if (n_max <= 0) return hipSuccess;
-  const uint32_t cpr = static_cast<uint32_t>(row_bytes / 16);
-  const uint64_t total = static_cast<uint64_t>(n_max) * cpr;
+hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_max, const GatherItem* items,
+                               int count, hipStream_t stream) {
+  if (n_max <= 0 || count <= 0) return hipSuccess;
+  if (count > kMaxGather) return hipErrorInvalidValue;
+  GatherSet g{};
+  uint32_t acc = 0;
+  for (int j = 0; j < count; ++j) {
+    g.X[j] = static_cast<const u32x4*>(items[j].X);
+    g.Xa[j] = static_cast<u32x4*>(items[j].Xa);
+    g.S[j] = items[j].S;
+    g.lo[j] = acc;
+    g.w[j] = static_cast<uint32_t>(items[j].row_bytes / 16);
+    acc += g.w[j];
+  }
+  for (int j = count; j < kMaxGather; ++j) {
+    g.X[j] = g.X[0];
+    g.Xa[j] = g.Xa[0];
+    g.S[j] = 0;
+    g.lo[j] = acc;
+    g.w[j] = 1;
+  }
+  g.cpr = acc;
+  const uint64_t total = static_cast<uint64_t>(n_max) * acc;
   const uint64_t per_block = static_cast<uint64_t>(kCompactThreads) * kCompactItems;
   const uint64_t blocks = (total + per_block - 1) / per_block;
   if (blocks == 0) return hipSuccess;
   if (total >= 0x80000000ull) return hipErrorInvalidValue;
   hipLaunchKernelGGL(compact_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCompactThreads), 0, stream, idx,
-                     n_dev, n_max, static_cast<const u32x4*>(X), S, cpr, static_cast<u32x4*>(Xa));
+                     n_dev, n_max, g);
   return hipGetLastError();
+}
+
+hipError_t launch_compact(const int32_t* idx, const int32_t* n_dev, int n_max, const void* X, int S,
+                          size_t row_bytes, void* Xa, hipStream_t stream) {
+  const GatherItem one{X, S, row_bytes, Xa};
+  return launch_compact_many(idx, n_dev, n_max, &one, 1, stream);
 }
 
 }  // namespace dash

@@ -322,6 +322,42 @@ int dash_compact(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_
   }
 }
 
+int dash_compact_many(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_max, const dash_gather* items,
+                      int count, void* stream) {
+  try {
+    if (n_max < 0) return fail(DASH_E_INVAL, "n_max must be >= 0");
+    if (count < 1 || count > dash::kMaxGather)
+      return fail(DASH_E_INVAL, "count %d outside [1, %d]", count, dash::kMaxGather);
+    if (!items) return fail(DASH_E_INVAL, "items is NULL");
+    dash::GatherItem g[dash::kMaxGather];
+    uint64_t chunks = 0;
+    for (int j = 0; j < count; ++j) {
+      const dash_gather& it = items[j];
+      if (it.S < 0) return fail(DASH_E_INVAL, "items[%d].S must be >= 0", j);
+      if (it.row_bytes == 0 || it.row_bytes % 16 != 0)
+        return fail(DASH_E_ALIGN, "items[%d].row_bytes must be a positive multiple of 16", j);
+      if (n_max > 0) {
+        if (!it.X || !it.Xa) return fail(DASH_E_INVAL, "items[%d] has a NULL tensor", j);
+        if (!aligned16(it.X) || !aligned16(it.Xa)) return fail(DASH_E_ALIGN, "items[%d] is not 16-byte aligned", j);
+      }
+      chunks += it.row_bytes / 16;
+      g[j] = dash::GatherItem{it.X, it.S, it.row_bytes, it.Xa};
+    }
+    if (n_max == 0) return DASH_OK;
+    if (!idx) return fail(DASH_E_INVAL, "idx is NULL");
+    if (static_cast<uint64_t>(n_max) * chunks >= (1ull << 31))
+      return fail(DASH_E_INVAL, "n_max * summed row_bytes too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int tr = trace_open(DASH_TR_COMPACT, st);
+    hipError_t e = dash::launch_compact_many(idx, n_dev, n_max, g, count, st);
+    trace_close(tr, st);
+    if (e != hipSuccess) return hip_fail(e, "compaction launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
 int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const int32_t* q_pos,
                      const int32_t* n_dev, int n_max, const void* K, const void* V, int kv_mode, void* Oa,
                      const void* Wo, void* Ua, float* score, void* ws, size_t ws_bytes, void* stream) {

@@ -23,6 +23,16 @@ hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_
                             const float* tau, int patience, uint8_t* counters, int32_t* out, int32_t* n_out,
                             hipStream_t stream);
 
+// One tensor of a multi-tensor gather: Xa[r] = X[idx[r]], rows of row_bytes.
+constexpr int kMaxGather = 4;
+struct GatherItem {
+  const void* X;
+  int S;
+  size_t row_bytes;
+  void* Xa;
+};
+hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_max, const GatherItem* items,
+                               int count, hipStream_t stream);
 hipError_t launch_compact(const int32_t* idx, const int32_t* n_dev, int n_max, const void* X, int S,
                           size_t row_bytes, void* Xa, hipStream_t stream);
 

@@ -77,13 +77,12 @@ class OneShotStack:
         k = self.k
         if k == 0:
             return
-        L.dash_compact(self.idx, x.Q, self.Qa, n_max=k)
         if self.kv_mode == L.DASH_KV_ACTIVE:
-            L.dash_compact(self.idx, x.K, self.Ka, n_max=k)
-            L.dash_compact(self.idx, x.V, self.Va, n_max=k)
+            L.dash_compact_many(self.idx, [(x.Q, self.Qa), (x.K, self.Ka), (x.V, self.Va)], n_max=k)
             L.dash_attn_active(self.Qa, self.Ka, self.Va, L.DASH_KV_ACTIVE, self.Oa, n_max=k, Wo=x.Wo,
                                Ua=self.Ua)
         else:
+            L.dash_compact(self.idx, x.Q, self.Qa, n_max=k)
             L.dash_attn_active(self.Qa, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=self.idx, n_max=k, Wo=x.Wo,
                                Ua=self.Ua, S=self.S)
 

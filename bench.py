@@ -198,8 +198,9 @@ def main():
     else:
         sel_bytes_step = 4.0 * S + 4.0 * w.k
         n_sel_step = 1
-        cmp_bytes_step = sum(k * (2 * esz * (Hq * D + 2 * Hkv * D) + 3 * 4) for k in k_rows)
-        n_cmp_step = 3 * len(k_rows)
+        # one launch gathers Q, K and V (kv active) at the kept rows, reading each index once
+        cmp_bytes_step = sum(k * (2 * esz * (Hq * D + 2 * Hkv * D) + 4) for k in k_rows)
+        n_cmp_step = len(k_rows)
     t_sel, t_cmp = by.get("select", []), by.get("compact", [])
     sel_gbps = (steps_traced * sel_bytes_step) / (sum(t_sel) * 1e-3) / 1e9 if t_sel else None
     cmp_gbps = (steps_traced * cmp_bytes_step) / (sum(t_cmp) * 1e-3) / 1e9 if t_cmp else None

@@ -156,6 +156,22 @@ int dash_select(void* ctx, const dash_sel* p, const float* score, const int32_t*
 int dash_compact(void* ctx, const int32_t* idx, const int32_t* n_dev, int n_max,
                  const void* X, int S, size_t row_bytes, void* Xa, void* stream);
 
+/* a4 for several tensors at once: the same gather for up to 4 tensors that
+ * share one index list (a layer's Q, K and V at the kept positions), in one
+ * launch.  For each j < count: items[j].Xa[r, :] = items[j].X[idx[r], :] for
+ * r < n, with the rules of dash_compact (items[j].S rows of
+ * items[j].row_bytes bytes, a multiple of 16; rows with idx[r] outside
+ * [0, S) not copied).  `items` is a HOST array read during the call.
+ * n_max times the summed row_bytes / 16 must stay below 2^31.  No workspace. */
+typedef struct {
+  const void* X;
+  int S;
+  size_t row_bytes;
+  void* Xa;
+} dash_gather;
+int dash_compact_many(void* ctx, const int32_t* idx, const int32_t* n_dev, int n_max,
+                      const dash_gather* items, int count, void* stream);
+
 /* a5: post-halt attention ([P1] §3.1 step 4 and §5.1; [P2] 选择性停止机制).
  *   Qa [n, Hq, D] are the active queries (n = *n_dev or n_max, s->B == 1),
  *   q_pos [n] their ascending original positions.

@@ -118,6 +118,28 @@ def test_compact_validation(lib):
     assert f(None, FAKE, None, 0, None, 10, 32, None, None) == L.DASH_OK  # nothing to do
 
 
+def test_compact_many_validation(lib):
+    f = lib.dash_compact_many
+    G = L.DashGather
+
+    def arr(*items):
+        a = (G * len(items))()
+        for j, it in enumerate(items):
+            a[j] = G(*it)
+        return a
+    good = (FAKE, 10, 32, FAKE)
+    assert f(None, FAKE, None, 10, arr(good), 0, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, None, 10, arr(good, good, good, good, good), 5, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, None, 10, None, 1, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, None, 10, arr(good, (FAKE, 10, 24, FAKE)), 2, None) == L.DASH_E_ALIGN
+    assert f(None, FAKE, None, 10, arr(good, (FAKE + 8, 10, 32, FAKE)), 2, None) == L.DASH_E_ALIGN
+    assert f(None, FAKE, None, 10, arr((None, 10, 32, FAKE)), 1, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, None, 10, arr((FAKE, -1, 32, FAKE)), 1, None) == L.DASH_E_INVAL
+    assert f(None, None, None, 10, arr(good), 1, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, None, 1 << 20, arr((FAKE, 10, 1 << 20, FAKE)), 1, None) == L.DASH_E_INVAL
+    assert f(None, None, None, 0, arr(good), 1, None) == L.DASH_OK  # nothing to do
+
+
 def test_attn_active_validation(lib):
     f = lib.dash_attn_active
     s = _shape()

@@ -257,6 +257,30 @@ def test_compact_bit_exact(dash, row_bytes, device_n):
     assert np.all(got[n:] == 0xAB)
 
 
+@pytest.mark.parametrize("widths", [(7168, 1024, 1024), (16,), (48, 16, 7168, 32), (1024, 48)])
+@pytest.mark.parametrize("device_n", [False, True])
+def test_compact_many_bit_exact(dash, widths, device_n):
+    """Several tensors of different row widths gathered at one index list in one
+    launch; idx holds out-of-range entries (those rows are not copied)."""
+    S, n_max = 2049, 1100
+    rng = np.random.default_rng(sum(widths))
+    Xs = [rng.integers(0, 256, (S, w), dtype=np.uint8) for w in widths]
+    idx = np.sort(rng.choice(S, n_max, replace=False)).astype(np.int32)
+    idx[[5, 700]] = [-1, S + 3]  # skipped rows
+    n = 987 if device_n else n_max
+    Xas = [torch.full((n_max, w), 0xCD, dtype=torch.uint8, device="cuda") for w in widths]
+    say("compact many", widths, device_n)
+    nd = torch.tensor([n, 0, 0, 0], dtype=torch.int32, device="cuda") if device_n else None
+    dash.dash_compact_many(torch.from_numpy(idx).cuda(), [(torch.from_numpy(X).cuda(), Xa) for X, Xa in zip(Xs, Xas)],
+                           n_dev=nd, n_max=n_max)
+    torch.cuda.synchronize()
+    ok = (idx[:n] >= 0) & (idx[:n] < S)
+    for X, Xa in zip(Xs, Xas):
+        got = Xa.cpu().numpy()
+        np.testing.assert_array_equal(got[:n][ok], oracle.compact(X, idx[:n][ok]))
+        assert np.all(got[:n][~ok] == 0xCD) and np.all(got[n:] == 0xCD)
+
+
 # ---------------------------------------------------------------------------
 # attention + projection + score
 # ---------------------------------------------------------------------------
