@@ -25,13 +25,14 @@ namespace dash {
 
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 1024;  // one workgroup per row
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 2048;
-// Each histogram is kept in kCopies copies, lane l counting into copy l % kCopies:
-// scores cluster in a few top-digit bins, and the copies cut the same-address
-// LDS atomic conflicts of one wave by that factor.
-constexpr int kCopies = 8;
+// Each histogram is kept in kCopies copies, lane l counting into copy
+// l % kCopies: scores cluster in a few bins, and the copies cut same-address
+// LDS atomic conflicts by that factor.
+template <int NT>
+constexpr int kCopies = 4;
 
 // Order-preserving key: larger score -> larger key.  NaN -> 0 (below every
 // number, including -inf whose key is 0x007fffff); -0 and +0 share one key.
@@ -50,33 +51,53 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(b);
 }
 
-// Inclusive wave scan (64 lanes) of a 64-bit value.
-__device__ __forceinline__ uint64_t wave_incl_scan(uint64_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint64_t o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+// Inclusive scan of a 32-bit value over the 64 lanes of a wave, in registers
+// (DPP): shifts by 1, 2, 4 and 8 within each row of 16 lanes, then the row
+// totals are carried across rows with the row_bcast:15 / row_bcast:31 moves.
+// Lanes whose DPP source does not exist read `id`, the operator's identity.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_op(uint32_t v, uint32_t id, Op op) {
+  const int i = static_cast<int>(id);
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(i, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
   return v;
 }
 
-// Exclusive workgroup scan of a 64-bit value; also returns the block total.
+__device__ __forceinline__ uint32_t wave_incl_scan32(uint32_t v) {
+  return wave_incl_scan_op(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Inclusive wave scan of a pair of 32-bit counts packed in 64 bits (no carry
+// crosses the halves: every count here is below 2^31).
+__device__ __forceinline__ uint64_t wave_incl_scan(uint64_t v) {
+  const uint32_t lo = wave_incl_scan32(static_cast<uint32_t>(v));
+  const uint32_t hi = wave_incl_scan32(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Exclusive scan of a 64-bit value over the NT threads of a workgroup; also
+// returns the workgroup total.  sh_waves holds 2 * NT / 64 + 1 entries.
+template <int NT>
 __device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* sh_waves, uint64_t& total) {
+  constexpr int kW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   const uint64_t incl = wave_incl_scan(v);
   if (lane == kWave - 1) sh_waves[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    uint64_t w = (lane < kSelWaves) ? sh_waves[lane] : 0ull;
+    uint64_t w = (lane < kW) ? sh_waves[lane] : 0ull;
     const uint64_t wi = wave_incl_scan(w);
-    if (lane < kSelWaves) sh_waves[kSelWaves + lane] = wi - w;  // exclusive wave offsets
-    if (lane == kSelWaves - 1) sh_waves[2 * kSelWaves] = wi;
+    if (lane < kW) sh_waves[kW + lane] = wi - w;  // exclusive wave offsets
+    if (lane == kW - 1) sh_waves[2 * kW] = wi;
   }
   __syncthreads();
-  const uint64_t res = sh_waves[kSelWaves + wid] + incl - v;
-  total = sh_waves[2 * kSelWaves];
+  const uint64_t res = sh_waves[kW + wid] + incl - v;
+  total = sh_waves[2 * kW];
   __syncthreads();
   return res;
 }
@@ -85,48 +106,86 @@ __device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t* sh_wav
 // `for_keys(f)` (which calls f(key) for each of this thread's keys).  Returns
 // the cut key; *take_eq = how many keys equal to it are ranked within the top
 // kk (the kk - #greater lowest-position ones).
-template <class ForKeys>
+//
+// Adaptive (keys held in registers, so an extra look is free): the bits every
+// key shares (the common prefix of the smallest and largest key) are settled
+// up front and the digits start right below them, so keys from a narrow score
+// range spread over many bins.  Otherwise the digits are bits 31-21, 20-10
+// and 9-0.
+template <int NT, bool Adaptive, class ForKeys>
 __device__ uint32_t radix_cut(ForKeys for_keys, uint32_t kk, uint32_t* hist, uint64_t* sh_scan, uint32_t* sh_cut,
                               uint32_t* take_eq) {
-  uint32_t prefix = 0u, pmask = 0u;
-  const int shifts[3] = {21, 10, 0};
-  const uint32_t dmask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass];
-    const uint32_t dm = dmask[pass];
-    for (int b = threadIdx.x; b < kCopies * kBins; b += kSelThreads) hist[b] = 0u;
+  constexpr int kBPT = kBins / NT;  // consecutive bins owned by one thread in the scan
+  constexpr int kW = NT / kWave;
+  static_assert(kBins % NT == 0, "bins split evenly");
+  int common = 0;  // leading bits shared by every key
+  uint32_t kmin = 0u;
+  if constexpr (Adaptive) {
+    kmin = 0xffffffffu;
+    uint32_t kmax = 0u;
+    for_keys([&](uint32_t key) {
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    });
+    kmin = wave_incl_scan_op(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
+    kmax = wave_incl_scan_op(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+    uint32_t* sh_mm = reinterpret_cast<uint32_t*>(sh_scan);  // [kW] minima, [kW] maxima
+    if ((threadIdx.x & (kWave - 1)) == kWave - 1) {
+      sh_mm[threadIdx.x / kWave] = kmin;
+      sh_mm[kW + threadIdx.x / kWave] = kmax;
+    }
     __syncthreads();
-    uint32_t* my_hist = hist + (threadIdx.x % kCopies) * kBins;
+    kmin = sh_mm[0];
+    kmax = sh_mm[kW];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) {
+      kmin = min(kmin, sh_mm[w]);
+      kmax = max(kmax, sh_mm[kW + w]);
+    }
+    __syncthreads();
+    common = kmin == kmax ? 32 : __clz(kmin ^ kmax);  // 0..32
+  }
+  uint32_t pmask = static_cast<uint32_t>(0xffffffff00000000ull >> common);  // top `common` bits
+  uint32_t prefix = kmin & pmask;
+  int sh = 32 - common;  // bits below the prefix still to settle (at most 3 passes of <= 11)
+#pragma unroll 1
+  while (sh > 0) {
+    const int w = sh < 11 ? sh : 11;
+    sh -= w;
+    const uint32_t dm = (1u << w) - 1u;
+    for (int b = threadIdx.x; b < kCopies<NT> * kBins; b += NT) hist[b] = 0u;
+    __syncthreads();
+    uint32_t* my_hist = hist + (threadIdx.x % kCopies<NT>) * kBins;
     for_keys([&](uint32_t key) {
       if ((key & pmask) == prefix) atomicAdd(&my_hist[(key >> sh) & dm], 1u);
     });
     __syncthreads();
-    // Suffix sums over bins (from the top): each thread owns 2 consecutive bins.
     const int nb = static_cast<int>(dm) + 1;
-    const int b0 = 2 * threadIdx.x;
-    uint32_t c0 = 0u, c1 = 0u;
-    if (b0 < nb) {
+    const int b0 = kBPT * threadIdx.x;
+    uint32_t c[kBPT];
+    uint32_t mine = 0u;
 #pragma unroll
-      for (int c = 0; c < kCopies; ++c) {
-        c0 += hist[c * kBins + b0];
-        c1 += hist[c * kBins + b0 + 1];
+    for (int j = 0; j < kBPT; ++j) {
+      c[j] = 0u;
+      if (b0 + j < nb) {
+#pragma unroll
+        for (int cp = 0; cp < kCopies<NT>; ++cp) c[j] += hist[cp * kBins + b0 + j];
       }
+      mine += c[j];
     }
     uint64_t tot;
-    const uint32_t mine = c0 + c1;
-    // Exclusive prefix over bins below 2t; keys strictly above bin 2t+1 = total - prefix - mine.
-    const uint64_t excl = block_excl_scan(mine, sh_scan, tot);
-    const uint32_t above1 = static_cast<uint32_t>(tot - excl - mine);  // keys in bins > 2t+1
-    const uint32_t above0 = above1 + c1;                               // keys in bins > 2t
-    // The cut bin b satisfies above(b) < kk <= above(b) + hist[b].
-    if (b0 + 1 < nb && above1 < kk && kk <= above1 + c1) {
-      sh_cut[0] = static_cast<uint32_t>(b0 + 1);
-      sh_cut[1] = kk - above1;
-    }
-    if (b0 < nb && above0 < kk && kk <= above0 + c0) {
-      sh_cut[0] = static_cast<uint32_t>(b0);
-      sh_cut[1] = kk - above0;
+    const uint64_t excl = block_excl_scan<NT>(mine, sh_scan, tot);  // keys in bins below b0
+    // Keys strictly above bin b0 + j = total - (keys in bins <= b0 + j); the
+    // cut bin b satisfies above(b) < kk <= above(b) + count(b).
+    uint32_t upto = static_cast<uint32_t>(excl);
+#pragma unroll
+    for (int j = 0; j < kBPT; ++j) {
+      upto += c[j];
+      const uint32_t above = static_cast<uint32_t>(tot) - upto;
+      if (b0 + j < nb && above < kk && kk <= above + c[j]) {
+        sh_cut[0] = static_cast<uint32_t>(b0 + j);
+        sh_cut[1] = kk - above;
+      }
     }
     __syncthreads();
     const uint32_t bin = sh_cut[0];
@@ -140,24 +199,26 @@ __device__ uint32_t radix_cut(ForKeys for_keys, uint32_t kk, uint32_t* hist, uin
 }
 
 // Keys of one score row read from global memory on every pass.
+template <int NT>
 struct RowKeys {
   const float* row;
   int n;
   template <class F>
   __device__ __forceinline__ void operator()(F&& f) const {
-    for (int i = threadIdx.x; i < n; i += kSelThreads) f(score_key(row[i]));
+    for (int i = threadIdx.x; i < n; i += NT) f(score_key(row[i]));
   }
 };
 
 // Emit, in ascending position order, every i with key > cut plus the first
 // `take_eq` positions with key == cut, as first + i, or out_map[i] when
-// out_map != nullptr.
+// out_map != nullptr.  Writes stop at cap entries.
+template <int NT>
 __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut, uint32_t take_eq,
                               const int32_t* __restrict__ out_map, int first, int32_t* __restrict__ out,
-                              uint64_t* sh_scan) {
+                              uint32_t cap, uint64_t* sh_scan) {
   constexpr int E = 8;  // consecutive elements per thread per chunk
   uint32_t eq_before = 0u, sel_before = 0u;
-  for (int base = 0; base < n; base += kSelThreads * E) {
+  for (int base = 0; base < n; base += NT * E) {
     const int i0 = base + threadIdx.x * E;
     uint32_t gt = 0u, eq = 0u;
     uint32_t flags = 0u;  // bit e: gt, bit 8+e: eq
@@ -172,7 +233,7 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
     }
     uint64_t tot;
     const uint64_t mine = (static_cast<uint64_t>(gt) << 32) | eq;
-    const uint64_t excl = block_excl_scan(mine, sh_scan, tot);
+    const uint64_t excl = block_excl_scan<NT>(mine, sh_scan, tot);
     uint32_t eq_rank = eq_before + static_cast<uint32_t>(excl & 0xffffffffu);
     const uint32_t gt_rank = static_cast<uint32_t>(excl >> 32);
     uint32_t eq_taken_before = eq_rank < take_eq ? eq_rank : take_eq;
@@ -184,7 +245,7 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
       if (flags & (1u << e)) take = true;
       else if (flags & (1u << (8 + e))) { take = eq_rank < take_eq; ++eq_rank; }
       if (take) {
-        out[o] = out_map ? out_map[i] : first + i;
+        if (o < cap) out[o] = out_map ? out_map[i] : first + i;
         ++o;
       }
     }
@@ -200,48 +261,52 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
 // Forced retention: the first f and last l positions of a row of n_row
 // scores are written to the two ends of its k_total outputs; the caller then
 // selects k_total - f - l among the middle positions.
+template <int NT>
 __device__ __forceinline__ void emit_forced(int n_row, int k_total, int f, int l, const int32_t* __restrict__ pos,
                                             int32_t* __restrict__ out) {
-  for (int i = threadIdx.x; i < f; i += kSelThreads) out[i] = pos ? pos[i] : i;
-  for (int j = threadIdx.x; j < l; j += kSelThreads) {
+  for (int i = threadIdx.x; i < f; i += NT) out[i] = pos ? pos[i] : i;
+  for (int j = threadIdx.x; j < l; j += NT) {
     const int i = n_row - l + j;
     out[k_total - l + j] = pos ? pos[i] : i;
   }
 }
 
-__global__ __launch_bounds__(kSelThreads, 1)
+// Rows of any length: keys are re-read from global memory on every pass.
+template <int NT>
+__global__ __launch_bounds__(NT, 1)
 void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f, int l,
                  const int32_t* __restrict__ pos, int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[kCopies * kBins];
-  __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
+  __shared__ uint32_t hist[kCopies<NT> * kBins];
+  __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
   const int row = blockIdx.x;
   int32_t* out = idx + static_cast<size_t>(row) * k_total;
-  emit_forced(n_row, k_total, f, l, pos, out);
+  emit_forced<NT>(n_row, k_total, f, l, pos, out);
   const int n = n_row - f - l;
   const int k = k_total - f - l;
   if (k == 0) return;
   const float* r = score + static_cast<size_t>(row) * n_row + f;
   uint32_t take_eq;
-  const uint32_t cut = radix_cut(RowKeys{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
-  emit_selected(r, n, cut, take_eq, pos ? pos + f : nullptr, f, out + f, sh_scan);
+  const uint32_t cut =
+      radix_cut<NT, false>(RowKeys<NT>{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
+  emit_selected<NT>(r, n, cut, take_eq, pos ? pos + f : nullptr, f, out + f, static_cast<uint32_t>(k), sh_scan);
 }
 
-// Rows of up to kSelThreads * ITEMS scores: each thread loads its ITEMS
-// consecutive scores once, keeps their keys in registers for the three radix
-// passes, and emits its survivors after one workgroup scan (thread order is
-// position order).
-template <int ITEMS>
-__global__ __launch_bounds__(kSelThreads, 1)
+// Rows of up to NT * ITEMS scores: each thread loads its ITEMS consecutive
+// scores once, keeps their keys in registers for the three radix passes, and
+// emits its survivors after one workgroup scan (thread order is position
+// order).
+template <int NT, int ITEMS>
+__global__ __launch_bounds__(NT, 1)
 void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, int f, int l,
                      const int32_t* __restrict__ pos, int32_t* __restrict__ idx) {
   static_assert(ITEMS <= 32, "masks are 32-bit");
-  __shared__ uint32_t hist[kCopies * kBins];
-  __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
+  __shared__ uint32_t hist[kCopies<NT> * kBins];
+  __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
   const int rowi = blockIdx.x;
   int32_t* out = idx + static_cast<size_t>(rowi) * k_total;
-  emit_forced(n_row, k_total, f, l, pos, out);
+  emit_forced<NT>(n_row, k_total, f, l, pos, out);
   const int n = n_row - f - l;
   const int k = k_total - f - l;
   if (k == 0) return;
@@ -252,13 +317,13 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) keys[e] = (i0 + e < n) ? score_key(r[i0 + e]) : 0u;
   const int valid = n - i0;  // keys e < valid exist
-  auto for_keys = [&](auto&& f) {
+  auto for_keys = [&](auto&& fn) {
 #pragma unroll
     for (int e = 0; e < ITEMS; ++e)
-      if (e < valid) f(keys[e]);
+      if (e < valid) fn(keys[e]);
   };
   uint32_t take_eq;
-  const uint32_t cut = radix_cut(for_keys, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
+  const uint32_t cut = radix_cut<NT, true>(for_keys, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
   uint32_t gt_mask = 0u, eq_mask = 0u;
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) {
@@ -269,7 +334,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
   }
   const uint32_t gt = __popc(gt_mask), eq = __popc(eq_mask);
   uint64_t tot;
-  const uint64_t excl = block_excl_scan((static_cast<uint64_t>(gt) << 32) | eq, sh_scan, tot);
+  const uint64_t excl = block_excl_scan<NT>((static_cast<uint64_t>(gt) << 32) | eq, sh_scan, tot);
   uint32_t eq_rank = static_cast<uint32_t>(excl & 0xffffffffu);
   uint32_t o = static_cast<uint32_t>(excl >> 32) + (eq_rank < take_eq ? eq_rank : take_eq);
 #pragma unroll
@@ -277,7 +342,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
     bool take = (gt_mask >> e) & 1u;
     if ((eq_mask >> e) & 1u) { take = eq_rank < take_eq; ++eq_rank; }
     if (take) {
-      out[o] = pos ? pos[f + i0 + e] : f + i0 + e;
+      if (o < static_cast<uint32_t>(k)) out[o] = pos ? pos[f + i0 + e] : f + i0 + e;
       ++o;
     }
   }
@@ -286,7 +351,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
 __global__ __launch_bounds__(kSelThreads, 1)
 void order_stat_kernel(const float* __restrict__ score, const int32_t* __restrict__ n_dev, int n_max,
                        int rank, float* __restrict__ tau_out) {
-  __shared__ uint32_t hist[kCopies * kBins];
+  __shared__ uint32_t hist[kCopies<kSelThreads> * kBins];
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   __shared__ uint32_t sh_cut[2];
   int n = n_dev ? *n_dev : n_max;
@@ -297,8 +362,9 @@ void order_stat_kernel(const float* __restrict__ score, const int32_t* __restric
   }
   uint32_t take_eq;
   // rank-th smallest == (n - rank + 1)-th largest under the same total order.
-  const uint32_t cut = radix_cut(RowKeys{score, n}, static_cast<uint32_t>(n - rank + 1), hist, sh_scan, sh_cut,
-                                 &take_eq);
+  const uint32_t cut = radix_cut<kSelThreads, false>(RowKeys<kSelThreads>{score, n},
+                                                     static_cast<uint32_t>(n - rank + 1), hist, sh_scan, sh_cut,
+                                                     &take_eq);
   if (threadIdx.x == 0) *tau_out = key_score(cut);
 }
 
@@ -331,11 +397,14 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
       }
     }
     uint64_t tot;
-    const uint64_t excl = block_excl_scan(cnt, sh_scan, tot);
+    const uint64_t excl = block_excl_scan<kSelThreads>(cnt, sh_scan, tot);
     uint32_t o = before + static_cast<uint32_t>(excl);
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (keep_bits & (1u << e)) out[o++] = p[e];
+      if (keep_bits & (1u << e)) {
+        if (o < static_cast<uint32_t>(n_max)) out[o] = p[e];  // never beyond the capacity
+        ++o;
+      }
     before += static_cast<uint32_t>(tot);
   }
   if (threadIdx.x == 0) *n_out = static_cast<int32_t>(before);
@@ -343,21 +412,30 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
 
 }  // namespace
 
+namespace {
+
+template <int NT>
+void launch_topk_nt(const float* score, int rows, int n, int k, int f, int l, const int32_t* pos, int32_t* idx,
+                    hipStream_t stream) {
+  const int n_mid = n - f - l;
+  if (n_mid <= NT * 4)
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 4>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+  else if (n_mid <= NT * 8)
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 8>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+  else if (n_mid <= NT * 16)
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 16>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+  else if (n_mid <= NT * 32)
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 32>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+  else
+    hipLaunchKernelGGL((topk_kernel<NT>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+}
+
+}  // namespace
+
 hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
                        const int32_t* pos, int32_t* idx, hipStream_t stream) {
   if (rows == 0 || k == 0) return hipSuccess;
-  const int f = keep_first, l = keep_last;
-  const int n_mid = n - f - l;
-  if (n_mid <= kSelThreads * 4)
-    hipLaunchKernelGGL(topk_reg_kernel<4>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
-  else if (n_mid <= kSelThreads * 8)
-    hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
-  else if (n_mid <= kSelThreads * 16)
-    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
-  else if (n_mid <= kSelThreads * 32)
-    hipLaunchKernelGGL(topk_reg_kernel<32>, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
-  else
-    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kSelThreads), 0, stream, score, n, k, f, l, pos, idx);
+  launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, stream);
   return hipGetLastError();
 }
 

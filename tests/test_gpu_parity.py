@@ -81,9 +81,13 @@ def test_topk_bit_exact(dash, kind, n):
         np.testing.assert_array_equal(idx.cpu().numpy()[:k], exp)
 
 
-def test_topk_batched_rows(dash):
-    rows, n, k = 48, 3000, 1234
-    s = np.stack([score_vector("fewvalues" if r % 2 else "normal", n, seed=r) for r in range(rows)])
+@pytest.mark.parametrize("rows,n,k", [(48, 3000, 1234), (80, 3000, 1234), (70, 8192, 4096), (64, 8193, 100),
+                                      (66, 1, 1), (65, 40000, 39999)])
+def test_topk_batched_rows(dash, rows, n, k):
+    """Batches of independent rows (from 64 rows on, rows fit in 256-thread workgroups
+    when n <= 8192; longer rows and smaller batches use 1024 threads)."""
+    s = np.stack([score_vector("fewvalues" if r % 2 else ("bf16ties" if r % 3 else "normal"), n, seed=r)
+                  for r in range(rows)])
     idx = torch.empty(rows, k, dtype=torch.int32, device="cuda")
     say("topk batched", rows, n, k)
     dash.dash_select(torch.from_numpy(s).cuda(), idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows)
@@ -126,8 +130,9 @@ def test_topk_forced_bit_exact(dash, kind, n):
             np.testing.assert_array_equal(idx.cpu().numpy()[:k], oracle.select_topk_forced(s, k, f, l))
 
 
-def test_topk_forced_batched_and_pos(dash):
-    rows, n, f, l = 24, 3000, 64, 32
+@pytest.mark.parametrize("rows", [24, 70])
+def test_topk_forced_batched_and_pos(dash, rows):
+    n, f, l = 3000, 64, 32
     k = dash.effective_keep(n, 0.333, f, l)
     assert k == oracle.effective_keep_count(n, 0.333, f, l)
     s = np.stack([score_vector("fewvalues" if r % 2 else "normal", n, seed=100 + r) for r in range(rows)])
