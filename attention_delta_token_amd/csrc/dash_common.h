@@ -39,16 +39,23 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Map a linear workgroup id so that workgroups dispatched to the same XCD
-// (ids congruent mod 8 land on the same XCD under round-robin dispatch) get
-// consecutive logical tiles, which then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+// Logical tile order for a grid spread over the 8 XCDs (each with its own L2).
+// Chunks of `chunk` consecutive logical ids are dealt to the XCDs in turn
+// (chunk c runs on XCD c % 8, its ids in order), so a chunk shares one L2 and
+// any prefix of the logical order (the tiles that hold rows when the row
+// count is only known on the device) is spread over all XCDs.  Grids smaller
+// than 8 chunks use chunks of nblocks / 8; ids past the last whole round of 8
+// chunks map to themselves.  (Workgroup ids are dispatched to XCD bid % 8.)
+__device__ __forceinline__ int xcd_remap_chunked(int bid, int nblocks, int chunk) {
   constexpr int kXcd = 8;
-  if (nblocks < kXcd) return bid;
-  const int per = nblocks / kXcd;           // full rounds
-  const int full = per * kXcd;
-  if (bid >= full) return bid;              // tail: identity
-  return (bid % kXcd) * per + bid / kXcd;
+  if (chunk > nblocks / kXcd) chunk = nblocks / kXcd;
+  if (chunk == 0) return bid;
+  const int round = kXcd * chunk;
+  const int full = (nblocks / round) * round;
+  if (bid >= full) return bid;
+  const int xcd = bid % kXcd;
+  const int j = bid / kXcd;  // j-th workgroup dispatched to this XCD
+  return ((j / chunk) * kXcd + xcd) * chunk + j % chunk;
 }
 
 }  // namespace dash

@@ -198,14 +198,24 @@ __device__ uint32_t radix_cut(ForKeys for_keys, uint32_t kk, uint32_t* hist, uin
   return prefix;
 }
 
-// Keys of one score row read from global memory on every pass.
+// Keys of one score row read from global memory on every pass, kU loads in
+// flight per thread before any of them is used.
 template <int NT>
 struct RowKeys {
+  static constexpr int kU = 16;
   const float* row;
   int n;
   template <class F>
   __device__ __forceinline__ void operator()(F&& f) const {
-    for (int i = threadIdx.x; i < n; i += NT) f(score_key(row[i]));
+    int i = threadIdx.x;
+    for (; i + (kU - 1) * NT < n; i += kU * NT) {
+      float v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = row[i + u * NT];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) f(score_key(v[u]));
+    }
+    for (; i < n; i += NT) f(score_key(row[i]));
   }
 };
 
@@ -271,8 +281,10 @@ __device__ __forceinline__ void emit_forced(int n_row, int k_total, int f, int l
   }
 }
 
-// Rows of any length: keys are re-read from global memory on every pass.
-template <int NT>
+// Rows of any length: keys are re-read from global memory on every pass
+// (Adaptive: one more read settles the common key prefix first; worth it for a
+// single row, where same-bin atomics dominate, not for batches).
+template <int NT, bool Adaptive>
 __global__ __launch_bounds__(NT, 1)
 void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f, int l,
                  const int32_t* __restrict__ pos, int32_t* __restrict__ idx) {
@@ -288,7 +300,7 @@ void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f,
   const float* r = score + static_cast<size_t>(row) * n_row + f;
   uint32_t take_eq;
   const uint32_t cut =
-      radix_cut<NT, false>(RowKeys<NT>{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
+      radix_cut<NT, Adaptive>(RowKeys<NT>{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
   emit_selected<NT>(r, n, cut, take_eq, pos ? pos + f : nullptr, f, out + f, static_cast<uint32_t>(k), sh_scan);
 }
 
@@ -362,7 +374,7 @@ void order_stat_kernel(const float* __restrict__ score, const int32_t* __restric
   }
   uint32_t take_eq;
   // rank-th smallest == (n - rank + 1)-th largest under the same total order.
-  const uint32_t cut = radix_cut<kSelThreads, false>(RowKeys<kSelThreads>{score, n},
+  const uint32_t cut = radix_cut<kSelThreads, true>(RowKeys<kSelThreads>{score, n},
                                                      static_cast<uint32_t>(n - rank + 1), hist, sh_scan, sh_cut,
                                                      &take_eq);
   if (threadIdx.x == 0) *tau_out = key_score(cut);
@@ -378,21 +390,27 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
   if (n > n_max) n = n_max;
   if (n < 0) n = 0;
   const float tau = *tau_p;
-  constexpr int E = 4;
+  constexpr int E = 16;  // consecutive rows per thread per chunk; all loads issued before use
   uint32_t before = 0u;
   for (int base = 0; base < n; base += kSelThreads * E) {
     const int i0 = base + threadIdx.x * E;
     uint32_t keep_bits = 0u, cnt = 0u;
     int32_t p[E];
+    float sc[E];
+    uint8_t c0[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = i0 + e;
-      p[e] = -1;
-      if (i < n) {
-        const int32_t q = pos ? pos[i] : i;
-        p[e] = q;
-        const uint32_t c = (score[i] < tau) ? static_cast<uint32_t>(counters[q]) + 1u : 0u;
-        counters[q] = static_cast<uint8_t>(c > 255u ? 255u : c);
+      p[e] = i < n ? (pos ? pos[i] : i) : -1;
+      sc[e] = i < n ? score[i] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) c0[e] = p[e] >= 0 ? counters[p[e]] : 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (p[e] >= 0) {
+        const uint32_t c = (sc[e] < tau) ? static_cast<uint32_t>(c0[e]) + 1u : 0u;
+        counters[p[e]] = static_cast<uint8_t>(c > 255u ? 255u : c);
         if (c < static_cast<uint32_t>(patience)) { keep_bits |= 1u << e; ++cnt; }
       }
     }
@@ -426,8 +444,10 @@ void launch_topk_nt(const float* score, int rows, int n, int k, int f, int l, co
     hipLaunchKernelGGL((topk_reg_kernel<NT, 16>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
   else if (n_mid <= NT * 32)
     hipLaunchKernelGGL((topk_reg_kernel<NT, 32>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+  else if (rows == 1)
+    hipLaunchKernelGGL((topk_kernel<NT, true>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
   else
-    hipLaunchKernelGGL((topk_kernel<NT>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+    hipLaunchKernelGGL((topk_kernel<NT, false>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
 }
 
 }  // namespace

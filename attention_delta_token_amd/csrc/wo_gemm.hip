@@ -95,7 +95,7 @@ void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
   int M = m_dev ? *m_dev : M_max;
   if (M > M_max) M = M_max;
   const int n_tiles_m = (M_max + kBM - 1) / kBM;
-  const int lid = xcd_remap(blockIdx.x, n_tiles_m * n_tiles_n);
+  const int lid = xcd_remap_chunked(blockIdx.x, n_tiles_m * n_tiles_n, kGroupM * n_tiles_n);
   // Groups of kGroupM m-tiles sweep all n-tiles together (shared A rows and W
   // k-slices stay in L2 while the group runs).
   const int group = lid / (kGroupM * n_tiles_n);
@@ -253,7 +253,7 @@ void wo_gemm_bf16_n224_kernel(const uint16_t* __restrict__ A, const uint16_t* __
   int M = m_dev ? *m_dev : M_max;
   if (M > M_max) M = M_max;
   const int n_tiles_m = (M_max + kBM - 1) / kBM;
-  const int lid = xcd_remap(blockIdx.x, n_tiles_m * n_tiles_n);
+  const int lid = xcd_remap_chunked(blockIdx.x, n_tiles_m * n_tiles_n, kGroupM * n_tiles_n);
   const int group = lid / (kGroupM * n_tiles_n);
   const int gm = min(kGroupM, n_tiles_m - group * kGroupM);
   const int within = lid - group * kGroupM * n_tiles_n;
