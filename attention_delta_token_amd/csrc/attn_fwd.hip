@@ -18,17 +18,18 @@
 // (32 per wave), 64 keys per step.  Scores are computed transposed,
 // S^T = K · Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one query and
 // 32 of the step's keys: the softmax max and sum stay in registers except for
-// one exchange with the partner half-wave.  The output is accumulated
-// transposed too, O^T += V^T · P^T, where P^T is fed straight from the score
-// accumulators (rounded to bf16) as the B operand and V^T is read from an LDS
-// copy of the V tile stored transposed, keys permuted within groups of 16 so
-// each MFMA operand is one 16-byte read, rows padded so the reads are free of
-// bank conflicts.  K and V tiles arrive through buffer loads (rows past the
-// key count read as zeros), are double-buffered in LDS with register prefetch
-// one tile ahead, and one barrier separates steps.  Workgroups
-// are ordered heaviest-first (causal work grows with the query position) and
-// the q-heads that share a kv-head are placed on the same XCD so they share
-// its L2.
+// one exchange with the partner half-wave.  The query is pre-scaled into exp2
+// units and the score accumulators start at -m, so P is a bare exp2.  The
+// output is accumulated transposed too, O^T += V^T · P^T, where P^T is fed
+// straight from the score accumulators (rounded to bf16) as the B operand and
+// V^T comes from transposing LDS reads (ds_read_b64_tr_b16) of the V tile.
+// K and V tiles go from global memory straight into LDS (buffer loads to LDS,
+// no register staging; rows past the key count read as zeros through the
+// buffer range) into a ring of two K and two V tiles, K two steps ahead and V
+// one; rows are XOR-swizzled so the operand reads are free of bank conflicts,
+// and one barrier separates steps.  Workgroups are ordered heaviest-first
+// (causal work grows with the query position) and the q-heads that share a
+// kv-head are placed on the same XCD so they share its L2.
 #include "dash_common.h"
 #include "dash_kernels.h"
 

@@ -62,7 +62,13 @@ def attn_flops(D, Hq, n):
 
 
 def source_digest(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Digest of a kernel source's code: comments, blank lines and trailing
+    spaces removed, so it changes with the kernel but not with its comments."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", l).rstrip() for l in text.split("\n")]
+    code = "\n".join(l for l in lines if l.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def read_traffic(digest):
@@ -76,7 +82,7 @@ def read_traffic(digest):
     if not m:
         return None
     data = json.loads(m.group(1))
-    if data.get("attn_fwd_sha256_16") != digest:
+    if data.get("attn_fwd_code_sha256_16") != digest:
         return None
     return data
 
