@@ -24,9 +24,9 @@ DASH_SEL_TOPK, DASH_SEL_THRESHOLD, DASH_SEL_ORDER_STAT = 0, 1, 2
 DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE = 0, 1, 2
 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
-            "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_attn_active",
+            "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_attn_active", "dash_score",
             "dash_trace_start", "dash_trace_stop", "dash_trace_read")
-TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact")
+TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact", "score")
 
 
 class DashShape(Structure):
@@ -81,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_compact.restype = c_int
     lib.dash_compact_many.argtypes = [c_void_p, c_void_p, c_void_p, c_int, POINTER(DashGather), c_int, c_void_p]
     lib.dash_compact_many.restype = c_int
+    lib.dash_score.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p]
+    lib.dash_score.restype = c_int
     lib.dash_attn_active.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_int,
                                      c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]
@@ -196,6 +198,15 @@ def dash_compact_many(idx, pairs, n_dev=None, n_max: int | None = None, stream=N
         row_bytes = X[0].numel() * X.element_size() if S > 0 else Xa[0].numel() * Xa.element_size()
         arr[j] = DashGather(_ptr(X), S, row_bytes, _ptr(Xa))
     _check(load().dash_compact_many(None, _ptr(idx), _ptr(n_dev), n_max, arr, len(pairs), _stream(stream)))
+
+
+def dash_score(U, score, n_dev=None, n_max: int | None = None, stream=None) -> None:
+    """score[t] = ||U[t]||_2 for t < n (U [n_max, hidden], bf16 or fp32)."""
+    if n_max is None:
+        n_max = U.shape[0]
+    hidden = U[0].numel() if U.shape[0] > 0 else U.shape[-1]
+    _check(load().dash_score(None, _ptr(U), _dtype_code(U), hidden, _ptr(n_dev), n_max, _ptr(score),
+                             _stream(stream)))
 
 
 def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: int | None = None, Wo=None,

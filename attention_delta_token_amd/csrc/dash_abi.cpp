@@ -40,6 +40,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -316,6 +317,32 @@ int dash_compact(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_
     hipError_t e = dash::launch_compact(idx, n_dev, n_max, X, S, row_bytes, Xa, st);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "compaction launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_score(void* /*ctx*/, const void* U, int dtype, int hidden, const int32_t* n_dev, int n_max, float* score,
+               void* stream) {
+  try {
+    if (dtype != DASH_F32 && dtype != DASH_BF16) return fail(DASH_E_DTYPE, "dtype %d unsupported", dtype);
+    if (n_max < 0) return fail(DASH_E_INVAL, "n_max must be >= 0");
+    const int esz = dtype == DASH_BF16 ? 2 : 4;
+    if (hidden < 1 || (static_cast<int64_t>(hidden) * esz) % 16 != 0)
+      return fail(DASH_E_SHAPE, "hidden %d: rows must be a positive multiple of 16 bytes", hidden);
+    if (static_cast<int64_t>(n_max) * hidden * esz / 16 >= (1ll << 31))
+      return fail(DASH_E_SHAPE, "n_max * hidden too large");
+    if (n_max == 0) return DASH_OK;
+    int rc = check_ptrs({{U, "U"}});
+    if (rc) return rc;
+    if (!score) return fail(DASH_E_INVAL, "score is NULL");
+    if (!aligned4(score)) return fail(DASH_E_ALIGN, "score is not 4-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int tr = trace_open(DASH_TR_SCORE, st);
+    hipError_t e = dash::launch_row_norm(dtype, U, n_dev, n_max, hidden, score, st);
+    trace_close(tr, st);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
     return DASH_OK;
   } catch (...) {
     return fail(DASH_E_INVAL, "unexpected host exception");

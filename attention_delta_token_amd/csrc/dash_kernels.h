@@ -23,6 +23,9 @@ hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_
                             const float* tau, int patience, uint8_t* counters, int32_t* out, int32_t* n_out,
                             hipStream_t stream);
 
+hipError_t launch_row_norm(int dtype, const void* U, const int32_t* n_dev, int n_max, int hidden, float* score,
+                           hipStream_t stream);
+
 // One tensor of a multi-tensor gather: Xa[r] = X[idx[r]], rows of row_bytes.
 constexpr int kMaxGather = 4;
 struct GatherItem {

@@ -143,7 +143,20 @@ def main():
 
     for _ in range(args.warmup):
         step.run()
-    ms = timed(step.run, args.steps)
+    # Per-step HIP events on the launch stream (torch's current stream, which the
+    # binding passes to every call) give the median and minimum step beside the mean.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+
+    def run_marked():
+        i = run_marked.i
+        if i == 0:
+            ev[0].record()
+        step.run()
+        ev[i + 1].record()
+        run_marked.i += 1
+    run_marked.i = 0
+    ms = timed(run_marked, args.steps)
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
 
     # Same steps again with the library's per-launch HIP events (on the launch stream).
     dash.trace_start(128 * args.steps)
@@ -248,6 +261,7 @@ def main():
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
         "ideal_speedup_flops": dense_flops / dash_flops,
         "traced_ms_per_step": ms_traced,
+        "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
         "kernels": {
             "attn_full_ms": avg("attn_layer"), "attn_post_ms": avg("attn_active"),
             "attn_full_tflops": (f_full / (avg("attn_layer") * 1e-3) / 1e12) if t_full else None,
@@ -264,6 +278,7 @@ def main():
 
     if not args.profile_only:
         out["select_sweep"] = [select_sweep(dash, torch, dev, rows, n) for rows, n in ((2048, 8192), (256, 65536))]
+        out["score"] = score_measurements(dash, torch, dev, step, layers[0])
 
     if not args.no_cpu_baseline and not args.profile_only:
         out["cpu_baseline"] = cpu_baseline(w, host_keep, step, k_rows)
@@ -289,6 +304,41 @@ def select_sweep(dash, torch, dev, rows=256, n=65536):
     ms = sum(t) / len(t)
     gbps = rows * (4.0 * n + 4.0 * k) / (ms * 1e-3) / 1e9
     return {"rows": rows, "n": n, "k": k, "ms": ms, "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS}
+
+
+def score_measurements(dash, torch, dev, step, layer):
+    """The score two ways on the full-length layer: standalone (||U_t|| read back
+    from a stored U: hidden * element size B read + 4 B written per row, HBM
+    bound) and fused (the W_o GEMM with and without the sum of squares)."""
+    U = step.U
+    rows, hidden = U.shape
+    score = torch.empty(rows, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        dash.dash_score(U, score)
+    dash.trace_start(64)
+    for _ in range(20):
+        dash.dash_score(U, score)
+    dash.trace_stop()
+    t = [ms for op, ms in dash.trace_read(64) if op == "score"]
+    ms = sum(t) / len(t)
+    gbps = rows * (hidden * U.element_size() + 4.0) / (ms * 1e-3) / 1e9
+    out = {"standalone_us": ms * 1e3, "standalone_GBps": gbps, "standalone_frac": gbps / PEAK_HBM_GBPS,
+           "rows": rows, "hidden": hidden}
+    # fused: the same layer's W_o GEMM with the score and without it
+    ws = step.ws
+    proj = {}
+    for with_score in (True, False, True, False):
+        dash.trace_start(64)
+        for _ in range(10):
+            dash.dash_attn_layer(layer.Q, layer.K, layer.V, layer.Wo, step.O, step.U,
+                                 step.score if with_score else None, ws)
+        dash.trace_stop()
+        proj.setdefault(with_score, []).extend(ms for op, ms in dash.trace_read(64) if op == "proj_layer")
+    with_ms = sum(proj[True]) / len(proj[True])
+    without_ms = sum(proj[False]) / len(proj[False])
+    out.update({"fused_proj_us": with_ms * 1e3, "plain_proj_us": without_ms * 1e3,
+                "fused_overhead_us": (with_ms - without_ms) * 1e3})
+    return out
 
 
 def describe(w):

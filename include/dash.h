@@ -148,6 +148,17 @@ int dash_select(void* ctx, const dash_sel* p, const float* score, const int32_t*
                 int32_t* idx, int32_t* n_out_dev, float* tau_out,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Δattn from a given U ([P1] §2.1, §2.2: the score needs only U, so any
+ * attention kernel can feed it): score[t] = ||U_t||_2 (fp32 sums of squares,
+ * fixed order) for t < n, n = *n_dev (or n_max).  U is [n_max, hidden] of
+ * dtype (bf16 or fp32), row-major, 16-byte aligned, hidden * element size a
+ * multiple of 16 (hidden % 8 == 0 for bf16, % 4 for fp32).  score[t] for
+ * t >= n is left untouched.  dash_attn_layer / dash_attn_active produce the
+ * same score fused into their W_o GEMM; this call serves a U made elsewhere.
+ * No workspace. */
+int dash_score(void* ctx, const void* U, int dtype, int hidden, const int32_t* n_dev, int n_max, float* score,
+               void* stream);
+
 /* a4: compaction ([P1] §3.1 step 4, §3.3): Xa[r, :] = X[idx[r], :] for
  * r < n, n = *n_dev (or n_max).  X has S rows of row_bytes bytes (a multiple
  * of 16).  A row whose idx[r] lies outside [0, S) is not copied (its Xa row is
@@ -203,7 +214,8 @@ typedef enum {
   DASH_TR_ATTN_ACTIVE = 2,  /* attention kernel of dash_attn_active */
   DASH_TR_PROJ_ACTIVE = 3,  /* W_o GEMM (+ score finalize) of dash_attn_active */
   DASH_TR_SELECT = 4,       /* selection kernel of dash_select */
-  DASH_TR_COMPACT = 5       /* gather kernel of dash_compact */
+  DASH_TR_COMPACT = 5,      /* gather kernel of dash_compact / dash_compact_many */
+  DASH_TR_SCORE = 6         /* row-norm kernel of dash_score */
 } dash_trace_op;
 
 int dash_trace_start(int capacity);

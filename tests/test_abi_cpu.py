@@ -140,6 +140,17 @@ def test_compact_many_validation(lib):
     assert f(None, None, None, 0, arr(good), 1, None) == L.DASH_OK  # nothing to do
 
 
+def test_score_validation(lib):
+    f = lib.dash_score
+    assert f(None, FAKE, 7, 256, None, 10, FAKE, None) == L.DASH_E_DTYPE
+    assert f(None, FAKE, L.DASH_BF16, 12, None, 10, FAKE, None) == L.DASH_E_SHAPE  # 24-byte rows
+    assert f(None, FAKE, L.DASH_F32, 0, None, 10, FAKE, None) == L.DASH_E_SHAPE
+    assert f(None, FAKE + 8, L.DASH_BF16, 256, None, 10, FAKE, None) == L.DASH_E_ALIGN
+    assert f(None, FAKE, L.DASH_BF16, 256, None, 10, None, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, L.DASH_BF16, 256, None, 10, FAKE + 2, None) == L.DASH_E_ALIGN
+    assert f(None, None, L.DASH_BF16, 256, None, 0, None, None) == L.DASH_OK  # nothing to do
+
+
 def test_attn_active_validation(lib):
     f = lib.dash_attn_active
     s = _shape()

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from workload import WORKLOADS, SCORE_KINDS, layer_inputs, score_vector
+from workload import WORKLOADS, SCORE_KINDS, layer_inputs, round_bf16, score_vector
 
 pytestmark = pytest.mark.gpu
 
@@ -284,6 +284,29 @@ def test_compact_many_bit_exact(dash, widths, device_n):
         got = Xa.cpu().numpy()
         np.testing.assert_array_equal(got[:n][ok], oracle.compact(X, idx[:n][ok]))
         assert np.all(got[:n][~ok] == 0xCD) and np.all(got[n:] == 0xCD)
+
+
+@pytest.mark.parametrize("dtype,hidden", [("bf16", 3584), ("bf16", 4096), ("bf16", 8), ("bf16", 264),
+                                          ("f32", 256), ("f32", 4)])
+@pytest.mark.parametrize("n,device_n", [(1, False), (1000, False), (8193, True)])
+def test_score_standalone(dash, dtype, hidden, n, device_n):
+    """score[t] = ||U_t||_2 from a given U, against the oracle's definition; fp32
+    sums of `hidden` positive terms: relative error below hidden * 2^-24."""
+    rng = np.random.default_rng(hidden + n)
+    U = (rng.standard_normal((n, hidden)) * rng.lognormal(0, 1, (n, 1))).astype(np.float32)
+    if dtype == "bf16":
+        U = round_bf16(U)
+    Ud = torch.from_numpy(U).to("cuda", torch.bfloat16 if dtype == "bf16" else torch.float32)
+    score = torch.full((n,), -1.0, dtype=torch.float32, device="cuda")
+    m = n - 7 if device_n else n
+    nd = torch.tensor([m, 0, 0, 0], dtype=torch.int32, device="cuda") if device_n else None
+    say("score standalone", dtype, hidden, n, device_n)
+    dash.dash_score(Ud, score, n_dev=nd, n_max=n)
+    torch.cuda.synchronize()
+    got = score.cpu().numpy()
+    ref = oracle.delta_attn(U[:m])
+    assert np.all(np.abs(got[:m] - ref) <= max(hidden, 16) * 2.0 ** -24 * ref)
+    assert np.all(got[m:] == -1.0)
 
 
 # ---------------------------------------------------------------------------
