@@ -26,6 +26,7 @@ namespace dash {
 namespace {
 
 constexpr int kSelThreads = 1024;  // one workgroup per row
+constexpr int kWaveRowsMin = 256;  // from this many rows on, short rows take one wave each
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kBins = 2048;
 // Each histogram is kept in kCopies copies, lane l counting into copy
@@ -432,6 +433,150 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
 
 namespace {
 
+// ---------------------------------------------------------------------------
+// Batched rows: one wave per row, no workgroup barrier anywhere.  Lane l holds
+// the keys of positions 256*j + 4*l + e (e < 4, j < J) in registers (one
+// 16-byte load each), counts into its wave's own 2048-bin LDS histogram, and
+// settles the cut with wave scans; the emit walks the 256-position chunks in
+// order with one scan each.  Rows are n % 4 == 0 scores, 16-byte aligned.
+// ---------------------------------------------------------------------------
+constexpr int kWaveRowsPerBlock = 4;
+
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+template <int J>
+__global__ __launch_bounds__(kWaveRowsPerBlock * kWave)
+void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist_all[kWaveRowsPerBlock * kBins];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int row = blockIdx.x * kWaveRowsPerBlock + w;
+  if (row >= rows) return;  // the whole wave leaves; nothing below synchronises waves
+  uint32_t* h = hist_all + w * kBins;
+  const u32x4* r4 = reinterpret_cast<const u32x4*>(score + static_cast<size_t>(row) * n);
+  int32_t* out = idx + static_cast<size_t>(row) * k;
+  const int n4 = n >> 2;
+  uint32_t keys[J][4];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i4 = j * kWave + lane;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (i4 < n4) v = __builtin_nontemporal_load(r4 + i4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keys[j][e] = score_key(__uint_as_float(v[e]));
+  }
+  auto valid = [&](int j) { return j * kWave + lane < n4; };
+
+  // Bits shared by every key of the row are settled first (wave min/max of the
+  // keys in registers); digits of up to 11 bits then start right below them, so
+  // a narrow score range spreads over many bins instead of piling same-address
+  // atomics onto a few.  (Widths are computed, not looked up: a table would put
+  // scalar loads on the counter the LDS atomics use.)
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (valid(j)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kmin = min(kmin, keys[j][e]);
+        kmax = max(kmax, keys[j][e]);
+      }
+    }
+  }
+  kmin = wave_incl_scan_op(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
+  kmax = wave_incl_scan_op(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+  kmin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kmin), kWave - 1));
+  kmax = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(kmax), kWave - 1));
+  const int common = kmin == kmax ? 32 : __clz(kmin ^ kmax);
+  uint32_t pmask = static_cast<uint32_t>(0xffffffff00000000ull >> common);
+  uint32_t prefix = kmin & pmask, kk = static_cast<uint32_t>(k);
+  constexpr int kBPL = kBins / kWave;  // bins per lane in the scan (32)
+  int sh = 32 - common;
+#pragma unroll 1
+  while (sh > 0) {
+    const int wd = sh < 11 ? sh : 11;
+    sh -= wd;
+    const uint32_t dm = (1u << wd) - 1u;
+#pragma unroll
+    for (int b = 0; b < kBPL; ++b) h[b * kWave + lane] = 0u;
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (valid(j)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((keys[j][e] & pmask) == prefix) atomicAdd(&h[(keys[j][e] >> sh) & dm], 1u);
+      }
+    }
+    wave_lds_fence();
+    const int nb = static_cast<int>(dm) + 1;
+    const int b0 = lane * kBPL;
+    uint32_t c[kBPL];
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int b = 0; b < kBPL; ++b) {
+      c[b] = (b0 + b < nb) ? h[b0 + b] : 0u;
+      mine += c[b];
+    }
+    const uint32_t incl = wave_incl_scan32(mine);
+    const uint32_t tot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+    uint32_t upto = incl - mine;  // keys in bins below b0
+    uint32_t found_bin = 0u, found_kk = 0u;
+    bool found = false;
+#pragma unroll
+    for (int b = 0; b < kBPL; ++b) {
+      upto += c[b];
+      const uint32_t above = tot - upto;  // keys in bins above b0 + b
+      if (b0 + b < nb && above < kk && kk <= above + c[b]) {
+        found = true;
+        found_bin = static_cast<uint32_t>(b0 + b);
+        found_kk = kk - above;
+      }
+    }
+    const uint64_t who = __ballot(found);
+    const int src = static_cast<int>(__builtin_ctzll(who));
+    const uint32_t bin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(found_bin), src));
+    kk = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(found_kk), src));
+    prefix |= bin << sh;
+    pmask |= dm << sh;
+  }
+  const uint32_t cut = prefix, take_eq = kk;
+
+  // Emit in position order: chunk j covers positions 256*j .. 256*j + 255, lane
+  // l its four positions 256*j + 4*l + e.
+  uint32_t sel_before = 0u, eq_before = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    uint32_t gt_bits = 0u, eq_bits = 0u;
+    if (valid(j)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (keys[j][e] > cut) gt_bits |= 1u << e;
+        else if (keys[j][e] == cut) eq_bits |= 1u << e;
+      }
+    }
+    const uint32_t packed = (static_cast<uint32_t>(__popc(gt_bits)) << 16) | static_cast<uint32_t>(__popc(eq_bits));
+    const uint32_t incl = wave_incl_scan32(packed);  // per-chunk sums stay below 2^16
+    const uint32_t tot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+    const uint32_t excl = incl - packed;
+    uint32_t eq_rank = eq_before + (excl & 0xffffu);
+    const uint32_t taken_eq_before = min(eq_rank, take_eq) - min(eq_before, take_eq);
+    uint32_t o = sel_before + (excl >> 16) + taken_eq_before;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool take = (gt_bits >> e) & 1u;
+      if ((eq_bits >> e) & 1u) { take = eq_rank < take_eq; ++eq_rank; }
+      if (take) {
+        if (o < static_cast<uint32_t>(k)) out[o] = j * 4 * kWave + 4 * lane + e;
+        ++o;
+      }
+    }
+    const uint32_t tot_eq = tot & 0xffffu;
+    sel_before += (tot >> 16) + (min(eq_before + tot_eq, take_eq) - min(eq_before, take_eq));
+    eq_before += tot_eq;
+  }
+}
+
 template <int NT>
 void launch_topk_nt(const float* score, int rows, int n, int k, int f, int l, const int32_t* pos, int32_t* idx,
                     hipStream_t stream) {
@@ -452,10 +597,24 @@ void launch_topk_nt(const float* score, int rows, int n, int k, int f, int l, co
 
 }  // namespace
 
+// Many rows of at most 8192 aligned scores without forced ends or a position
+// map: one wave per row.  Otherwise one 1024-thread workgroup per row.
 hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
                        const int32_t* pos, int32_t* idx, hipStream_t stream) {
   if (rows == 0 || k == 0) return hipSuccess;
-  launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, stream);
+  const bool wave_rows = rows >= kWaveRowsMin && !pos && keep_first == 0 && keep_last == 0 && n % 4 == 0 &&
+                         n <= 8192 && (reinterpret_cast<uintptr_t>(score) & 15u) == 0;
+  if (wave_rows) {
+    const dim3 grid((rows + kWaveRowsPerBlock - 1) / kWaveRowsPerBlock), block(kWaveRowsPerBlock * kWave);
+    if (n <= 2048)
+      hipLaunchKernelGGL(topk_wave_kernel<8>, grid, block, 0, stream, score, rows, n, k, idx);
+    else if (n <= 4096)
+      hipLaunchKernelGGL(topk_wave_kernel<16>, grid, block, 0, stream, score, rows, n, k, idx);
+    else
+      hipLaunchKernelGGL(topk_wave_kernel<32>, grid, block, 0, stream, score, rows, n, k, idx);
+  } else {
+    launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, stream);
+  }
   return hipGetLastError();
 }
 

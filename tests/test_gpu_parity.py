@@ -82,10 +82,12 @@ def test_topk_bit_exact(dash, kind, n):
 
 
 @pytest.mark.parametrize("rows,n,k", [(48, 3000, 1234), (80, 3000, 1234), (70, 8192, 4096), (64, 8193, 100),
-                                      (66, 1, 1), (65, 40000, 39999)])
+                                      (66, 1, 1), (65, 40000, 39999),
+                                      (256, 8192, 4096), (300, 2048, 1000), (257, 4, 2), (512, 4100, 1),
+                                      (256, 12, 12), (264, 1000, 999), (256, 3001, 100), (256, 8196, 77)])
 def test_topk_batched_rows(dash, rows, n, k):
-    """Batches of independent rows (from 64 rows on, rows fit in 256-thread workgroups
-    when n <= 8192; longer rows and smaller batches use 1024 threads)."""
+    """Batches of independent rows: from 256 rows of at most 8192 scores (n % 4 == 0)
+    one wave per row; otherwise one 1024-thread workgroup per row."""
     s = np.stack([score_vector("fewvalues" if r % 2 else ("bf16ties" if r % 3 else "normal"), n, seed=r)
                   for r in range(rows)])
     idx = torch.empty(rows, k, dtype=torch.int32, device="cuda")
