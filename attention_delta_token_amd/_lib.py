@@ -24,7 +24,8 @@ DASH_SEL_TOPK, DASH_SEL_THRESHOLD, DASH_SEL_ORDER_STAT = 0, 1, 2
 DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE = 0, 1, 2
 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
-            "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_attn_active", "dash_score",
+            "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
+            "dash_attn_active", "dash_score",
             "dash_trace_start", "dash_trace_stop", "dash_trace_read")
 TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact", "score")
 
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_compact.restype = c_int
     lib.dash_compact_many.argtypes = [c_void_p, c_void_p, c_void_p, c_int, POINTER(DashGather), c_int, c_void_p]
     lib.dash_compact_many.restype = c_int
+    lib.dash_compact_batch.argtypes = [c_void_p, c_void_p, c_int, c_int, POINTER(DashGather), c_int, c_void_p]
+    lib.dash_compact_batch.restype = c_int
     lib.dash_score.argtypes = [c_void_p, c_void_p, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p]
     lib.dash_score.restype = c_int
     lib.dash_attn_active.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_int,
@@ -200,6 +203,18 @@ def dash_compact_many(idx, pairs, n_dev=None, n_max: int | None = None, stream=N
     _check(load().dash_compact_many(None, _ptr(idx), _ptr(n_dev), n_max, arr, len(pairs), _stream(stream)))
 
 
+def dash_compact_batch(idx, pairs, stream=None) -> None:
+    """Per-sample gathers of B samples in one launch: idx [B, k] local positions;
+    for each (X [B, S, ...], Xa [B, k, ...]) in pairs, Xa[b, r] = X[b, idx[b, r]]."""
+    B, k = idx.shape
+    arr = (DashGather * len(pairs))()
+    for j, (X, Xa) in enumerate(pairs):
+        S = X.shape[1]
+        row_bytes = X[0, 0].numel() * X.element_size() if S > 0 else Xa[0, 0].numel() * Xa.element_size()
+        arr[j] = DashGather(_ptr(X), S, row_bytes, _ptr(Xa))
+    _check(load().dash_compact_batch(None, _ptr(idx), B, k, arr, len(pairs), _stream(stream)))
+
+
 def dash_score(U, score, n_dev=None, n_max: int | None = None, stream=None) -> None:
     """score[t] = ||U[t]||_2 for t < n (U [n_max, hidden], bf16 or fp32)."""
     if n_max is None:
@@ -212,15 +227,22 @@ def dash_score(U, score, n_dev=None, n_max: int | None = None, stream=None) -> N
 def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: int | None = None, Wo=None,
                      Ua=None, score=None, ws=None, S: int | None = None, hidden: int | None = None,
                      stream=None) -> None:
-    """Post-halt attention (see include/dash.h).  Qa [n,Hq,D]; K, V [n or S, Hkv, D]."""
-    n_cap, Hq, D = Qa.shape
+    """Post-halt attention (see include/dash.h).  Qa [n,Hq,D] or [B,n,Hq,D];
+    K, V [n or S, Hkv, D] or [B, n or S, Hkv, D]."""
+    if Qa.dim() == 4:
+        B, n_cap, Hq, D = Qa.shape
+        kv_rows, Hkv = K.shape[1], K.shape[2]
+    else:
+        B = 1
+        n_cap, Hq, D = Qa.shape
+        kv_rows, Hkv = K.shape[0], K.shape[1]
     if n_max is None:
         n_max = n_cap
     if S is None:
-        S = K.shape[0] if kv_mode == DASH_KV_ALL else n_max
+        S = kv_rows if kv_mode == DASH_KV_ALL else n_max
     if hidden is None:
         hidden = Wo.shape[0] if Wo is not None else Hq * D
-    shape = make_shape(1, S, Hq, K.shape[1], D, hidden, _dtype_code(Qa))
+    shape = make_shape(B, S, Hq, Hkv, D, hidden, _dtype_code(Qa))
     _check(load().dash_attn_active(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(n_dev), n_max, _ptr(K),
                                    _ptr(V), kv_mode, _ptr(Oa), _ptr(Wo), _ptr(Ua), _ptr(score), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))

@@ -141,7 +141,8 @@ __global__ __launch_bounds__(kAttnThreads, 2)
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_dev, int n_q_max,
-                          int n_kv, int Hq, int Hkv, float c_log2, int64_t q_bs, int64_t kv_bs, int64_t o_bs) {
+                          int n_kv, int Hq, int Hkv, float c_log2, int64_t q_bs, int64_t kv_bs, int64_t o_bs,
+                          int qp_bs) {
   using C = AttnCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kTotal];
 
@@ -158,6 +159,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int64_t b = blockIdx.y;
   Q += b * q_bs;
   O += b * o_bs;
+  if (q_pos) q_pos += b * qp_bs;
   K += b * kv_bs + static_cast<int64_t>(kvh) * D;
   V += b * kv_bs + static_cast<int64_t>(kvh) * D;
   const int q_ld = Hq * D;
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(64)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                          float* __restrict__ O, const int32_t* __restrict__ q_pos,
                          const int32_t* __restrict__ n_dev, int n_q_max, int n_kv, int Hq, int Hkv, float scale,
-                         int64_t q_bs, int64_t kv_bs, int64_t o_bs) {
+                         int64_t q_bs, int64_t kv_bs, int64_t o_bs, int qp_bs) {
   __shared__ float ks[64][D];
   __shared__ float vs[64][D];
   int n_q = n_dev ? *n_dev : n_q_max;
@@ -439,6 +441,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   const int64_t b = blockIdx.z;
   Q += b * q_bs;
   O += b * o_bs;
+  if (q_pos) q_pos += b * qp_bs;
   K += b * kv_bs + static_cast<int64_t>(kvh) * D;
   V += b * kv_bs + static_cast<int64_t>(kvh) * D;
   const int q_ld = Hq * D, kv_ld = Hkv * D;
@@ -487,7 +490,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 
 hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* K, const void* V, void* O,
                             const int32_t* q_pos, const int32_t* n_dev, int n_q_max, int n_kv, int Hq, int Hkv,
-                            int64_t q_bs, int64_t kv_bs, int64_t o_bs, hipStream_t stream) {
+                            int64_t q_bs, int64_t kv_bs, int64_t o_bs, int qp_bs, hipStream_t stream) {
   if (n_q_max <= 0 || B <= 0) return hipSuccess;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   if (dtype == 1) {
@@ -500,10 +503,10 @@ hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* 
     auto o = static_cast<uint16_t*>(O);
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
-                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs);
+                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs, qp_bs);
     else if (D == 64)
       hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
-                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs);
+                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs, qp_bs);
     else
       return hipErrorInvalidValue;
   } else {
@@ -514,13 +517,13 @@ hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* 
     auto o = static_cast<float*>(O);
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
-                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs);
+                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs, qp_bs);
     else if (D == 64)
       hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
-                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs);
+                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs, qp_bs);
     else if (D == 32)
       hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
-                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs);
+                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs, qp_bs);
     else
       return hipErrorInvalidValue;
   }

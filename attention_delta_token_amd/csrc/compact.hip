@@ -1,4 +1,4 @@
-// Compaction of active rows: Xa[r] = X[idx[r]] — the gather of the selected
+// Compaction of active rows: Xa[r] = X[idx[r]] (batched: Xa[b, r] = X[b, idx[b, r]]) — the gather of the selected
 // tokens that later layers work on, from the CSDN explainer
 // "DASH：基于注意力增量的Transformer令牌压缩，实现长序列推理高效加速", §3.1 step 4
 // and §3.3 (gather by the active index set, avoiding needless copies).
@@ -42,7 +42,8 @@ __device__ __forceinline__ T pick(const T (&a)[kMaxGather], int j) {
 }
 
 __global__ __launch_bounds__(kCompactThreads)
-void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_dev, int n_max, GatherSet g) {
+void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_dev, int n_max, int per_sample,
+                    GatherSet g) {
   int n = n_dev ? *n_dev : n_max;
   if (n > n_max) n = n_max;
   const uint32_t cpr = g.cpr;
@@ -65,8 +66,11 @@ void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__
       const uint32_t cj = c - pick(g.lo, j);
       const uint32_t w = pick(g.w, j);
       const int32_t src = idx[r];
-      if (src >= 0 && src < pick(g.S, j)) {
-        v[it] = __builtin_nontemporal_load(pick(g.X, j) + static_cast<uint64_t>(src) * w + cj);
+      const int Sj = pick(g.S, j);
+      if (src >= 0 && src < Sj) {
+        // batched: row r belongs to sample r / per_sample, whose rows start at sample * S
+        const uint64_t base = per_sample > 0 ? static_cast<uint64_t>(r / static_cast<uint32_t>(per_sample)) * Sj : 0u;
+        v[it] = __builtin_nontemporal_load(pick(g.X, j) + (base + static_cast<uint64_t>(src)) * w + cj);
         dst[it] = pick(g.Xa, j) + static_cast<uint64_t>(r) * w + cj;
       }
     }
@@ -79,7 +83,7 @@ void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__
 }  // namespace
 
 hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_max, const GatherItem* items,
-                               int count, hipStream_t stream) {
+                               int count, hipStream_t stream, int per_sample) {
   if (n_max <= 0 || count <= 0) return hipSuccess;
   if (count > kMaxGather) return hipErrorInvalidValue;
   GatherSet g{};
@@ -106,14 +110,14 @@ hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_m
   if (blocks == 0) return hipSuccess;
   if (total >= 0x80000000ull) return hipErrorInvalidValue;
   hipLaunchKernelGGL(compact_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCompactThreads), 0, stream, idx,
-                     n_dev, n_max, g);
+                     n_dev, n_max, per_sample, g);
   return hipGetLastError();
 }
 
 hipError_t launch_compact(const int32_t* idx, const int32_t* n_dev, int n_max, const void* X, int S,
                           size_t row_bytes, void* Xa, hipStream_t stream) {
   const GatherItem one{X, S, row_bytes, Xa};
-  return launch_compact_many(idx, n_dev, n_max, &one, 1, stream);
+  return launch_compact_many(idx, n_dev, n_max, &one, 1, stream, 0);
 }
 
 }  // namespace dash

@@ -193,8 +193,8 @@ size_t dash_workspace_size(void* /*ctx*/, int op, const dash_shape* s, int n_max
         if (check_shape(s, false) != DASH_OK) return 0;
         return score_ws_bytes(s, static_cast<int64_t>(s->B) * s->S);
       case DASH_OP_ATTN_ACTIVE:
-        if (check_shape(s, true) != DASH_OK || n_max < 0) return 0;
-        return score_ws_bytes(s, n_max);
+        if (check_shape(s, false) != DASH_OK || n_max < 0) return 0;
+        return score_ws_bytes(s, static_cast<int64_t>(s->B) * n_max);
       case DASH_OP_SELECT:
         return 0;  // selection keeps its state in LDS
       default:
@@ -224,7 +224,7 @@ int dash_attn_layer(void* /*ctx*/, const dash_shape* s, const void* Q, const voi
     const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
     int tr = trace_open(DASH_TR_ATTN_LAYER, st);
     hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Q, K, V, O, nullptr, nullptr, s->S, s->S, s->Hq,
-                                          s->Hkv, s->S * qd, s->S * kvd, s->S * qd, st);
+                                          s->Hkv, s->S * qd, s->S * kvd, s->S * qd, 0, st);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     tr = trace_open(DASH_TR_PROJ_LAYER, st);
@@ -349,8 +349,10 @@ int dash_score(void* /*ctx*/, const void* U, int dtype, int hidden, const int32_
   }
 }
 
-int dash_compact_many(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_max, const dash_gather* items,
-                      int count, void* stream) {
+namespace {
+
+int compact_many_impl(const int32_t* idx, const int32_t* n_dev, int n_max, const dash_gather* items, int count,
+                      void* stream, int per_sample) {
   try {
     if (n_max < 0) return fail(DASH_E_INVAL, "n_max must be >= 0");
     if (count < 1 || count > dash::kMaxGather)
@@ -376,7 +378,7 @@ int dash_compact_many(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, i
       return fail(DASH_E_INVAL, "n_max * summed row_bytes too large");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int tr = trace_open(DASH_TR_COMPACT, st);
-    hipError_t e = dash::launch_compact_many(idx, n_dev, n_max, g, count, st);
+    hipError_t e = dash::launch_compact_many(idx, n_dev, n_max, g, count, st, per_sample);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "compaction launch");
     return DASH_OK;
@@ -385,12 +387,31 @@ int dash_compact_many(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, i
   }
 }
 
+}  // namespace
+
+int dash_compact_many(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_max, const dash_gather* items,
+                      int count, void* stream) {
+  return compact_many_impl(idx, n_dev, n_max, items, count, stream, 0);
+}
+
+int dash_compact_batch(void* /*ctx*/, const int32_t* idx, int B, int k, const dash_gather* items, int count,
+                       void* stream) {
+  if (B < 1 || k < 0) return fail(DASH_E_INVAL, "B must be >= 1 and k >= 0");
+  if (static_cast<int64_t>(B) * k > (1ll << 30)) return fail(DASH_E_INVAL, "B * k too large");
+  if (items && count >= 1 && count <= dash::kMaxGather)
+    for (int j = 0; j < count; ++j)
+      if (static_cast<int64_t>(B) * items[j].S > (1ll << 30))
+        return fail(DASH_E_INVAL, "B * items[%d].S too large", j);
+  return compact_many_impl(idx, nullptr, B * k, items, count, stream, k);
+}
+
 int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const int32_t* q_pos,
                      const int32_t* n_dev, int n_max, const void* K, const void* V, int kv_mode, void* Oa,
                      const void* Wo, void* Ua, float* score, void* ws, size_t ws_bytes, void* stream) {
   try {
-    int rc = check_shape(s, true);
+    int rc = check_shape(s, false);
     if (rc) return rc;
+    if (s->B > 1 && n_dev) return fail(DASH_E_SHAPE, "a device row count (n_dev) needs B == 1");
     if (kv_mode != DASH_KV_ACTIVE && kv_mode != DASH_KV_ALL) return fail(DASH_E_INVAL, "kv_mode %d unknown", kv_mode);
     if (n_max < 0 || n_max > s->S) return fail(DASH_E_INVAL, "n_max %d outside [0, S=%d]", n_max, s->S);
     if (n_max == 0) return DASH_OK;
@@ -402,7 +423,7 @@ int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const i
       if (rc) return rc;
       if (score) {
         if (!aligned16(score)) return fail(DASH_E_ALIGN, "score is not 16-byte aligned");
-        const size_t need = score_ws_bytes(s, n_max);
+        const size_t need = score_ws_bytes(s, static_cast<int64_t>(s->B) * n_max);
         if (!ws || ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
         if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
       }
@@ -411,19 +432,22 @@ int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const i
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
+    const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
     // ACTIVE: keys are the compacted rows aligned with the queries (their count
     // follows the query count, -1); ALL: the layer's S rows at their positions.
     const int n_kv = kv_mode == DASH_KV_ACTIVE ? (n_dev ? -1 : n_max) : s->S;
     const int32_t* qp = kv_mode == DASH_KV_ALL ? q_pos : nullptr;
+    const int64_t kv_rows = kv_mode == DASH_KV_ACTIVE ? n_max : s->S;  // per sample
     int tr = trace_open(DASH_TR_ATTN_ACTIVE, st);
-    hipError_t e = dash::launch_attention(s->dtype, 1, s->D, Qa, K, V, Oa, qp, n_dev, n_max, n_kv, s->Hq, s->Hkv,
-                                          0, 0, 0, st);
+    hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Qa, K, V, Oa, qp, n_dev, n_max, n_kv, s->Hq,
+                                          s->Hkv, n_max * qd, kv_rows * kvd, n_max * qd, n_max, st);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (Wo) {
+      // the B samples' rows are contiguous: one GEMM over B * n_max rows
       tr = trace_open(DASH_TR_PROJ_ACTIVE, st);
-      e = dash::launch_wo_gemm(s->dtype, Oa, Wo, Ua, score, static_cast<float*>(ws), n_dev, n_max, s->hidden,
-                               static_cast<int>(qd), st);
+      e = dash::launch_wo_gemm(s->dtype, Oa, Wo, Ua, score, static_cast<float*>(ws), n_dev, s->B * n_max,
+                               s->hidden, static_cast<int>(qd), st);
       trace_close(tr, st);
       if (e != hipSuccess) return hip_fail(e, "projection launch");
     }

@@ -9,7 +9,7 @@ namespace dash {
 // dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* K, const void* V, void* O,
                             const int32_t* q_pos, const int32_t* n_dev, int n_q_max, int n_kv, int Hq, int Hkv,
-                            int64_t q_bs, int64_t kv_bs, int64_t o_bs, hipStream_t stream);
+                            int64_t q_bs, int64_t kv_bs, int64_t o_bs, int qp_bs, hipStream_t stream);
 
 int wo_gemm_parts(int dtype, int N);
 hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, float* score, float* part,
@@ -34,8 +34,10 @@ struct GatherItem {
   size_t row_bytes;
   void* Xa;
 };
+// per_sample > 0: idx holds per_sample local row indices per sample; row r
+// reads X row (r / per_sample) * S + idx[r].
 hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_max, const GatherItem* items,
-                               int count, hipStream_t stream);
+                               int count, hipStream_t stream, int per_sample = 0);
 hipError_t launch_compact(const int32_t* idx, const int32_t* n_dev, int n_max, const void* X, int S,
                           size_t row_bytes, void* Xa, hipStream_t stream);
 

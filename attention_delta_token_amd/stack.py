@@ -34,55 +34,71 @@ class LayerTensors:
 
 
 def _shape_of(layer: LayerTensors):
+    """(B, S, Hq, Hkv, D, hidden); Q is [S, Hq, D] (B = 1) or [B, S, Hq, D]."""
+    if layer.Q.dim() == 4:
+        B, S, Hq, D = layer.Q.shape
+        return B, S, Hq, layer.K.shape[2], D, layer.Wo.shape[0]
     S, Hq, D = layer.Q.shape
-    return S, Hq, layer.K.shape[1], D, layer.Wo.shape[0]
+    return 1, S, Hq, layer.K.shape[1], D, layer.Wo.shape[0]
 
 
 class OneShotStack:
     """Layers 0..hl full length, top-k at hl (optionally forcing the first
-    keep_first and last keep_last tokens in), layers hl+1..L-1 on the kept rows."""
+    keep_first and last keep_last tokens in), layers hl+1..L-1 on the kept rows.
+    Layers may hold one sample (Q [S, Hq, D]) or B samples of equal length
+    (Q [B, S, Hq, D]); every sample keeps k tokens."""
 
     def __init__(self, layers: list[LayerTensors], halt_layer: int, k: int, kv_mode: int = L.DASH_KV_ACTIVE,
                  keep_first: int = 0, keep_last: int = 0):
         self.layers = layers
         self.hl = halt_layer
-        self.k = k  # total kept, forced ends included
+        self.k = k  # total kept per sample, forced ends included
         self.kv_mode = kv_mode
         self.keep_first, self.keep_last = keep_first, keep_last
-        S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        B, S, Hq, Hkv, D, hidden = _shape_of(layers[0])
         dev, dt = layers[0].Q.device, layers[0].Q.dtype
-        self.S, self.Hq, self.Hkv, self.D, self.hidden = S, Hq, Hkv, D, hidden
-        self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
-        self.U = torch.empty(S, hidden, device=dev, dtype=dt)
-        self.score = torch.empty(S, device=dev, dtype=torch.float32)
-        self.idx = torch.empty(max(k, 1), device=dev, dtype=torch.int32)
-        self.Qa = torch.empty(max(k, 1), Hq, D, device=dev, dtype=dt)
-        self.Ka = torch.empty(max(k, 1), Hkv, D, device=dev, dtype=dt)
-        self.Va = torch.empty(max(k, 1), Hkv, D, device=dev, dtype=dt)
-        self.Oa = torch.empty(max(k, 1), Hq * D, device=dev, dtype=dt)
-        self.Ua = torch.empty(max(k, 1), hidden, device=dev, dtype=dt)
+        self.B, self.S, self.Hq, self.Hkv, self.D, self.hidden = B, S, Hq, Hkv, D, hidden
+        lead = (B,) if layers[0].Q.dim() == 4 else ()
+        kk = max(k, 1)
+        self.O = torch.empty(*lead, S, Hq * D, device=dev, dtype=dt)
+        self.U = torch.empty(*lead, S, hidden, device=dev, dtype=dt)
+        self.score = torch.empty(*lead, S, device=dev, dtype=torch.float32)
+        self.idx = torch.empty(*lead, kk, device=dev, dtype=torch.int32)
+        self.Qa = torch.empty(*lead, kk, Hq, D, device=dev, dtype=dt)
+        self.Ka = torch.empty(*lead, kk, Hkv, D, device=dev, dtype=dt)
+        self.Va = torch.empty(*lead, kk, Hkv, D, device=dev, dtype=dt)
+        self.Oa = torch.empty(*lead, kk, Hq * D, device=dev, dtype=dt)
+        self.Ua = torch.empty(*lead, kk, hidden, device=dev, dtype=dt)
         dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
-        self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
+        self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(B, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
 
     def full_layer(self, l: int, with_score: bool) -> None:
         x = self.layers[l]
         L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.score if with_score else None, self.ws)
 
     def select(self) -> None:
-        L.dash_select(self.score, self.idx, mode=L.DASH_SEL_TOPK, k=self.k, keep_first=self.keep_first,
-                      keep_last=self.keep_last)
+        L.dash_select(self.score, self.idx, mode=L.DASH_SEL_TOPK, k=self.k, n_max=self.S, rows=self.B,
+                      keep_first=self.keep_first, keep_last=self.keep_last)
 
     def post_layer(self, l: int) -> None:
         x = self.layers[l]
         k = self.k
         if k == 0:
             return
+        batched = x.Q.dim() == 4
         if self.kv_mode == L.DASH_KV_ACTIVE:
-            L.dash_compact_many(self.idx, [(x.Q, self.Qa), (x.K, self.Ka), (x.V, self.Va)], n_max=k)
+            pairs = [(x.Q, self.Qa), (x.K, self.Ka), (x.V, self.Va)]
+            if batched:
+                L.dash_compact_batch(self.idx, pairs)
+            else:
+                L.dash_compact_many(self.idx, pairs, n_max=k)
             L.dash_attn_active(self.Qa, self.Ka, self.Va, L.DASH_KV_ACTIVE, self.Oa, n_max=k, Wo=x.Wo,
                                Ua=self.Ua)
         else:
-            L.dash_compact(self.idx, x.Q, self.Qa, n_max=k)
+            if batched:
+                L.dash_compact_batch(self.idx, [(x.Q, self.Qa)])
+            else:
+                L.dash_compact(self.idx, x.Q, self.Qa, n_max=k)
             L.dash_attn_active(self.Qa, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=self.idx, n_max=k, Wo=x.Wo,
                                Ua=self.Ua, S=self.S)
 
@@ -106,7 +122,7 @@ class ThresholdStack:
         self.layers = layers
         self.rank = tau_rank
         self.patience = patience
-        S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        _, S, Hq, Hkv, D, hidden = _shape_of(layers[0])
         dev, dt = layers[0].Q.device, layers[0].Q.dtype
         self.S = S
         self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
@@ -159,10 +175,11 @@ class DenseStack:
 
     def __init__(self, layers: list[LayerTensors]):
         self.layers = layers
-        S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        B, S, Hq, Hkv, D, hidden = _shape_of(layers[0])
         dev, dt = layers[0].Q.device, layers[0].Q.dtype
-        self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
-        self.U = torch.empty(S, hidden, device=dev, dtype=dt)
+        lead = (B,) if layers[0].Q.dim() == 4 else ()
+        self.O = torch.empty(*lead, S, Hq * D, device=dev, dtype=dt)
+        self.U = torch.empty(*lead, S, hidden, device=dev, dtype=dt)
 
     def run(self) -> None:
         for x in self.layers:

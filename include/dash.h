@@ -183,17 +183,28 @@ typedef struct {
 int dash_compact_many(void* ctx, const int32_t* idx, const int32_t* n_dev, int n_max,
                       const dash_gather* items, int count, void* stream);
 
+/* a4 for a batch of B samples of equal shape (same k per sample): for each
+ * b < B, r < k and j < count, items[j].Xa[b*k + r, :] =
+ * items[j].X[b*S_j + idx[b*k + r], :] with S_j = items[j].S rows per sample;
+ * idx holds each sample's local positions (as dash_select writes them for
+ * rows = B).  Other rules as dash_compact_many.  No workspace. */
+int dash_compact_batch(void* ctx, const int32_t* idx, int B, int k, const dash_gather* items, int count,
+                       void* stream);
+
 /* a5: post-halt attention ([P1] §3.1 step 4 and §5.1; [P2] 选择性停止机制).
- *   Qa [n, Hq, D] are the active queries (n = *n_dev or n_max, s->B == 1),
- *   q_pos [n] their ascending original positions.
- *   DASH_KV_ACTIVE: K, V are [n, Hkv, D], compacted at the same positions
+ *   Qa [B, n, Hq, D] are the active queries of B = s->B samples (n = n_max
+ *   per sample; n = *n_dev allowed for B == 1 only), q_pos [B, n] their
+ *   ascending original positions within the sample.
+ *   DASH_KV_ACTIVE: K, V are [B, n, Hkv, D], compacted at the same positions
  *     (pruned tokens left the KV cache); q_pos may be NULL.
- *   DASH_KV_ALL: K, V are the full [S, Hkv, D] of this layer (halted tokens
- *     keep their K/V); q_pos is required.
- *   Key r is visible to query i iff pos(r) <= q_pos[i].
- *   Oa [n, Hq*D].  If Wo != NULL: Ua = Oa · Wo^T [n, hidden], and score[i] =
- *   ||Ua_i||_2 when score != NULL.  Rows at or beyond n are left untouched.
- * Workspace: dash_workspace_size(DASH_OP_ATTN_ACTIVE, s, n_max). */
+ *   DASH_KV_ALL: K, V are the full [B, S, Hkv, D] of this layer (halted
+ *     tokens keep their K/V); q_pos is required.
+ *   Key r is visible to query i iff pos(r) <= q_pos[i] (same sample).
+ *   Oa [B, n, Hq*D].  If Wo != NULL: Ua = Oa · Wo^T [B, n, hidden], and
+ *   score[b*n + i] = ||Ua_{b,i}||_2 when score != NULL.  Rows at or beyond n
+ *   are left untouched.
+ * Workspace: dash_workspace_size(DASH_OP_ATTN_ACTIVE, s, n_max) (covers the
+ * B * n_max rows). */
 int dash_attn_active(void* ctx, const dash_shape* s, const void* Qa, const int32_t* q_pos,
                      const int32_t* n_dev, int n_max, const void* K, const void* V, int kv_mode,
                      void* Oa, const void* Wo, void* Ua, float* score,

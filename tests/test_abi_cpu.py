@@ -151,6 +151,19 @@ def test_score_validation(lib):
     assert f(None, None, L.DASH_BF16, 256, None, 0, None, None) == L.DASH_OK  # nothing to do
 
 
+def test_compact_batch_validation(lib):
+    f = lib.dash_compact_batch
+    G = L.DashGather
+    one = (G * 1)(G(FAKE, 10, 32, FAKE))
+    assert f(None, FAKE, 0, 4, one, 1, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, 2, -1, one, 1, None) == L.DASH_E_INVAL
+    assert f(None, FAKE, 2, 4, one, 0, None) == L.DASH_E_INVAL
+    bad = (G * 1)(G(FAKE, 10, 40, FAKE))
+    assert f(None, FAKE, 2, 4, bad, 1, None) == L.DASH_E_ALIGN
+    assert f(None, None, 2, 4, one, 1, None) == L.DASH_E_INVAL
+    assert f(None, None, 2, 0, one, 1, None) == L.DASH_OK  # nothing to do
+
+
 def test_attn_active_validation(lib):
     f = lib.dash_attn_active
     s = _shape()
@@ -158,7 +171,8 @@ def test_attn_active_validation(lib):
                                   Oa=FAKE, Wo=None, Ua=None, score=None, ws=None, wsb=0), **kw)
     call = lambda shape, a: f(None, ctypes.byref(shape), a["Qa"], a["q_pos"], a["n_dev"], a["n_max"], a["K"], a["V"],
                                a["mode"], a["Oa"], a["Wo"], a["Ua"], a["score"], a["ws"], a["wsb"], None)
-    assert call(_shape(B=2), args()) == L.DASH_E_SHAPE
+    assert call(_shape(B=2), args(n_dev=FAKE)) == L.DASH_E_SHAPE  # a device row count needs B == 1
+    assert "B == 1" in _last(lib)
     assert call(s, args(mode=5)) == L.DASH_E_INVAL
     assert call(s, args(n_max=65)) == L.DASH_E_INVAL
     assert call(s, args(mode=L.DASH_KV_ALL)) == L.DASH_E_INVAL

@@ -407,6 +407,96 @@ def test_attn_active(dash, dtype, mode, device_n):
     assert np.all(host(Oa)[n:] == 0) and np.all(host(Ua)[n:] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["active", "all"])
+def test_attn_active_batched(dash, dtype, mode):
+    """B = 3 samples in one call, each with its own kept positions; every sample
+    against the oracle (the samples' layers differ)."""
+    B, S, Hq, Hkv, D, hidden = 3, 640, 8, 2, (128 if dtype == "bf16" else 64), 256
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    xs = [_layer(S, Hq, Hkv, D, hidden, seed=11 + b, dtype=dtype) for b in range(B)]
+    Wo_h = xs[0]["Wo"]  # one weight for the batch
+    k = 250
+    idx = np.stack([np.sort(np.random.default_rng(b).choice(S, k, replace=False)) for b in range(B)]).astype(np.int32)
+    say("attn_active batched", dtype, mode)
+    Qa = dev_t(np.stack([x["Q"][idx[b]] for b, x in enumerate(xs)]), tdt)
+    if mode == "active":
+        K = dev_t(np.stack([x["K"][idx[b]] for b, x in enumerate(xs)]), tdt)
+        V = dev_t(np.stack([x["V"][idx[b]] for b, x in enumerate(xs)]), tdt)
+    else:
+        K = dev_t(np.stack([x["K"] for x in xs]), tdt)
+        V = dev_t(np.stack([x["V"] for x in xs]), tdt)
+    Wo = dev_t(Wo_h.T, tdt)
+    Oa = torch.zeros(B, k, Hq * D, device="cuda", dtype=tdt)
+    Ua = torch.zeros(B, k, hidden, device="cuda", dtype=tdt)
+    sc = torch.zeros(B, k, device="cuda", dtype=torch.float32)
+    dc = dash.DASH_BF16 if dtype == "bf16" else dash.DASH_F32
+    ws = dash.workspace(dash.DASH_OP_ATTN_ACTIVE, dash.make_shape(B, S, Hq, Hkv, D, hidden, dc), k)
+    km = dash.DASH_KV_ACTIVE if mode == "active" else dash.DASH_KV_ALL
+    dash.dash_attn_active(Qa, K, V, km, Oa, q_pos=torch.from_numpy(idx).cuda(), n_max=k, Wo=Wo, Ua=Ua, score=sc,
+                          ws=ws, S=S if mode == "all" else None)
+    torch.cuda.synchronize()
+    for b, x in enumerate(xs):
+        ref_O = oracle.attn_active(x["Q"], x["K"], x["V"], idx[b], mode)
+        ref_U = oracle.output_projection(ref_O, Wo_h)
+        ref_s = oracle.delta_attn(ref_U)
+        assert maxrel(host(Oa)[b], ref_O) <= tol
+        assert maxrel(host(Ua)[b], ref_U) <= tol
+        assert np.all(np.abs(host(sc)[b] - ref_s) <= TOL_SCORE * ref_s)
+
+
+@pytest.mark.parametrize("widths", [(7168, 1024, 1024), (48,), (16, 32)])
+def test_compact_batch_bit_exact(dash, widths):
+    """Per-sample gathers of B = 4 samples (local positions, with out-of-range entries skipped)."""
+    B, S, k = 4, 1000, 300
+    rng = np.random.default_rng(len(widths))
+    Xs = [rng.integers(0, 256, (B, S, w), dtype=np.uint8) for w in widths]
+    idx = np.stack([np.sort(rng.choice(S, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    idx[1, 7] = -3
+    idx[2, 100] = S
+    Xas = [torch.full((B, k, w), 0xEE, dtype=torch.uint8, device="cuda") for w in widths]
+    say("compact batch", widths)
+    dash.dash_compact_batch(torch.from_numpy(idx).cuda(), [(torch.from_numpy(X).cuda(), Xa) for X, Xa in zip(Xs, Xas)])
+    torch.cuda.synchronize()
+    for X, Xa in zip(Xs, Xas):
+        got = Xa.cpu().numpy()
+        for b in range(B):
+            ok = (idx[b] >= 0) & (idx[b] < S)
+            np.testing.assert_array_equal(got[b][ok], oracle.compact(X[b], idx[b][ok]))
+            assert np.all(got[b][~ok] == 0xEE)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_shot_step_batched(dash, dtype):
+    """B = 3 samples through the one-shot stack: halting layer at full length, top-k
+    per sample, one gather, post-halt layer; every sample against the oracle (the
+    selection bit-exact on the GPU's own scores, the post-halt layer teacher-forced)."""
+    from attention_delta_token_amd.stack import LayerTensors, OneShotStack
+    B = 3
+    w = WORKLOADS[0] if dtype == "f32" else WORKLOADS[1].scaled(S=768, hidden=512)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    hostl = [[layer_inputs(w, 20 + b, l) for b in range(B)] for l in range(2)]
+    Wo = [hostl[l][0]["Wo"] for l in range(2)]  # one weight per layer, shared by the batch
+    layers = [LayerTensors(*(dev_t(np.stack([h[n] for h in hostl[l]]), tdt) for n in ("Q", "K", "V")),
+                           dev_t(Wo[l].T, tdt)) for l in range(2)]
+    say("one-shot batched", dtype, w.S, w.k)
+    st = OneShotStack(layers, halt_layer=0, k=w.k)
+    st.run()
+    torch.cuda.synchronize()
+    for b in range(B):
+        x0, x1 = hostl[0][b], hostl[1][b]
+        _, U_ref, s_ref = oracle.attention_layer(x0["Q"], x0["K"], x0["V"], Wo[0])
+        assert maxrel(host(st.U)[b], U_ref) <= tol
+        score = host(st.score)[b]
+        assert np.all(np.abs(score - s_ref) <= TOL_SCORE * s_ref)
+        idx = st.idx.cpu().numpy()[b]
+        np.testing.assert_array_equal(idx, oracle.select_topk(score, w.k))
+        Oa = oracle.attn_active(x1["Q"], x1["K"], x1["V"], idx, "active")
+        assert maxrel(host(st.Ua)[b], oracle.output_projection(Oa, Wo[1])) <= tol
+
+
 def test_kv_all_at_halt_layer_equals_dense_rows(dash):
     """On the GPU: post-halt attention with all K/V at the halting layer equals the dense rows."""
     S, Hq, Hkv, D, hidden = 700, 8, 2, 128, 256
