@@ -289,6 +289,41 @@ def run_one_shot(get_layer, L: int, halt_layer: int, k: int, kv_mode: str = "act
     return out
 
 
+def run_multi_shot(get_layer, L: int, schedule, kv_mode: str = "active"):
+    """Halting decisions at several layers — the multi-round alternative to the
+    single decision that [P1] §2.3 weighs against it, and the pruning at several
+    key layers with growing ratios of [P1] §5.3.
+
+    schedule = [(l_1, k_1), (l_2, k_2), ...] with l_1 < l_2 < ... and
+    k_1 >= k_2 >= ...  Layers 0..l_1 run at full length and the score of layer
+    l_1 keeps k_1 positions (select_topk).  Each later decision layer l_i is a
+    post-halt layer: among its active rows it keeps the k_i with the largest
+    score (same order as select_topk over those rows), and the layers after it
+    run on that subset of positions.  With kv_mode "active" every decision also
+    prunes the keys and values.
+
+    Returns per-layer U and the position set chosen at each decision."""
+    decisions = dict(schedule)
+    layers = [l for l, _ in schedule]
+    if layers != sorted(set(layers)) or any(b[1] > a[1] for a, b in zip(schedule, schedule[1:])):
+        raise ValueError("decision layers must increase and kept counts must not grow")
+    idx = None
+    out = {"U": [], "idx": []}
+    for l in range(L):
+        x = get_layer(l)
+        if idx is None:
+            _, U, s = attention_layer(x["Q"], x["K"], x["V"], x["Wo"], want_score=(l in decisions))
+        else:
+            U = output_projection(attn_active(x["Q"], x["K"], x["V"], idx, kv_mode), x["Wo"])
+            s = delta_attn(U)
+        if l in decisions:
+            keep = select_topk(s, decisions[l])
+            idx = keep.astype(np.int32) if idx is None else idx[keep]
+            out["idx"].append(idx)
+        out["U"].append(U)
+    return out
+
+
 def run_threshold(get_layer, L: int, S: int, tau_rank: int, patience: int = 2, kv_mode: str = "all"):
     """Selective-halting policy, [P2] "层间更新动态监测" / "选择性停止机制": layer 0
     runs at full length and fixes τ as the tau_rank-th smallest layer-0 score;

@@ -421,6 +421,58 @@ def test_one_shot_stack_selection_from_halt_layer():
     assert res["U"][2].shape == (20, w.hidden)
 
 
+def test_multi_shot_single_decision_is_one_shot():
+    w = WORKLOADS[0].scaled(S=40, layers=3, halt_layer=1)
+    get = lambda l: layer_inputs(w, 2, l)
+    a = oracle.run_multi_shot(get, 3, [(1, 15)])
+    b = oracle.run_one_shot(get, 3, 1, k=15)
+    np.testing.assert_array_equal(a["idx"][0], b["idx"])
+    np.testing.assert_allclose(a["U"][2], b["U"][2], rtol=0, atol=0)
+
+
+def test_multi_shot_second_decision_brute_force():
+    """The second decision, recomputed with explicit softmax attention over the
+    first decision's rows (keys pruned to them), picks the top scores by the
+    pairwise-rank rule."""
+    w = WORKLOADS[0].scaled(S=48, Hq=2, Hkv=1, D=8, hidden=16, layers=4, halt_layer=0)
+    get = lambda l: layer_inputs(w, 3, l)
+    res = oracle.run_multi_shot(get, 4, [(0, 30), (2, 12)])
+    idx1, idx2 = res["idx"]
+    assert idx1.shape == (30,) and idx2.shape == (12,)
+    assert set(idx2) <= set(idx1) and np.all(np.diff(idx2) > 0)
+    x = get(2)
+    Q, K, V = (x[n].astype(np.float64) for n in ("Q", "K", "V"))
+    D = Q.shape[-1]
+    rows = []
+    for i, p in enumerate(idx1):
+        heads = []
+        for h in range(2):
+            keys = idx1[idx1 <= p]
+            sc = np.array([Q[p, h] @ K[j, 0] for j in keys]) / math.sqrt(D)
+            pr = np.exp(sc - sc.max())
+            pr /= pr.sum()
+            heads.append(sum(pr[t] * V[j, 0] for t, j in enumerate(keys)))
+        rows.append(np.concatenate(heads))
+    U = np.array(rows) @ x["Wo"].astype(np.float64)
+    s2 = np.sqrt((U * U).sum(1))
+    np.testing.assert_array_equal(idx2, idx1[brute_topk(s2, 12)])
+    # layer 3 runs on idx2 only
+    assert res["U"][3].shape == (12, w.hidden)
+
+
+def test_multi_shot_keep_all_is_dense():
+    w = WORKLOADS[0].scaled(S=32, layers=4, halt_layer=0)
+    get = lambda l: layer_inputs(w, 4, l)
+    res = oracle.run_multi_shot(get, 4, [(0, 32), (2, 32)])
+    x = get(3)
+    _, U, _ = oracle.attention_layer(x["Q"], x["K"], x["V"], x["Wo"])
+    np.testing.assert_allclose(res["U"][3], U, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.run_multi_shot(get, 4, [(2, 10), (1, 5)])
+    with pytest.raises(ValueError):
+        oracle.run_multi_shot(get, 4, [(0, 10), (2, 20)])
+
+
 def test_threshold_stack_min_tau_never_halts():
     w = WORKLOADS[3].scaled(S=32, Hq=4, Hkv=2, D=8, hidden=32, layers=4, dtype="f32")
     get = lambda l: layer_inputs(w, 0, l)
