@@ -112,6 +112,68 @@ class OneShotStack:
                 self.post_layer(l)
 
 
+class MultiShotStack:
+    """Halting decisions at several layers (one sample): schedule
+    [(l_1, k_1), (l_2, k_2), ...] with increasing layers and non-increasing
+    counts.  Layers 0..l_1 run at full length and layer l_1's scores keep k_1
+    positions; each later decision layer scores its active rows and keeps the
+    k_i best of them (top-k over the active rows, mapped to positions); the
+    layers after a decision run on its set.  kv_mode active prunes the keys
+    and values at every decision, kv_mode all keeps them."""
+
+    def __init__(self, layers: list[LayerTensors], schedule, kv_mode: int = L.DASH_KV_ACTIVE):
+        self.layers = layers
+        self.schedule = list(schedule)
+        self.kv_mode = kv_mode
+        lays = [l for l, _ in self.schedule]
+        if lays != sorted(set(lays)) or any(b[1] > a[1] for a, b in zip(self.schedule, self.schedule[1:])):
+            raise ValueError("decision layers must increase and kept counts must not grow")
+        B, S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        if B != 1:
+            raise ValueError("multi-shot stacks take one sample")
+        dev, dt = layers[0].Q.device, layers[0].Q.dtype
+        self.S = S
+        k1 = max(self.schedule[0][1], 1)
+        self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
+        self.U = torch.empty(S, hidden, device=dev, dtype=dt)
+        self.score = torch.empty(S, device=dev, dtype=torch.float32)
+        self.pos = [torch.empty(max(k, 1), device=dev, dtype=torch.int32) for _, k in self.schedule]
+        self.Qa = torch.empty(k1, Hq, D, device=dev, dtype=dt)
+        self.Ka = torch.empty(k1, Hkv, D, device=dev, dtype=dt)
+        self.Va = torch.empty(k1, Hkv, D, device=dev, dtype=dt)
+        self.Oa = torch.empty(k1, Hq * D, device=dev, dtype=dt)
+        self.Ua = torch.empty(k1, hidden, device=dev, dtype=dt)
+        dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
+        self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
+        self.record = []  # (layer, position set, scores or None) per decision, device tensors
+        self.keep_scores = False  # also copy each decision's scores (tests, measurement)
+
+    def run(self) -> None:
+        decisions = dict(self.schedule)
+        self.record = []
+        cur, n, d = None, self.S, 0
+        for l, x in enumerate(self.layers):
+            decide = l in decisions
+            if cur is None:
+                L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.score if decide else None, self.ws)
+            elif n > 0:
+                if self.kv_mode == L.DASH_KV_ACTIVE:
+                    L.dash_compact_many(cur, [(x.Q, self.Qa), (x.K, self.Ka), (x.V, self.Va)], n_max=n)
+                    L.dash_attn_active(self.Qa[:n], self.Ka[:n], self.Va[:n], L.DASH_KV_ACTIVE, self.Oa, n_max=n,
+                                       Wo=x.Wo, Ua=self.Ua, score=self.score if decide else None, ws=self.ws)
+                else:
+                    L.dash_compact(cur, x.Q, self.Qa, n_max=n)
+                    L.dash_attn_active(self.Qa[:n], x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=cur, n_max=n, Wo=x.Wo,
+                                       Ua=self.Ua, score=self.score if decide else None, ws=self.ws, S=self.S)
+            if decide:
+                k = decisions[l]
+                nxt = self.pos[d]
+                if k > 0:
+                    L.dash_select(self.score, nxt, mode=L.DASH_SEL_TOPK, k=k, n_max=n, pos=cur)
+                self.record.append((l, nxt, self.score[:n].clone() if self.keep_scores else None))
+                cur, n, d = nxt, k, d + 1
+
+
 class ThresholdStack:
     """Layer 0 full length fixes tau (rank-th smallest score); every layer then
     updates the counters and compacts the surviving queries; keys and values

@@ -565,6 +565,39 @@ def test_tiny_fp32_one_shot_step_forced(dash):
     assert maxrel(host(st.Ua), Ua) <= TOL_F32
 
 
+@pytest.mark.parametrize("dtype,mode", [("f32", "active"), ("f32", "all"), ("bf16", "active")])
+def test_multi_shot_stack(dash, dtype, mode):
+    """Two halting decisions (layers 0 and 2 of 4): each decision bit-exact against
+    the oracle's top-k of the GPU's own scores, the scores and the last layer
+    against the oracle teacher-forced on the GPU's position sets."""
+    from attention_delta_token_amd.stack import MultiShotStack
+    w = WORKLOADS[0].scaled(layers=4) if dtype == "f32" else WORKLOADS[1].scaled(S=1024, hidden=512, layers=4)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    k1, k2 = (3 * w.S) // 4, (3 * w.S) // 10
+    hostl, devl = _stack_inputs(w, 0, dtype)
+    say("multi-shot", dtype, mode, w.S, k1, k2)
+    st = MultiShotStack(devl, [(0, k1), (2, k2)], kv_mode=dash.DASH_KV_ACTIVE if mode == "active" else dash.DASH_KV_ALL)
+    st.keep_scores = True
+    st.run()
+    torch.cuda.synchronize()
+    (l1, p1, s0), (l2, p2, s2) = st.record
+    idx1, idx2 = p1.cpu().numpy(), p2.cpu().numpy()
+    s0, s2 = host(s0), host(s2)
+    x0 = hostl[0]
+    _, _, s0_ref = oracle.attention_layer(x0["Q"], x0["K"], x0["V"], x0["Wo"])
+    assert np.all(np.abs(s0 - s0_ref) <= TOL_SCORE * s0_ref)
+    np.testing.assert_array_equal(idx1, oracle.select_topk(s0, k1))
+    x2 = hostl[2]
+    s2_ref = oracle.delta_attn(oracle.output_projection(oracle.attn_active(x2["Q"], x2["K"], x2["V"], idx1, mode),
+                                                        x2["Wo"]))
+    assert np.all(np.abs(s2 - s2_ref) <= TOL_SCORE * s2_ref)
+    np.testing.assert_array_equal(idx2, idx1[oracle.select_topk(s2, k2)])
+    x3 = hostl[3]
+    U3 = oracle.output_projection(oracle.attn_active(x3["Q"], x3["K"], x3["V"], idx2, mode), x3["Wo"])
+    assert maxrel(host(st.Ua)[:k2], U3) <= tol
+
+
 @pytest.mark.timeout(900)
 def test_qwen_s8192_one_shot_step(dash):
     """S=8192, 28/4 heads, D=128, hidden 3584, bf16: the full halt layer against the oracle,
