@@ -25,7 +25,8 @@ DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE = 0, 1, 2
 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
             "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
-            "dash_attn_active", "dash_score",
+            "dash_attn_active", "dash_score", "dash_attn_layer_varlen", "dash_select_ragged",
+            "dash_attn_active_varlen",
             "dash_trace_start", "dash_trace_stop", "dash_trace_read")
 TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact", "score")
 
@@ -90,6 +91,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]
     lib.dash_attn_active.restype = c_int
+    lib.dash_attn_layer_varlen.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_int, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                           c_void_p]
+    lib.dash_attn_layer_varlen.restype = c_int
+    lib.dash_select_ragged.argtypes = [c_void_p, POINTER(DashSel), c_void_p, c_int, c_int, c_void_p, c_void_p,
+                                       c_int, c_int, c_void_p, c_void_p]
+    lib.dash_select_ragged.restype = c_int
+    lib.dash_attn_active_varlen.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_int,
+                                            c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dash_attn_active_varlen.restype = c_int
     lib.dash_trace_start.argtypes = [c_int]
     lib.dash_trace_start.restype = c_int
     lib.dash_trace_stop.argtypes = []
@@ -246,6 +258,38 @@ def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: 
     _check(load().dash_attn_active(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(n_dev), n_max, _ptr(K),
                                    _ptr(V), kv_mode, _ptr(Oa), _ptr(Wo), _ptr(Ua), _ptr(score), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dash_attn_layer_varlen(Q, K, V, Wo, O, U, cu_seqlens, max_len: int, score=None, ws=None, stream=None) -> None:
+    """Packed batch: Q [T, Hq, D], K, V [T, Hkv, D], cu_seqlens [B+1] (device int32), max_len = longest sample."""
+    T, Hq, D = Q.shape
+    B = cu_seqlens.shape[0] - 1
+    shape = make_shape(B, max_len, Hq, K.shape[1], D, Wo.shape[0], _dtype_code(Q))
+    _check(load().dash_attn_layer_varlen(None, ctypes.byref(shape), _ptr(cu_seqlens), T, _ptr(Q), _ptr(K), _ptr(V),
+                                         _ptr(Wo), _ptr(O), _ptr(U), _ptr(score), _ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dash_select_ragged(score, idx, cu_n, cu_k, max_n: int, keep_first: int = 0, keep_last: int = 0,
+                       stream=None) -> None:
+    """Per-sample top-k of a packed score vector; idx receives packed row indices."""
+    sel = DashSel(DASH_SEL_TOPK, 0, 0, None, 2, None, keep_first, keep_last)
+    B = cu_n.shape[0] - 1
+    _check(load().dash_select_ragged(None, ctypes.byref(sel), _ptr(score), score.shape[0], B, _ptr(cu_n), _ptr(cu_k),
+                                     max_n, idx.shape[0], _ptr(idx), _stream(stream)))
+
+
+def dash_attn_active_varlen(Qa, K, V, kv_mode: int, Oa, cu_q, max_rows: int, q_pos=None, cu_kv=None, Wo=None,
+                            Ua=None, score=None, ws=None, stream=None) -> None:
+    """Packed post-halt attention: Qa [n_total, Hq, D]; K, V [n_total or kv_total, Hkv, D]."""
+    n_total, Hq, D = Qa.shape
+    B = cu_q.shape[0] - 1
+    hidden = Wo.shape[0] if Wo is not None else Hq * D
+    shape = make_shape(B, max_rows, Hq, K.shape[1], D, hidden, _dtype_code(Qa))
+    _check(load().dash_attn_active_varlen(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(cu_q), n_total,
+                                          _ptr(K), _ptr(V), kv_mode, _ptr(cu_kv), K.shape[0], _ptr(Oa), _ptr(Wo),
+                                          _ptr(Ua), _ptr(score), _ptr(ws),
+                                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def trace_start(capacity: int) -> None:

@@ -141,14 +141,15 @@ __global__ __launch_bounds__(kAttnThreads, 2)
 void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_dev, int n_q_max,
-                          int n_kv, int Hq, int Hkv, float c_log2, int64_t q_bs, int64_t kv_bs, int64_t o_bs,
-                          int qp_bs) {
+                          int n_kv, int Hq, int Hkv, float c_log2, AttnBatch bt) {
   using C = AttnCfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kTotal];
 
-  int n_q = n_dev ? *n_dev : n_q_max;
-  if (n_q > n_q_max) n_q = n_q_max;
-  if (n_kv < 0) n_kv = n_q;  // keys compacted alongside the queries
+  const int64_t b = blockIdx.y;
+  const int q_ld = Hq * D;
+  const int kv_ld = Hkv * D;
+  int n_q, pos_base;
+  bt.locate(b, n_dev, n_q_max, n_kv, q_ld, kv_ld, Q, O, q_pos, K, V, n_q, pos_base);
   const int n_qt = (n_q_max + kBQ - 1) / kBQ;
   const int g = Hq / Hkv;
   int qt, h;
@@ -156,14 +157,8 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int q0 = qt * kBQ;
   if (q0 >= n_q) return;
   const int kvh = h / g;
-  const int64_t b = blockIdx.y;
-  Q += b * q_bs;
-  O += b * o_bs;
-  if (q_pos) q_pos += b * qp_bs;
-  K += b * kv_bs + static_cast<int64_t>(kvh) * D;
-  V += b * kv_bs + static_cast<int64_t>(kvh) * D;
-  const int q_ld = Hq * D;
-  const int kv_ld = Hkv * D;
+  K += static_cast<int64_t>(kvh) * D;
+  V += static_cast<int64_t>(kvh) * D;
   const uint32_t row_bytes = static_cast<uint32_t>(kv_ld) * 2u;
   // bytes from this kv-head's first element to the end of the last key row;
   // loads past it (rows beyond the key count) return zeros
@@ -179,13 +174,13 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = min(qrow, n_q - 1);
-  const int my_pos = q_pos ? q_pos[qrow_c] : qrow_c;
+  const int my_pos = q_pos ? q_pos[qrow_c] - pos_base : qrow_c;
   const int w_first = min(q0 + wave * 32, n_q - 1);
   const int w_last = min(q0 + wave * 32 + 31, n_q - 1);
-  const int wave_pmin = q_pos ? q_pos[w_first] : w_first;
-  const int wave_pmax = q_pos ? q_pos[w_last] : w_last;
+  const int wave_pmin = q_pos ? q_pos[w_first] - pos_base : w_first;
+  const int wave_pmax = q_pos ? q_pos[w_last] - pos_base : w_last;
   const int b_last = min(q0 + kBQ - 1, n_q - 1);
-  const int block_pmax = q_pos ? q_pos[b_last] : b_last;
+  const int block_pmax = q_pos ? q_pos[b_last] - pos_base : b_last;
   const int kv_end = min(n_kv, block_pmax + 1);
   const int n_tiles = (kv_end + kBKV - 1) / kBKV;
   // Tiles this wave computes (keys k0 <= wave_pmax) and the first one that
@@ -428,28 +423,24 @@ __global__ __launch_bounds__(64)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                          float* __restrict__ O, const int32_t* __restrict__ q_pos,
                          const int32_t* __restrict__ n_dev, int n_q_max, int n_kv, int Hq, int Hkv, float scale,
-                         int64_t q_bs, int64_t kv_bs, int64_t o_bs, int qp_bs) {
+                         AttnBatch bt) {
   __shared__ float ks[64][D];
   __shared__ float vs[64][D];
-  int n_q = n_dev ? *n_dev : n_q_max;
-  if (n_q > n_q_max) n_q = n_q_max;
-  if (n_kv < 0) n_kv = n_q;  // keys compacted alongside the queries
+  const int64_t b = blockIdx.z;
+  const int q_ld = Hq * D, kv_ld = Hkv * D;
+  int n_q, pos_base;
+  bt.locate(b, n_dev, n_q_max, n_kv, q_ld, kv_ld, Q, O, q_pos, K, V, n_q, pos_base);
   const int q0 = blockIdx.x * 64;
   if (q0 >= n_q) return;
   const int h = blockIdx.y;
   const int kvh = h / (Hq / Hkv);
-  const int64_t b = blockIdx.z;
-  Q += b * q_bs;
-  O += b * o_bs;
-  if (q_pos) q_pos += b * qp_bs;
-  K += b * kv_bs + static_cast<int64_t>(kvh) * D;
-  V += b * kv_bs + static_cast<int64_t>(kvh) * D;
-  const int q_ld = Hq * D, kv_ld = Hkv * D;
+  K += static_cast<int64_t>(kvh) * D;
+  V += static_cast<int64_t>(kvh) * D;
   const int qi = q0 + threadIdx.x;
   const int qc = min(qi, n_q - 1);
-  const int my_pos = q_pos ? q_pos[qc] : qc;
+  const int my_pos = q_pos ? q_pos[qc] - pos_base : qc;
   const int last = min(q0 + 63, n_q - 1);
-  const int pmax = q_pos ? q_pos[last] : last;
+  const int pmax = q_pos ? q_pos[last] - pos_base : last;
   const int kv_end = min(n_kv, pmax + 1);
   float q[D], acc[D];
 #pragma unroll
@@ -490,7 +481,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 
 hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* K, const void* V, void* O,
                             const int32_t* q_pos, const int32_t* n_dev, int n_q_max, int n_kv, int Hq, int Hkv,
-                            int64_t q_bs, int64_t kv_bs, int64_t o_bs, int qp_bs, hipStream_t stream) {
+                            const AttnBatch& bt, hipStream_t stream) {
   if (n_q_max <= 0 || B <= 0) return hipSuccess;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   if (dtype == 1) {
@@ -503,10 +494,10 @@ hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* 
     auto o = static_cast<uint16_t*>(O);
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
-                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs, qp_bs);
+                         n_q_max, n_kv, Hq, Hkv, c, bt);
     else if (D == 64)
       hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
-                         n_q_max, n_kv, Hq, Hkv, c, q_bs, kv_bs, o_bs, qp_bs);
+                         n_q_max, n_kv, Hq, Hkv, c, bt);
     else
       return hipErrorInvalidValue;
   } else {
@@ -517,13 +508,13 @@ hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* 
     auto o = static_cast<float*>(O);
     if (D == 128)
       hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
-                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs, qp_bs);
+                         n_kv, Hq, Hkv, scale, bt);
     else if (D == 64)
       hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
-                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs, qp_bs);
+                         n_kv, Hq, Hkv, scale, bt);
     else if (D == 32)
       hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, grid, dim3(64), 0, stream, q, k, v, o, q_pos, n_dev, n_q_max,
-                         n_kv, Hq, Hkv, scale, q_bs, kv_bs, o_bs, qp_bs);
+                         n_kv, Hq, Hkv, scale, bt);
     else
       return hipErrorInvalidValue;
   }

@@ -223,8 +223,12 @@ int dash_attn_layer(void* /*ctx*/, const dash_shape* s, const void* Q, const voi
     const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
     const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
     int tr = trace_open(DASH_TR_ATTN_LAYER, st);
+    dash::AttnBatch bt;
+    bt.q_bs = s->S * qd;
+    bt.kv_bs = s->S * kvd;
+    bt.o_bs = s->S * qd;
     hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Q, K, V, O, nullptr, nullptr, s->S, s->S, s->Hq,
-                                          s->Hkv, s->S * qd, s->S * kvd, s->S * qd, 0, st);
+                                          s->Hkv, bt, st);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     tr = trace_open(DASH_TR_PROJ_LAYER, st);
@@ -317,6 +321,129 @@ int dash_compact(void* /*ctx*/, const int32_t* idx, const int32_t* n_dev, int n_
     hipError_t e = dash::launch_compact(idx, n_dev, n_max, X, S, row_bytes, Xa, st);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "compaction launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_attn_layer_varlen(void* /*ctx*/, const dash_shape* s, const int32_t* cu_seqlens, int total,
+                           const void* Q, const void* K, const void* V, const void* Wo, void* O, void* U,
+                           float* score, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    if (total < 0 || static_cast<int64_t>(total) > static_cast<int64_t>(s->B) * s->S)
+      return fail(DASH_E_SHAPE, "total %d outside [0, B * S]", total);
+    if (total == 0) return DASH_OK;
+    rc = check_ptrs({{Q, "Q"}, {K, "K"}, {V, "V"}, {Wo, "Wo"}, {O, "O"}, {U, "U"}});
+    if (rc) return rc;
+    if (!cu_seqlens) return fail(DASH_E_INVAL, "cu_seqlens is NULL");
+    if (score) {
+      if (!aligned16(score)) return fail(DASH_E_ALIGN, "score is not 16-byte aligned");
+      const size_t need = score_ws_bytes(s, total);
+      if (!ws || ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+      if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
+    dash::AttnBatch bt;
+    bt.cu_q = cu_seqlens;
+    bt.cu_kv = cu_seqlens;
+    bt.q_total = total;
+    bt.kv_total = total;
+    int tr = trace_open(DASH_TR_ATTN_LAYER, st);
+    hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Q, K, V, O, nullptr, nullptr, s->S, 0, s->Hq,
+                                          s->Hkv, bt, st);
+    trace_close(tr, st);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    tr = trace_open(DASH_TR_PROJ_LAYER, st);
+    e = dash::launch_wo_gemm(s->dtype, O, Wo, U, score, static_cast<float*>(ws), nullptr, total, s->hidden,
+                             static_cast<int>(qd), st);
+    trace_close(tr, st);
+    if (e != hipSuccess) return hip_fail(e, "projection launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_attn_active_varlen(void* /*ctx*/, const dash_shape* s, const void* Qa, const int32_t* q_pos,
+                            const int32_t* cu_q, int n_total, const void* K, const void* V, int kv_mode,
+                            const int32_t* cu_kv, int kv_total, void* Oa, const void* Wo, void* Ua, float* score,
+                            void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    if (kv_mode != DASH_KV_ACTIVE && kv_mode != DASH_KV_ALL) return fail(DASH_E_INVAL, "kv_mode %d unknown", kv_mode);
+    if (n_total < 0 || static_cast<int64_t>(n_total) > static_cast<int64_t>(s->B) * s->S)
+      return fail(DASH_E_SHAPE, "n_total %d outside [0, B * S]", n_total);
+    if (n_total == 0) return DASH_OK;
+    rc = check_ptrs({{Qa, "Qa"}, {K, "K"}, {V, "V"}, {Oa, "Oa"}});
+    if (rc) return rc;
+    if (!cu_q) return fail(DASH_E_INVAL, "cu_q is NULL");
+    if (kv_mode == DASH_KV_ALL && (!q_pos || !cu_kv)) return fail(DASH_E_INVAL, "kv_mode ALL needs q_pos and cu_kv");
+    if (kv_mode == DASH_KV_ALL && (kv_total < 1 || kv_total > (1 << 26)))
+      return fail(DASH_E_SHAPE, "kv_total %d outside [1, 2^26]", kv_total);
+    if (kv_mode == DASH_KV_ACTIVE && cu_kv && cu_kv != cu_q)
+      return fail(DASH_E_INVAL, "kv_mode ACTIVE keeps the keys with the queries (cu_kv must be NULL or cu_q)");
+    if (Wo) {
+      rc = check_ptrs({{Wo, "Wo"}, {Ua, "Ua"}});
+      if (rc) return rc;
+      if (score) {
+        if (!aligned16(score)) return fail(DASH_E_ALIGN, "score is not 16-byte aligned");
+        const size_t need = score_ws_bytes(s, n_total);
+        if (!ws || ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+        if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
+      }
+    } else if (Ua || score) {
+      return fail(DASH_E_INVAL, "Ua / score need Wo");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
+    dash::AttnBatch bt;
+    bt.cu_q = cu_q;
+    bt.cu_kv = kv_mode == DASH_KV_ACTIVE ? cu_q : cu_kv;
+    bt.q_total = n_total;
+    bt.kv_total = kv_mode == DASH_KV_ACTIVE ? n_total : kv_total;
+    const int n_kv = kv_mode == DASH_KV_ACTIVE ? -1 : 0;  // ACTIVE: keys follow the queries; ALL: from cu_kv
+    const int32_t* qp = kv_mode == DASH_KV_ALL ? q_pos : nullptr;
+    int tr = trace_open(DASH_TR_ATTN_ACTIVE, st);
+    hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Qa, K, V, Oa, qp, nullptr, s->S, n_kv, s->Hq,
+                                          s->Hkv, bt, st);
+    trace_close(tr, st);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (Wo) {
+      tr = trace_open(DASH_TR_PROJ_ACTIVE, st);
+      e = dash::launch_wo_gemm(s->dtype, Oa, Wo, Ua, score, static_cast<float*>(ws), nullptr, n_total, s->hidden,
+                               static_cast<int>(qd), st);
+      trace_close(tr, st);
+      if (e != hipSuccess) return hip_fail(e, "projection launch");
+    }
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_select_ragged(void* /*ctx*/, const dash_sel* p, const float* score, int n_total, int B, const int32_t* cu_n,
+                       const int32_t* cu_k, int max_n, int k_total, int32_t* idx, void* stream) {
+  try {
+    if (!p) return fail(DASH_E_INVAL, "selection parameters are NULL");
+    if (p->mode != DASH_SEL_TOPK) return fail(DASH_E_INVAL, "ragged selection supports top-k only");
+    if (B < 1 || B > (1 << 20)) return fail(DASH_E_INVAL, "B %d out of range", B);
+    if (max_n < 0 || max_n > (1 << 30)) return fail(DASH_E_INVAL, "max_n %d out of range", max_n);
+    if (k_total < 0 || n_total < 0) return fail(DASH_E_INVAL, "n_total and k_total must be >= 0");
+    if (max_n > n_total) return fail(DASH_E_INVAL, "max_n %d exceeds n_total %d", max_n, n_total);
+    if (p->keep_first < 0 || p->keep_last < 0) return fail(DASH_E_INVAL, "forced counts must be >= 0");
+    if (k_total == 0 || max_n == 0) return DASH_OK;
+    if (!score || !idx || !cu_n || !cu_k) return fail(DASH_E_INVAL, "score, idx, cu_n and cu_k are required");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int tr = trace_open(DASH_TR_SELECT, st);
+    hipError_t e =
+        dash::launch_topk_ragged(score, n_total, B, cu_n, cu_k, max_n, k_total, p->keep_first, p->keep_last, idx, st);
+    trace_close(tr, st);
+    if (e != hipSuccess) return hip_fail(e, "selection launch");
     return DASH_OK;
   } catch (...) {
     return fail(DASH_E_INVAL, "unexpected host exception");
@@ -439,8 +566,13 @@ int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const i
     const int32_t* qp = kv_mode == DASH_KV_ALL ? q_pos : nullptr;
     const int64_t kv_rows = kv_mode == DASH_KV_ACTIVE ? n_max : s->S;  // per sample
     int tr = trace_open(DASH_TR_ATTN_ACTIVE, st);
+    dash::AttnBatch bt;
+    bt.q_bs = n_max * qd;
+    bt.kv_bs = kv_rows * kvd;
+    bt.o_bs = n_max * qd;
+    bt.qp_bs = n_max;
     hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Qa, K, V, Oa, qp, n_dev, n_max, n_kv, s->Hq,
-                                          s->Hkv, n_max * qd, kv_rows * kvd, n_max * qd, n_max, st);
+                                          s->Hkv, bt, st);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (Wo) {

@@ -7,9 +7,55 @@
 namespace dash {
 
 // dtype: 0 = fp32, 1 = bf16.
+// Where sample b's rows live.  Fixed batch (cu_q == nullptr): sample b starts
+// b * q_bs / kv_bs / o_bs elements in, its query positions b * qp_bs entries
+// in, and it has *n_dev (or n_q_max) queries.  Ragged (packed) batch: sample
+// b's query rows are cu_q[b] .. cu_q[b+1]-1 and its key rows cu_kv[b] ..
+// cu_kv[b+1]-1 of the packed tensors; query positions index the packed key
+// rows, so a query's position within its sample is q_pos - cu_kv[b].  In both
+// cases n_kv < 0 makes the key count follow the query count (keys compacted
+// with the queries); a ragged batch otherwise takes it from cu_kv.
+struct AttnBatch {
+  int64_t q_bs = 0, kv_bs = 0, o_bs = 0;
+  int qp_bs = 0;
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_kv = nullptr;
+  int q_total = 0, kv_total = 0;  // ragged: packed query / key rows; every sample is clamped into them
+
+  // Moves the (restrict-qualified) tensor pointers to sample b and sets its
+  // query count, key count and position base.
+  template <class PQ, class PO, class PP, class PK>
+  __device__ __forceinline__ void locate(int64_t b, const int32_t* n_dev, int n_q_max, int& n_kv, int q_ld,
+                                         int kv_ld, PQ& Q, PO& O, PP& q_pos, PK& K, PK& V, int& n_q,
+                                         int& pos_base) const {
+    if (cu_q) {
+      const int q_row0 = min(max(cu_q[b], 0), q_total);
+      const int kv_row0 = min(max(cu_kv[b], 0), kv_total);
+      n_q = max(0, min(min(cu_q[b + 1], q_total) - q_row0, n_q_max));
+      n_kv = n_kv < 0 ? n_q : max(0, min(cu_kv[b + 1], kv_total) - kv_row0);
+      pos_base = kv_row0;
+      Q += static_cast<int64_t>(q_row0) * q_ld;
+      O += static_cast<int64_t>(q_row0) * q_ld;
+      if (q_pos) q_pos += q_row0;
+      K += static_cast<int64_t>(kv_row0) * kv_ld;
+      V += static_cast<int64_t>(kv_row0) * kv_ld;
+    } else {
+      n_q = n_dev ? *n_dev : n_q_max;
+      if (n_q > n_q_max) n_q = n_q_max;
+      if (n_kv < 0) n_kv = n_q;
+      pos_base = 0;
+      Q += b * q_bs;
+      O += b * o_bs;
+      if (q_pos) q_pos += b * qp_bs;
+      K += b * kv_bs;
+      V += b * kv_bs;
+    }
+  }
+};
+
 hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* K, const void* V, void* O,
                             const int32_t* q_pos, const int32_t* n_dev, int n_q_max, int n_kv, int Hq, int Hkv,
-                            int64_t q_bs, int64_t kv_bs, int64_t o_bs, int qp_bs, hipStream_t stream);
+                            const AttnBatch& bt, hipStream_t stream);
 
 int wo_gemm_parts(int dtype, int N);
 hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, float* score, float* part,
@@ -17,6 +63,12 @@ hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, floa
 
 hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
                        const int32_t* pos, int32_t* idx, hipStream_t stream);
+// Ragged top-k: sample b's scores are cu_n[b] .. cu_n[b+1]-1 of `score`
+// (n_total entries); it keeps cu_k[b+1] - cu_k[b] of them, written as packed
+// row indices to idx[cu_k[b] ..] (capacity k_cap); max_n bounds every
+// sample's length.
+hipError_t launch_topk_ragged(const float* score, int n_total, int B, const int32_t* cu_n, const int32_t* cu_k,
+                              int max_n, int k_cap, int keep_first, int keep_last, int32_t* idx, hipStream_t stream);
 hipError_t launch_order_stat(const float* score, const int32_t* n_dev, int n_max, int rank, float* tau_out,
                              hipStream_t stream);
 hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,

@@ -269,16 +269,47 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
   }
 }
 
+// Row b of the selection.  Fixed rows: n_row scores at b * n_row, k_total
+// outputs at b * k_total, positions 0..n_row-1.  Ragged rows (packed samples):
+// scores cu_n[b] .. cu_n[b+1]-1, outputs cu_k[b] .. cu_k[b+1]-1, and the
+// written positions are packed row indices (cu_n[b] + local position).  A
+// ragged row asks for at most its length and at least its forced ends; counts
+// outside that are clamped (the unused outputs are left untouched).
+struct SelRow {
+  int64_t in_off, out_off;
+  int n, k, f, l, base;
+  __device__ __forceinline__ SelRow(int64_t b, int n_row, int k_total, int f_, int l_, const int32_t* cu_n,
+                                    const int32_t* cu_k) {
+    if (cu_n) {  // n_row / k_total are then the packed score count / output capacity; rows are clamped into them
+      in_off = min(max(cu_n[b], 0), n_row);
+      n = max(0, min(cu_n[b + 1], n_row) - static_cast<int>(in_off));
+      out_off = min(max(cu_k[b], 0), k_total);
+      k = max(0, min(min(cu_k[b + 1] - cu_k[b], n), k_total - static_cast<int>(out_off)));
+      f = min(f_, k);
+      l = min(l_, k - f);
+      base = static_cast<int>(in_off);
+    } else {
+      in_off = b * n_row;
+      n = n_row;
+      out_off = b * k_total;
+      k = k_total;
+      f = f_;
+      l = l_;
+      base = 0;
+    }
+  }
+};
+
 // Forced retention: the first f and last l positions of a row of n_row
 // scores are written to the two ends of its k_total outputs; the caller then
 // selects k_total - f - l among the middle positions.
 template <int NT>
 __device__ __forceinline__ void emit_forced(int n_row, int k_total, int f, int l, const int32_t* __restrict__ pos,
-                                            int32_t* __restrict__ out) {
-  for (int i = threadIdx.x; i < f; i += NT) out[i] = pos ? pos[i] : i;
+                                            int base, int32_t* __restrict__ out) {
+  for (int i = threadIdx.x; i < f; i += NT) out[i] = pos ? pos[i] : base + i;
   for (int j = threadIdx.x; j < l; j += NT) {
     const int i = n_row - l + j;
-    out[k_total - l + j] = pos ? pos[i] : i;
+    out[k_total - l + j] = pos ? pos[i] : base + i;
   }
 }
 
@@ -287,22 +318,25 @@ __device__ __forceinline__ void emit_forced(int n_row, int k_total, int f, int l
 // single row, where same-bin atomics dominate, not for batches).
 template <int NT, bool Adaptive>
 __global__ __launch_bounds__(NT, 1)
-void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f, int l,
-                 const int32_t* __restrict__ pos, int32_t* __restrict__ idx) {
+void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f_in, int l_in,
+                 const int32_t* __restrict__ pos, int32_t* __restrict__ idx, const int32_t* __restrict__ cu_n,
+                 const int32_t* __restrict__ cu_k) {
   __shared__ uint32_t hist[kCopies<NT> * kBins];
   __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
-  const int row = blockIdx.x;
-  int32_t* out = idx + static_cast<size_t>(row) * k_total;
-  emit_forced<NT>(n_row, k_total, f, l, pos, out);
-  const int n = n_row - f - l;
-  const int k = k_total - f - l;
-  if (k == 0) return;
-  const float* r = score + static_cast<size_t>(row) * n_row + f;
+  const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k);
+  const int f = rw.f, l = rw.l;
+  int32_t* out = idx + rw.out_off;
+  emit_forced<NT>(rw.n, rw.k, f, l, pos, rw.base, out);
+  const int n = rw.n - f - l;
+  const int k = rw.k - f - l;
+  if (k <= 0) return;
+  const float* r = score + rw.in_off + f;
   uint32_t take_eq;
   const uint32_t cut =
       radix_cut<NT, Adaptive>(RowKeys<NT>{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
-  emit_selected<NT>(r, n, cut, take_eq, pos ? pos + f : nullptr, f, out + f, static_cast<uint32_t>(k), sh_scan);
+  emit_selected<NT>(r, n, cut, take_eq, pos ? pos + f : nullptr, rw.base + f, out + f, static_cast<uint32_t>(k),
+                   sh_scan);
 }
 
 // Rows of up to NT * ITEMS scores: each thread loads its ITEMS consecutive
@@ -311,19 +345,21 @@ void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f,
 // order).
 template <int NT, int ITEMS>
 __global__ __launch_bounds__(NT, 1)
-void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, int f, int l,
-                     const int32_t* __restrict__ pos, int32_t* __restrict__ idx) {
+void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, int f_in, int l_in,
+                     const int32_t* __restrict__ pos, int32_t* __restrict__ idx, const int32_t* __restrict__ cu_n,
+                     const int32_t* __restrict__ cu_k) {
   static_assert(ITEMS <= 32, "masks are 32-bit");
   __shared__ uint32_t hist[kCopies<NT> * kBins];
   __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
-  const int rowi = blockIdx.x;
-  int32_t* out = idx + static_cast<size_t>(rowi) * k_total;
-  emit_forced<NT>(n_row, k_total, f, l, pos, out);
-  const int n = n_row - f - l;
-  const int k = k_total - f - l;
-  if (k == 0) return;
-  const float* r = score + static_cast<size_t>(rowi) * n_row + f;
+  const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k);
+  const int f = rw.f, l = rw.l;
+  int32_t* out = idx + rw.out_off;
+  emit_forced<NT>(rw.n, rw.k, f, l, pos, rw.base, out);
+  const int n = min(rw.n - f - l, NT * ITEMS);  // rows longer than the launch assumed are cut (never read past)
+  const int k = rw.k - f - l;
+  if (k <= 0) return;
+  const float* r = score + rw.in_off + f;
   out += f;
   const int i0 = threadIdx.x * ITEMS;
   uint32_t keys[ITEMS];
@@ -355,7 +391,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
     bool take = (gt_mask >> e) & 1u;
     if ((eq_mask >> e) & 1u) { take = eq_rank < take_eq; ++eq_rank; }
     if (take) {
-      if (o < static_cast<uint32_t>(k)) out[o] = pos ? pos[f + i0 + e] : f + i0 + e;
+      if (o < static_cast<uint32_t>(k)) out[o] = pos ? pos[f + i0 + e] : rw.base + f + i0 + e;
       ++o;
     }
   }
@@ -577,22 +613,25 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
   }
 }
 
+// n: the row length (ragged: the packed score count); n_longest: the longest
+// row (picks the kernel); cu_n / cu_k: ragged layout or null.
 template <int NT>
 void launch_topk_nt(const float* score, int rows, int n, int k, int f, int l, const int32_t* pos, int32_t* idx,
-                    hipStream_t stream) {
-  const int n_mid = n - f - l;
+                    const int32_t* cu_n, const int32_t* cu_k, hipStream_t stream, int n_longest = -1) {
+  const int n_mid = cu_n ? n_longest : n - f - l;
+  const dim3 g(rows), b(NT);
   if (n_mid <= NT * 4)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 4>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 4>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
   else if (n_mid <= NT * 8)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 8>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 8>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
   else if (n_mid <= NT * 16)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 16>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 16>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
   else if (n_mid <= NT * 32)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 32>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 32>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
   else if (rows == 1)
-    hipLaunchKernelGGL((topk_kernel<NT, true>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+    hipLaunchKernelGGL((topk_kernel<NT, true>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
   else
-    hipLaunchKernelGGL((topk_kernel<NT, false>), dim3(rows), dim3(NT), 0, stream, score, n, k, f, l, pos, idx);
+    hipLaunchKernelGGL((topk_kernel<NT, false>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
 }
 
 }  // namespace
@@ -613,8 +652,16 @@ hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_firs
     else
       hipLaunchKernelGGL(topk_wave_kernel<32>, grid, block, 0, stream, score, rows, n, k, idx);
   } else {
-    launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, stream);
+    launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, nullptr, nullptr, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_ragged(const float* score, int n_total, int B, const int32_t* cu_n, const int32_t* cu_k,
+                              int max_n, int k_cap, int keep_first, int keep_last, int32_t* idx, hipStream_t stream) {
+  if (B == 0 || max_n == 0 || k_cap == 0 || n_total == 0) return hipSuccess;
+  launch_topk_nt<kSelThreads>(score, B, n_total, k_cap, keep_first, keep_last, nullptr, idx, cu_n, cu_k, stream,
+                              max_n);
   return hipGetLastError();
 }
 

@@ -112,6 +112,81 @@ class OneShotStack:
                 self.post_layer(l)
 
 
+class RaggedOneShotStack:
+    """One-shot halting for a packed batch of samples of different lengths:
+    layers hold packed tensors (Q [T, Hq, D] ...) with the samples back to back
+    (`lengths` on the host).  Every sample keeps its own
+    k_b = effective_keep(len_b, keep, keep_first, keep_last) tokens; the kept
+    rows stay packed (sample by sample) through the post-halt layers."""
+
+    def __init__(self, layers: list[LayerTensors], lengths, halt_layer: int, keep: float,
+                 kv_mode: int = L.DASH_KV_ACTIVE, keep_first: int = 0, keep_last: int = 0):
+        self.layers = layers
+        self.hl = halt_layer
+        self.kv_mode = kv_mode
+        self.keep_first, self.keep_last = keep_first, keep_last
+        self.lengths = [int(n) for n in lengths]
+        self.ks = [L.effective_keep(n, keep, min(keep_first, n), min(keep_last, n - min(keep_first, n)))
+                   for n in self.lengths]
+        _, T, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        if T != sum(self.lengths):
+            raise ValueError("packed rows do not match the sample lengths")
+        dev, dt = layers[0].Q.device, layers[0].Q.dtype
+        cu = [0]
+        for n in self.lengths:
+            cu.append(cu[-1] + n)
+        cuk = [0]
+        for k in self.ks:
+            cuk.append(cuk[-1] + k)
+        self.cu_seqlens = torch.tensor(cu, dtype=torch.int32, device=dev)
+        self.cu_k = torch.tensor(cuk, dtype=torch.int32, device=dev)
+        self.T, self.K = T, cuk[-1]
+        self.max_len, self.max_k = max(self.lengths), max(max(self.ks), 1)
+        kk = max(self.K, 1)
+        self.O = torch.empty(T, Hq * D, device=dev, dtype=dt)
+        self.U = torch.empty(T, hidden, device=dev, dtype=dt)
+        self.score = torch.empty(T, device=dev, dtype=torch.float32)
+        self.idx = torch.empty(kk, device=dev, dtype=torch.int32)
+        self.Qa = torch.empty(kk, Hq, D, device=dev, dtype=dt)
+        self.Ka = torch.empty(kk, Hkv, D, device=dev, dtype=dt)
+        self.Va = torch.empty(kk, Hkv, D, device=dev, dtype=dt)
+        self.Oa = torch.empty(kk, Hq * D, device=dev, dtype=dt)
+        self.Ua = torch.empty(kk, hidden, device=dev, dtype=dt)
+        dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
+        self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, T, Hq, Hkv, D, hidden, dtc), T, device=dev)
+
+    def full_layer(self, l: int, with_score: bool) -> None:
+        x = self.layers[l]
+        L.dash_attn_layer_varlen(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.cu_seqlens, self.max_len,
+                                 self.score if with_score else None, self.ws)
+
+    def select(self) -> None:
+        L.dash_select_ragged(self.score, self.idx, self.cu_seqlens, self.cu_k, self.max_len,
+                             keep_first=self.keep_first, keep_last=self.keep_last)
+
+    def post_layer(self, l: int) -> None:
+        x = self.layers[l]
+        if self.K == 0:
+            return
+        if self.kv_mode == L.DASH_KV_ACTIVE:
+            L.dash_compact_many(self.idx, [(x.Q, self.Qa), (x.K, self.Ka), (x.V, self.Va)], n_max=self.K)
+            L.dash_attn_active_varlen(self.Qa[:self.K], self.Ka[:self.K], self.Va[:self.K], L.DASH_KV_ACTIVE,
+                                      self.Oa, self.cu_k, self.max_k, Wo=x.Wo, Ua=self.Ua)
+        else:
+            L.dash_compact(self.idx, x.Q, self.Qa, n_max=self.K)
+            L.dash_attn_active_varlen(self.Qa[:self.K], x.K, x.V, L.DASH_KV_ALL, self.Oa, self.cu_k, self.max_k,
+                                      q_pos=self.idx, cu_kv=self.cu_seqlens, Wo=x.Wo, Ua=self.Ua)
+
+    def run(self) -> None:
+        for l in range(len(self.layers)):
+            if l <= self.hl:
+                self.full_layer(l, with_score=(l == self.hl))
+                if l == self.hl:
+                    self.select()
+            else:
+                self.post_layer(l)
+
+
 class MultiShotStack:
     """Halting decisions at several layers (one sample): schedule
     [(l_1, k_1), (l_2, k_2), ...] with increasing layers and non-increasing

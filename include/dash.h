@@ -148,6 +148,48 @@ int dash_select(void* ctx, const dash_sel* p, const float* score, const int32_t*
                 int32_t* idx, int32_t* n_out_dev, float* tau_out,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Ragged batches ([P1] §5.1/§5.2: samples of one batch prune
+ * independently; with different lengths and kept counts they are packed back
+ * to back).  cu_* are DEVICE int32 prefix offsets with B + 1 entries
+ * (cu[0] = 0, sample b owns rows cu[b] .. cu[b+1]-1 of the packed tensors);
+ * their totals are passed from the host.  The kernels clamp every sample's
+ * rows into those totals and capacities, so inconsistent offsets can give
+ * wrong results but never out-of-bounds accesses. */
+
+/* a1 + a2 for a packed batch: s->B samples, s->S = the longest sample,
+ * cu_seqlens [B + 1], `total` = cu_seqlens[B] packed rows.  Q [total, Hq, D],
+ * K, V [total, Hkv, D], O [total, Hq*D], U [total, hidden], score [total]:
+ * causal attention within each sample, then the W_o GEMM and score over all
+ * rows.  Workspace: dash_workspace_size(DASH_OP_ATTN_LAYER, {B = 1, S =
+ * total, ...}, total). */
+int dash_attn_layer_varlen(void* ctx, const dash_shape* s, const int32_t* cu_seqlens, int total,
+                           const void* Q, const void* K, const void* V, const void* Wo, void* O, void* U,
+                           float* score, void* ws, size_t ws_bytes, void* stream);
+
+/* a3 for a packed batch (top-k only): sample b's n_b = cu_n[b+1] - cu_n[b]
+ * scores (of n_total) keep k_b = cu_k[b+1] - cu_k[b] positions (k_b <= n_b;
+ * with p->keep_first / keep_last applied per sample, f + l <= k_b), written
+ * ascending to idx[cu_k[b] ..] as PACKED row indices (cu_n[b] + position in
+ * the sample), so dash_compact / dash_compact_many gather them directly.
+ * k_total = cu_k[B] is idx's capacity; max_n >= every n_b.  p->k is unused. */
+int dash_select_ragged(void* ctx, const dash_sel* p, const float* score, int n_total, int B, const int32_t* cu_n,
+                       const int32_t* cu_k, int max_n, int k_total, int32_t* idx, void* stream);
+
+/* a5 for a packed batch: s->B samples, s->S = the most active rows of any
+ * sample.  Qa [n_total, Hq, D] are the packed active queries (sample b's at
+ * rows cu_q[b] .. cu_q[b+1]-1).  DASH_KV_ACTIVE: K, V are [n_total, Hkv, D],
+ * compacted with the queries (cu_kv NULL or cu_q); q_pos unused.
+ * DASH_KV_ALL: K, V are the full packed [kv_total, Hkv, D] with offsets
+ * cu_kv (the batch's cu_seqlens) and q_pos [n_total] gives each query's packed
+ * row (as dash_select_ragged writes it).  Oa [n_total, Hq*D]; if Wo != NULL,
+ * Ua [n_total, hidden] and score [n_total] as in dash_attn_active.
+ * Workspace: dash_workspace_size(DASH_OP_ATTN_ACTIVE, {B = 1, S = n_total,
+ * ...}, n_total). */
+int dash_attn_active_varlen(void* ctx, const dash_shape* s, const void* Qa, const int32_t* q_pos,
+                            const int32_t* cu_q, int n_total, const void* K, const void* V, int kv_mode,
+                            const int32_t* cu_kv, int kv_total, void* Oa, const void* Wo, void* Ua, float* score,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Δattn from a given U ([P1] §2.1, §2.2: the score needs only U, so any
  * attention kernel can feed it): score[t] = ||U_t||_2 (fp32 sums of squares,
  * fixed order) for t < n, n = *n_dev (or n_max).  U is [n_max, hidden] of

@@ -164,6 +164,35 @@ def test_compact_batch_validation(lib):
     assert f(None, None, 2, 0, one, 1, None) == L.DASH_OK  # nothing to do
 
 
+def test_ragged_validation(lib):
+    s = _shape(B=3, S=64)
+    f = lib.dash_attn_layer_varlen
+    ptrs = [FAKE] * 6
+    assert f(None, ctypes.byref(s), FAKE, 3 * 64 + 1, *ptrs, None, None, 0, None) == L.DASH_E_SHAPE
+    assert f(None, ctypes.byref(s), None, 100, *ptrs, None, None, 0, None) == L.DASH_E_INVAL
+    assert f(None, ctypes.byref(s), FAKE, 100, *ptrs, FAKE, None, 0, None) == L.DASH_E_WORKSPACE
+    assert f(None, ctypes.byref(s), FAKE, 0, *ptrs, None, None, 0, None) == L.DASH_OK
+    g = lib.dash_select_ragged
+    top = L.DashSel(L.DASH_SEL_TOPK, 0, 0, None, 2, None, 0, 0)
+    assert g(None, ctypes.byref(L.DashSel(L.DASH_SEL_ORDER_STAT, 0, 1, None, 2, None, 0, 0)), FAKE, 10, 2, FAKE,
+             FAKE, 8, 5, FAKE, None) == L.DASH_E_INVAL
+    assert g(None, ctypes.byref(top), FAKE, 10, 2, FAKE, FAKE, 11, 5, FAKE, None) == L.DASH_E_INVAL  # max_n > n_total
+    assert g(None, ctypes.byref(top), FAKE, 10, 2, None, FAKE, 8, 5, FAKE, None) == L.DASH_E_INVAL
+    assert g(None, ctypes.byref(top), FAKE, 10, 0, FAKE, FAKE, 8, 5, FAKE, None) == L.DASH_E_INVAL
+    assert g(None, ctypes.byref(top), None, 10, 2, None, None, 8, 0, None, None) == L.DASH_OK  # nothing kept
+    h = lib.dash_attn_active_varlen
+    a = dict(Qa=FAKE, q_pos=None, cu_q=FAKE, n=40, K=FAKE, V=FAKE, mode=L.DASH_KV_ACTIVE, cu_kv=None, kvt=0,
+             Oa=FAKE, Wo=None, Ua=None, score=None, ws=None, wsb=0)
+    call = lambda **kw: h(None, ctypes.byref(s), *dict(a, **kw).values(), None)
+    assert call(n=3 * 64 + 1) == L.DASH_E_SHAPE
+    assert call(cu_q=None) == L.DASH_E_INVAL
+    assert call(mode=L.DASH_KV_ALL) == L.DASH_E_INVAL  # needs q_pos and cu_kv
+    assert call(mode=L.DASH_KV_ALL, q_pos=FAKE, cu_kv=FAKE, kvt=0) == L.DASH_E_SHAPE
+    assert call(cu_kv=FAKE + 64) == L.DASH_E_INVAL  # active keys follow the queries
+    assert call(Ua=FAKE) == L.DASH_E_INVAL
+    assert call(n=0) == L.DASH_OK
+
+
 def test_attn_active_validation(lib):
     f = lib.dash_attn_active
     s = _shape()

@@ -598,6 +598,106 @@ def test_multi_shot_stack(dash, dtype, mode):
     assert maxrel(host(st.Ua)[:k2], U3) <= tol
 
 
+# ---------------------------------------------------------------------------
+# ragged (packed) batches: every sample against the oracle on its own slice
+# ---------------------------------------------------------------------------
+
+def _packed_layer(lengths, Hq, Hkv, D, hidden, dtype, seed, layer=0):
+    """Per-sample seeded inputs packed back to back; W_o shared (the first sample's)."""
+    xs = [layer_inputs(WORKLOADS[1].scaled(S=n, Hq=Hq, Hkv=Hkv, D=D, hidden=hidden, dtype=dtype), seed + b, layer)
+          for b, n in enumerate(lengths)]
+    cat = {n: np.concatenate([x[n] for x in xs]) for n in ("Q", "K", "V")}
+    cat["Wo"] = xs[0]["Wo"]
+    return xs, cat
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attn_layer_varlen(dash, dtype):
+    lengths = [300, 77, 1, 513, 128]
+    Hq, Hkv, D, hidden = 8, 2, (128 if dtype == "bf16" else 64), 256
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    xs, cat = _packed_layer(lengths, Hq, Hkv, D, hidden, dtype, seed=40)
+    T = sum(lengths)
+    cu = _cu(lengths)
+    Q, K, V = (dev_t(cat[n], tdt) for n in ("Q", "K", "V"))
+    Wo = dev_t(cat["Wo"].T, tdt)
+    O = torch.empty(T, Hq * D, device="cuda", dtype=tdt)
+    U = torch.empty(T, hidden, device="cuda", dtype=tdt)
+    sc = torch.empty(T, device="cuda", dtype=torch.float32)
+    dc = dash.DASH_BF16 if dtype == "bf16" else dash.DASH_F32
+    ws = dash.workspace(dash.DASH_OP_ATTN_LAYER, dash.make_shape(1, T, Hq, Hkv, D, hidden, dc), T)
+    say("attn layer varlen", dtype, lengths)
+    dash.dash_attn_layer_varlen(Q, K, V, Wo, O, U, torch.from_numpy(cu).cuda(), max(lengths), sc, ws)
+    torch.cuda.synchronize()
+    for b, x in enumerate(xs):
+        sl = slice(cu[b], cu[b + 1])
+        O_ref, U_ref, s_ref = oracle.attention_layer(x["Q"], x["K"], x["V"], cat["Wo"])
+        assert maxrel(host(O)[sl], O_ref) <= tol
+        assert maxrel(host(U)[sl], U_ref) <= tol
+        assert np.all(np.abs(host(sc)[sl] - s_ref) <= TOL_SCORE * s_ref)
+
+
+def test_select_ragged_bit_exact(dash):
+    lengths = [1000, 1, 37, 8192, 5000, 70000, 4]
+    rng = np.random.default_rng(5)
+    s = np.concatenate([score_vector(["normal", "equal", "bf16ties", "fewvalues", "perm", "normal", "special"][b],
+                                     n, seed=b) for b, n in enumerate(lengths)])
+    cu = _cu(lengths)
+    for f, l in ((0, 0), (3, 2)):
+        ks = [min(n, max(f + l, int(rng.integers(0, n + 1)))) for n in lengths]
+        ks[1] = 1 if f + l == 0 else ks[1]
+        cuk = _cu(ks)
+        idx = torch.full((int(cuk[-1]),), -5, dtype=torch.int32, device="cuda")
+        say("select ragged", lengths, ks, f, l)
+        dash.dash_select_ragged(torch.from_numpy(s).cuda(), idx, torch.from_numpy(cu).cuda(),
+                                torch.from_numpy(cuk).cuda(), max(lengths), keep_first=f, keep_last=l)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for b, n in enumerate(lengths):
+            fb = min(f, ks[b])
+            lb = min(l, ks[b] - fb)
+            ref = oracle.select_topk_forced(s[cu[b]:cu[b + 1]], ks[b], fb, lb) + cu[b]
+            np.testing.assert_array_equal(got[cuk[b]:cuk[b + 1]], ref)
+
+
+@pytest.mark.parametrize("dtype,mode", [("bf16", "active"), ("bf16", "all"), ("f32", "active")])
+def test_ragged_one_shot_step(dash, dtype, mode):
+    """Packed samples of different lengths, each keeping its own share: the halting
+    layer and each sample's selection (bit-exact on the GPU's scores) and the
+    post-halt layer teacher-forced, all per sample against the oracle."""
+    from attention_delta_token_amd.stack import LayerTensors, RaggedOneShotStack
+    lengths = [700, 256, 1024, 90, 1]
+    Hq, Hkv, D, hidden = 8, 2, (128 if dtype == "bf16" else 64), 384
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    packs = [_packed_layer(lengths, Hq, Hkv, D, hidden, dtype, seed=60, layer=l) for l in range(2)]
+    layers = [LayerTensors(*(dev_t(c[n], tdt) for n in ("Q", "K", "V")), dev_t(c["Wo"].T, tdt)) for _, c in packs]
+    st = RaggedOneShotStack(layers, lengths, halt_layer=0, keep=0.4,
+                            kv_mode=dash.DASH_KV_ACTIVE if mode == "active" else dash.DASH_KV_ALL)
+    say("ragged one-shot", dtype, mode, lengths, st.ks)
+    st.run()
+    torch.cuda.synchronize()
+    cu, cuk = _cu(lengths), _cu(st.ks)
+    score, idx = host(st.score), st.idx.cpu().numpy()
+    (xs0, c0), (xs1, c1) = packs
+    for b, n in enumerate(lengths):
+        sl = slice(cu[b], cu[b + 1])
+        _, U_ref, s_ref = oracle.attention_layer(xs0[b]["Q"], xs0[b]["K"], xs0[b]["V"], c0["Wo"])
+        assert maxrel(host(st.U)[sl], U_ref) <= tol
+        assert np.all(np.abs(score[sl] - s_ref) <= TOL_SCORE * s_ref)
+        mine = idx[cuk[b]:cuk[b + 1]] - cu[b]
+        np.testing.assert_array_equal(mine, oracle.select_topk(score[sl], st.ks[b]))
+        if st.ks[b] == 0:  # nothing kept (the one-token sample at keep 0.4)
+            continue
+        Oa = oracle.attn_active(xs1[b]["Q"], xs1[b]["K"], xs1[b]["V"], mine, mode)
+        assert maxrel(host(st.Ua)[cuk[b]:cuk[b + 1]], oracle.output_projection(Oa, c1["Wo"])) <= tol
+
+
 @pytest.mark.timeout(900)
 def test_qwen_s8192_one_shot_step(dash):
     """S=8192, 28/4 heads, D=128, hidden 3584, bf16: the full halt layer against the oracle,
