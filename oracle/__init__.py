@@ -8,5 +8,5 @@ from .dash_oracle import (  # noqa: F401
     causal_gqa_attention, output_projection, delta_attn, attention_layer,
     topk_count, select_topk, effective_keep_count, select_topk_forced,
     order_statistic, percentile_rank, threshold_step,
-    compact, attn_active, run_one_shot, run_multi_shot, run_threshold,
+    compact, attn_active, decode_step, run_one_shot, run_multi_shot, run_threshold,
 )

@@ -259,6 +259,28 @@ def attn_active(Q, K, V, idx, kv_mode: str) -> np.ndarray:
     raise ValueError(kv_mode)
 
 
+def decode_step(Q_new, K_new, V_new, K, V, idx, kv_mode: str) -> np.ndarray:
+    """Attention of n_new decode tokens after a pruned prefill ([P1] §3.1 step 5
+    and §5.1: the KV cache keeps only the active tokens, which also shortens
+    decoding).  The prefill's cache is K[idx], V[idx] ("active", at positions
+    idx) or all S rows ("all"); the new tokens' own K/V follow at positions
+    S, S+1, ...; every key at a position at or before a query's is visible.
+    Returns O [n_new, Hq*D]."""
+    S = K.shape[0]
+    n_new = Q_new.shape[0]
+    idx = np.asarray(idx, dtype=np.int64)
+    if kv_mode == "active":
+        Kc, Vc, pos = compact(K, idx), compact(V, idx), idx
+    elif kv_mode == "all":
+        Kc, Vc, pos = np.asarray(K, np.float64), np.asarray(V, np.float64), np.arange(S)
+    else:
+        raise ValueError(kv_mode)
+    new_pos = S + np.arange(n_new)
+    Kc = np.concatenate([Kc, np.asarray(K_new, np.float64)])
+    Vc = np.concatenate([Vc, np.asarray(V_new, np.float64)])
+    return causal_gqa_attention(Q_new, Kc, Vc, q_pos=new_pos, kv_pos=np.concatenate([pos, new_pos]))
+
+
 # ---------------------------------------------------------------------------
 # Whole stacks (small sizes only): one-shot and threshold policies
 # ---------------------------------------------------------------------------

@@ -421,6 +421,37 @@ def test_one_shot_stack_selection_from_halt_layer():
     assert res["U"][2].shape == (20, w.hidden)
 
 
+def test_decode_full_cache_is_dense_tail():
+    """Keeping every token, decode rows equal the last rows of causal attention
+    over the prefill followed by the new tokens."""
+    w = WORKLOADS[0].scaled(S=40, Hq=4, Hkv=2, D=16, hidden=32)
+    x = layer_inputs(w, 5, 0)
+    y = layer_inputs(w.scaled(S=3), 6, 0)
+    full = {n: np.concatenate([x[n], y[n]]) for n in ("Q", "K", "V")}
+    dense = oracle.causal_gqa_attention(full["Q"], full["K"], full["V"])
+    for mode in ("active", "all"):
+        got = oracle.decode_step(y["Q"], y["K"], y["V"], x["K"], x["V"], np.arange(40), mode)
+        np.testing.assert_allclose(got, dense[40:], rtol=0, atol=1e-12)
+
+
+def test_decode_pruned_cache_brute_force():
+    w = WORKLOADS[0].scaled(S=24, Hq=2, Hkv=1, D=8, hidden=16)
+    x = layer_inputs(w, 7, 0)
+    y = layer_inputs(w.scaled(S=2), 8, 0)
+    idx = np.array([0, 3, 4, 9, 15, 23])
+    got = oracle.decode_step(y["Q"], y["K"], y["V"], x["K"], x["V"], idx, "active")
+    Kc = np.concatenate([x["K"][idx], y["K"]]).astype(np.float64)
+    Vc = np.concatenate([x["V"][idx], y["V"]]).astype(np.float64)
+    for i in range(2):
+        visible = len(idx) + i + 1  # the cache plus the new tokens up to this one
+        for h in range(2):
+            sc = np.array([y["Q"][i, h].astype(np.float64) @ Kc[j, 0] for j in range(visible)]) / math.sqrt(8)
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            ref = sum(p[j] * Vc[j, 0] for j in range(visible))
+            np.testing.assert_allclose(got[i, h * 8:(h + 1) * 8], ref, rtol=0, atol=1e-12)
+
+
 def test_multi_shot_single_decision_is_one_shot():
     w = WORKLOADS[0].scaled(S=40, layers=3, halt_layer=1)
     get = lambda l: layer_inputs(w, 2, l)
