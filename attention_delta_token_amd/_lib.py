@@ -21,14 +21,14 @@ DASH_OK, DASH_E_INVAL, DASH_E_SHAPE, DASH_E_DTYPE, DASH_E_ALIGN, DASH_E_WORKSPAC
 DASH_F32, DASH_BF16 = 0, 1
 DASH_KV_ACTIVE, DASH_KV_ALL = 0, 1
 DASH_SEL_TOPK, DASH_SEL_THRESHOLD, DASH_SEL_ORDER_STAT = 0, 1, 2
-DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE = 0, 1, 2
+DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE, DASH_OP_DECODE = 0, 1, 2, 3
 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
             "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
             "dash_attn_active", "dash_score", "dash_attn_layer_varlen", "dash_select_ragged",
-            "dash_attn_active_varlen",
+            "dash_attn_active_varlen", "dash_decode",
             "dash_trace_start", "dash_trace_stop", "dash_trace_read")
-TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact", "score")
+TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact", "score", "decode")
 
 
 class DashShape(Structure):
@@ -102,6 +102,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.dash_attn_active_varlen.restype = c_int
+    lib.dash_decode.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.dash_decode.restype = c_int
     lib.dash_trace_start.argtypes = [c_int]
     lib.dash_trace_start.restype = c_int
     lib.dash_trace_stop.argtypes = []
@@ -290,6 +293,17 @@ def dash_attn_active_varlen(Qa, K, V, kv_mode: int, Oa, cu_q, max_rows: int, q_p
                                           _ptr(K), _ptr(V), kv_mode, _ptr(cu_kv), K.shape[0], _ptr(Oa), _ptr(Wo),
                                           _ptr(Ua), _ptr(score), _ptr(ws),
                                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dash_decode(Qd, Kc, Vc, n_kv, Od, ws=None, stream=None) -> None:
+    """Decode attention: Qd [B, n_new, Hq, D]; Kc, Vc [B, S, Hkv, D] caches with n_kv [B] (device) rows."""
+    B, n_new, Hq, D = Qd.shape
+    S, Hkv = Kc.shape[1], Kc.shape[2]
+    shape = make_shape(B, S, Hq, Hkv, D, Hq * D, _dtype_code(Qd))
+    if ws is None:
+        ws = workspace(DASH_OP_DECODE, shape, n_new, device=Qd.device)
+    _check(load().dash_decode(None, ctypes.byref(shape), _ptr(Qd), n_new, _ptr(Kc), _ptr(Vc), _ptr(n_kv), _ptr(Od),
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def trace_start(capacity: int) -> None:

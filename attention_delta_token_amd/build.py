@@ -13,7 +13,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdash.so")
-SOURCES = ["attn_fwd.hip", "wo_gemm.hip", "score.hip", "select.hip", "compact.hip", "dash_abi.cpp"]
+SOURCES = ["attn_fwd.hip", "wo_gemm.hip", "score.hip", "decode.hip", "select.hip", "compact.hip", "dash_abi.cpp"]
 ARCH = os.environ.get("DASH_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -197,6 +197,9 @@ size_t dash_workspace_size(void* /*ctx*/, int op, const dash_shape* s, int n_max
         return score_ws_bytes(s, static_cast<int64_t>(s->B) * n_max);
       case DASH_OP_SELECT:
         return 0;  // selection keeps its state in LDS
+      case DASH_OP_DECODE:
+        if (check_shape(s, false) != DASH_OK || n_max < 1) return 0;
+        return align_up(dash::decode_workspace_bytes(s->B, s->S, s->Hkv, s->D));
       default:
         return 0;
     }
@@ -444,6 +447,34 @@ int dash_select_ragged(void* /*ctx*/, const dash_sel* p, const float* score, int
         dash::launch_topk_ragged(score, n_total, B, cu_n, cu_k, max_n, k_total, p->keep_first, p->keep_last, idx, st);
     trace_close(tr, st);
     if (e != hipSuccess) return hip_fail(e, "selection launch");
+    return DASH_OK;
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_decode(void* /*ctx*/, const dash_shape* s, const void* Qd, int n_new, const void* Kc, const void* Vc,
+                const int32_t* n_kv, void* Od, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    if (s->dtype != DASH_BF16) return fail(DASH_E_DTYPE, "decode supports bf16 only");
+    if (n_new < 1) return fail(DASH_E_INVAL, "n_new must be >= 1");
+    if ((s->Hq / s->Hkv) * n_new > dash::decode_max_rows())
+      return fail(DASH_E_SHAPE, "(Hq / Hkv) * n_new = %d exceeds %d", (s->Hq / s->Hkv) * n_new,
+                  dash::decode_max_rows());
+    rc = check_ptrs({{Qd, "Qd"}, {Kc, "Kc"}, {Vc, "Vc"}, {Od, "Od"}});
+    if (rc) return rc;
+    if (!n_kv) return fail(DASH_E_INVAL, "n_kv is NULL");
+    const size_t need = align_up(dash::decode_workspace_bytes(s->B, s->S, s->Hkv, s->D));
+    if (!ws || ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+    if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int tr = trace_open(DASH_TR_DECODE, st);
+    hipError_t e = dash::launch_decode(s->D, Qd, Kc, Vc, n_kv, s->B, s->S, n_new, s->Hq, s->Hkv, Od,
+                                       static_cast<float*>(ws), st);
+    trace_close(tr, st);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
     return DASH_OK;
   } catch (...) {
     return fail(DASH_E_INVAL, "unexpected host exception");

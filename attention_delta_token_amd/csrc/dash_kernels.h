@@ -78,6 +78,13 @@ hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_
 hipError_t launch_row_norm(int dtype, const void* U, const int32_t* n_dev, int n_max, int hidden, float* score,
                            hipStream_t stream);
 
+// Decode attention (bf16, D in {64, 128}): g * n_new <= decode_max_rows().
+int decode_chunks(int B, int S_cap, int Hkv, int* chunk_out);
+size_t decode_workspace_bytes(int B, int S_cap, int Hkv, int D);
+int decode_max_rows();
+hipError_t launch_decode(int D, const void* Qd, const void* Kc, const void* Vc, const int32_t* n_kv, int B,
+                         int S_cap, int n_new, int Hq, int Hkv, void* Od, float* part, hipStream_t stream);
+
 // One tensor of a multi-tensor gather: Xa[r] = X[idx[r]], rows of row_bytes.
 constexpr int kMaxGather = 4;
 struct GatherItem {

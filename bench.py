@@ -279,6 +279,8 @@ def main():
     if not args.profile_only:
         out["select_sweep"] = [select_sweep(dash, torch, dev, rows, n) for rows, n in ((2048, 8192), (256, 65536))]
         out["score"] = score_measurements(dash, torch, dev, step, layers[0])
+        if w.dtype == "bf16" and w.mode != "threshold":
+            out["decode"] = decode_measurements(dash, torch, dev, w, layers[-1])
 
     if not args.no_cpu_baseline and not args.profile_only:
         out["cpu_baseline"] = cpu_baseline(w, host_keep, step, k_rows)
@@ -339,6 +341,32 @@ def score_measurements(dash, torch, dev, step, layer):
     out.update({"fused_proj_us": with_ms * 1e3, "plain_proj_us": without_ms * 1e3,
                 "fused_overhead_us": (with_ms - without_ms) * 1e3})
     return out
+
+
+def decode_measurements(dash, torch, dev, w, layer):
+    """One decode token per sample against the cache a prefill leaves: the k kept
+    rows (pruned) versus all S rows (dense), same kernel; the cache read
+    (K and V of every cached row) is the algorithmic traffic."""
+    res = {}
+    Hkv, D, Hq = w.Hkv, w.D, w.Hq
+    Qd = layer.Q[:1].reshape(1, 1, Hq, D).contiguous()
+    for name, rows in (("pruned", w.k), ("dense", w.S)):  # cache rows, the new token's own included
+        Kc = layer.K[:rows].reshape(1, rows, Hkv, D)
+        Vc = layer.V[:rows].reshape(1, rows, Hkv, D)
+        n_kv = torch.tensor([rows], dtype=torch.int32, device=dev)
+        Od = torch.empty(1, 1, Hq * D, dtype=layer.Q.dtype, device=dev)
+        for _ in range(3):
+            dash.dash_decode(Qd, Kc, Vc, n_kv, Od)
+        dash.trace_start(64)
+        for _ in range(20):
+            dash.dash_decode(Qd, Kc, Vc, n_kv, Od)
+        dash.trace_stop()
+        t = [ms for op, ms in dash.trace_read(64) if op == "decode"]
+        ms = sum(t) / len(t)
+        gbps = rows * Hkv * D * 2 * 2 / (ms * 1e-3) / 1e9
+        res[name] = {"cache_rows": rows, "us": ms * 1e3, "cache_GBps": gbps}
+    res["speedup"] = res["dense"]["us"] / res["pruned"]["us"]
+    return res
 
 
 def describe(w):

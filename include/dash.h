@@ -60,7 +60,7 @@ typedef enum {
 typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
 typedef enum { DASH_KV_ACTIVE = 0, DASH_KV_ALL = 1 } dash_kv_mode;
 typedef enum { DASH_SEL_TOPK = 0, DASH_SEL_THRESHOLD = 1, DASH_SEL_ORDER_STAT = 2 } dash_sel_mode;
-typedef enum { DASH_OP_ATTN_LAYER = 0, DASH_OP_SELECT = 1, DASH_OP_ATTN_ACTIVE = 2 } dash_op;
+typedef enum { DASH_OP_ATTN_LAYER = 0, DASH_OP_SELECT = 1, DASH_OP_ATTN_ACTIVE = 2, DASH_OP_DECODE = 3 } dash_op;
 
 /* Problem shape.  hidden is the width of U; Hq*D is the width of O. */
 typedef struct {
@@ -190,6 +190,20 @@ int dash_attn_active_varlen(void* ctx, const dash_shape* s, const void* Qa, cons
                             const int32_t* cu_kv, int kv_total, void* Oa, const void* Wo, void* Ua, float* score,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Decode attention over a KV cache — the step after a (pruned) prefill ([P1]
+ * §3.1 step 5, §5.1: the cache holds only the active tokens, so each decode
+ * step reads less).  s->B samples, s->S = cache capacity (rows per sample),
+ * s->Hq, s->Hkv, s->D (bf16 only, D in {64, 128}); s->hidden is unused.
+ *   Qd [B, n_new, Hq, D]: the new tokens' queries.
+ *   Kc, Vc [B, S, Hkv, D]: each sample's cache; sample b holds n_kv[b] rows
+ *     (DEVICE int32 [B], clamped to S), its last n_new rows being the new
+ *     tokens' own K/V, earlier rows the kept prefill tokens in position order.
+ *   Od [B, n_new, Hq*D]: new token i sees cache rows 0 .. n_kv[b] - n_new + i.
+ * Requires (Hq / Hkv) * n_new <= 32.  Split over the keys: workspace
+ * dash_workspace_size(DASH_OP_DECODE, s, n_new). */
+int dash_decode(void* ctx, const dash_shape* s, const void* Qd, int n_new, const void* Kc, const void* Vc,
+                const int32_t* n_kv, void* Od, void* ws, size_t ws_bytes, void* stream);
+
 /* Δattn from a given U ([P1] §2.1, §2.2: the score needs only U, so any
  * attention kernel can feed it): score[t] = ||U_t||_2 (fp32 sums of squares,
  * fixed order) for t < n, n = *n_dev (or n_max).  U is [n_max, hidden] of
@@ -268,7 +282,8 @@ typedef enum {
   DASH_TR_PROJ_ACTIVE = 3,  /* W_o GEMM (+ score finalize) of dash_attn_active */
   DASH_TR_SELECT = 4,       /* selection kernel of dash_select */
   DASH_TR_COMPACT = 5,      /* gather kernel of dash_compact / dash_compact_many */
-  DASH_TR_SCORE = 6         /* row-norm kernel of dash_score */
+  DASH_TR_SCORE = 6,        /* row-norm kernel of dash_score */
+  DASH_TR_DECODE = 7        /* chunk + merge kernels of dash_decode */
 } dash_trace_op;
 
 int dash_trace_start(int capacity);

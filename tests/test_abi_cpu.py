@@ -193,6 +193,20 @@ def test_ragged_validation(lib):
     assert call(n=0) == L.DASH_OK
 
 
+def test_decode_validation(lib):
+    f = lib.dash_decode
+    s = _shape(B=2, S=128, Hq=28, Hkv=4)
+    need = lib.dash_workspace_size(None, L.DASH_OP_DECODE, ctypes.byref(s), 1)
+    assert need > 0
+    args = lambda **kw: dict(dict(Qd=FAKE, n_new=1, K=FAKE, V=FAKE, n_kv=FAKE, Od=FAKE, ws=FAKE, wsb=need), **kw)
+    call = lambda shape, a: f(None, ctypes.byref(shape), *a.values(), None)
+    assert call(_shape(B=2, S=128, Hq=28, Hkv=4, dtype=L.DASH_F32, D=64), args()) == L.DASH_E_DTYPE
+    assert call(s, args(n_new=5)) == L.DASH_E_SHAPE  # 7 * 5 rows > 32
+    assert call(s, args(n_new=0)) == L.DASH_E_INVAL
+    assert call(s, args(n_kv=None)) == L.DASH_E_INVAL
+    assert call(s, args(wsb=need - 1)) == L.DASH_E_WORKSPACE
+
+
 def test_attn_active_validation(lib):
     f = lib.dash_attn_active
     s = _shape()

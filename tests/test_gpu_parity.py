@@ -599,6 +599,43 @@ def test_multi_shot_stack(dash, dtype, mode):
 
 
 # ---------------------------------------------------------------------------
+# decode over the pruned KV cache
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,n_new,mode,Hq,Hkv,D", [(900, 1, "active", 28, 4, 128), (900, 4, "active", 28, 4, 128),
+                                                   (700, 2, "all", 8, 2, 64), (8192, 1, "active", 28, 4, 128),
+                                                   (3000, 3, "all", 32, 8, 128)])
+def test_decode_vs_oracle(dash, S, n_new, mode, Hq, Hkv, D):
+    """B = 2 samples: the cache holds each sample's kept prefill rows (kv active) or
+    all of them (kv all), then the new tokens' own K/V; every new token against the
+    oracle's decode step."""
+    B = 2
+    w = WORKLOADS[1].scaled(S=S, Hq=Hq, Hkv=Hkv, D=D, hidden=Hq * D)
+    pre = [layer_inputs(w, 70 + b, 0) for b in range(B)]
+    new = [layer_inputs(w.scaled(S=n_new), 80 + b, 0) for b in range(B)]
+    rng = np.random.default_rng(S + n_new)
+    idx = [np.sort(rng.choice(S, int(S * (0.5 - 0.1 * b)), replace=False)) if mode == "active" else np.arange(S)
+           for b in range(B)]
+    cap = S + n_new
+    Kc = np.zeros((B, cap, Hkv, D), np.float32)
+    Vc = np.zeros((B, cap, Hkv, D), np.float32)
+    n_kv = []
+    for b in range(B):
+        m = len(idx[b])
+        Kc[b, :m], Vc[b, :m] = pre[b]["K"][idx[b]], pre[b]["V"][idx[b]]
+        Kc[b, m:m + n_new], Vc[b, m:m + n_new] = new[b]["K"], new[b]["V"]
+        n_kv.append(m + n_new)
+    Qd = dev_t(np.stack([x["Q"] for x in new]))
+    Od = torch.zeros(B, n_new, Hq * D, device="cuda", dtype=torch.bfloat16)
+    say("decode", S, n_new, mode, Hq, Hkv, D, n_kv)
+    dash.dash_decode(Qd, dev_t(Kc), dev_t(Vc), torch.tensor(n_kv, dtype=torch.int32, device="cuda"), Od)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = oracle.decode_step(new[b]["Q"], new[b]["K"], new[b]["V"], pre[b]["K"], pre[b]["V"], idx[b], mode)
+        assert maxrel(host(Od)[b], ref) <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
 # ragged (packed) batches: every sample against the oracle on its own slice
 # ---------------------------------------------------------------------------
 
