@@ -350,13 +350,22 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     __builtin_amdgcn_s_barrier();        // everyone's; and everyone is past step j-1
     if (j + 2 < n_tiles) kload.issue(k_src, kbuf(j), static_cast<uint32_t>(j + 2) * tile_bytes);
     if (j + 1 < n_tiles) vload.issue(v_src, vbuf(j + 1), static_cast<uint32_t>(j + 1) * tile_bytes);
+    // The score MFMAs (which wait on their K operand reads) run at raised wave
+    // priority, so the SIMD's other wave fills in with its softmax and P V work
+    // rather than competing for the same issue slots.
     if (j + 1 < j_mask) {  // steady state: tile j+1 fully visible
+      __builtin_amdgcn_s_setprio(1);
       qk(kbuf(j + 1), s_nxt, -m_run);
+      __builtin_amdgcn_s_setprio(0);
       softmax(s_cur);
       pv(s_cur, vbuf(j));
       update_max(s_nxt, false);
     } else {
-      if (j + 1 < n_w) qk(kbuf(j + 1), s_nxt, -m_run);
+      if (j + 1 < n_w) {
+        __builtin_amdgcn_s_setprio(1);
+        qk(kbuf(j + 1), s_nxt, -m_run);
+        __builtin_amdgcn_s_setprio(0);
+      }
       if (j < n_w) {
         softmax(s_cur);
         pv(s_cur, vbuf(j));
