@@ -3,11 +3,13 @@
 // "DASH：基于注意力增量的Transformer令牌压缩，实现长序列推理高效加速", §3.1 step 4
 // and §3.3 (gather by the active index set, avoiding needless copies).
 //
-// HBM-bound copy.  The (row, 16-byte chunk) space is flattened so that
-// consecutive lanes move consecutive 16-byte chunks of one row (coalesced
-// reads and writes for any row width), each thread moves several chunks with
-// all loads issued before the stores, and the grid is sized from the row
-// capacity so a device-resident row count needs no host round trip.
+// HBM-bound copy.  One wave moves one row: the row's source index is read
+// once, every 16-byte chunk of the row (across the gathered tensors) is loaded
+// before any is stored, consecutive lanes move consecutive chunks (coalesced
+// for any row width), and the stores bypass the caches' write-allocate
+// (nontemporal), which measured as fast as a plain device-to-device copy of
+// the same bytes.  The grid is sized from the row capacity, so a
+// device-resident row count needs no host round trip.
 #include "dash_common.h"
 #include "dash_kernels.h"
 
@@ -16,12 +18,12 @@ namespace dash {
 namespace {
 
 constexpr int kCompactThreads = 256;
-constexpr int kCompactItems = 4;
+constexpr int kCompactRows = kCompactThreads / 64;  // one row per wave
 
-// Up to kMaxGather tensors gathered at the same rows.  Row r of the flattened
-// space holds the 16-byte chunks of row r of tensor 0, then of tensor 1, ...;
-// lo[j] is the first chunk of tensor j within a flattened row, w[j] its chunks
-// per row and cpr the flattened row length.  Unused slots have lo = cpr.
+// Up to kMaxGather tensors gathered at the same rows.  A gathered row is the
+// 16-byte chunks of row r of tensor 0, then of tensor 1, ...; lo[j] is the
+// first chunk of tensor j within it, w[j] its chunks per row and cpr the
+// gathered row length.  Unused slots have lo = cpr.
 struct GatherSet {
   const u32x4* X[kMaxGather];
   u32x4* Xa[kMaxGather];
@@ -41,43 +43,45 @@ __device__ __forceinline__ T pick(const T (&a)[kMaxGather], int j) {
   return v;
 }
 
+// U chunks per lane in flight: a row of up to 64 * U chunks moves in one batch.
+template <int U>
 __global__ __launch_bounds__(kCompactThreads)
 void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_dev, int n_max, int per_sample,
                     GatherSet g) {
   int n = n_dev ? *n_dev : n_max;
   if (n > n_max) n = n_max;
+  const int r = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kCompactRows + (threadIdx.x >> 6));
+  if (r >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t src = idx[r];
+  // batched: row r belongs to sample r / per_sample, whose source rows start at sample * S
+  const uint64_t sample = per_sample > 0 ? static_cast<uint32_t>(r) / static_cast<uint32_t>(per_sample) : 0u;
   const uint32_t cpr = g.cpr;
-  // The host guarantees n_max * cpr < 2^31, so 32-bit indexing is exact.
-  const uint32_t total = static_cast<uint32_t>(n < 0 ? 0 : n) * cpr;
-  const uint32_t base = blockIdx.x * (kCompactItems * kCompactThreads) + threadIdx.x;
-  u32x4 v[kCompactItems];
-  u32x4* dst[kCompactItems];
+  for (uint32_t c0 = 0; c0 < cpr; c0 += 64u * U) {
+    u32x4 v[U];
+    u32x4* dst[U];
 #pragma unroll
-  for (int it = 0; it < kCompactItems; ++it) {
-    const uint32_t e = base + static_cast<uint32_t>(it) * kCompactThreads;
-    dst[it] = nullptr;
-    if (e < total) {
-      const uint32_t r = e / cpr;
-      const uint32_t c = e - r * cpr;
-      int j = 0;
+    for (int i = 0; i < U; ++i) {
+      const uint32_t c = c0 + static_cast<uint32_t>(lane + 64 * i);
+      dst[i] = nullptr;
+      if (c < cpr) {
+        int j = 0;
 #pragma unroll
-      for (int t = 1; t < kMaxGather; ++t)
-        if (c >= g.lo[t]) j = t;
-      const uint32_t cj = c - pick(g.lo, j);
-      const uint32_t w = pick(g.w, j);
-      const int32_t src = idx[r];
-      const int Sj = pick(g.S, j);
-      if (src >= 0 && src < Sj) {
-        // batched: row r belongs to sample r / per_sample, whose rows start at sample * S
-        const uint64_t base = per_sample > 0 ? static_cast<uint64_t>(r / static_cast<uint32_t>(per_sample)) * Sj : 0u;
-        v[it] = __builtin_nontemporal_load(pick(g.X, j) + (base + static_cast<uint64_t>(src)) * w + cj);
-        dst[it] = pick(g.Xa, j) + static_cast<uint64_t>(r) * w + cj;
+        for (int t = 1; t < kMaxGather; ++t)
+          if (c >= g.lo[t]) j = t;
+        const int Sj = pick(g.S, j);
+        if (src >= 0 && src < Sj) {
+          const uint32_t cj = c - pick(g.lo, j);
+          const uint32_t w = pick(g.w, j);
+          v[i] = __builtin_nontemporal_load(pick(g.X, j) + (sample * Sj + static_cast<uint64_t>(src)) * w + cj);
+          dst[i] = pick(g.Xa, j) + static_cast<uint64_t>(r) * w + cj;
+        }
       }
     }
-  }
 #pragma unroll
-  for (int it = 0; it < kCompactItems; ++it)
-    if (dst[it]) *dst[it] = v[it];
+    for (int i = 0; i < U; ++i)
+      if (dst[i]) __builtin_nontemporal_store(v[i], dst[i]);
+  }
 }
 
 }  // namespace
@@ -105,12 +109,21 @@ hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_m
   }
   g.cpr = acc;
   const uint64_t total = static_cast<uint64_t>(n_max) * acc;
-  const uint64_t per_block = static_cast<uint64_t>(kCompactThreads) * kCompactItems;
-  const uint64_t blocks = (total + per_block - 1) / per_block;
-  if (blocks == 0) return hipSuccess;
   if (total >= 0x80000000ull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(compact_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCompactThreads), 0, stream, idx,
-                     n_dev, n_max, per_sample, g);
+  const dim3 grid(static_cast<unsigned>((static_cast<uint64_t>(n_max) + kCompactRows - 1) / kCompactRows));
+  const uint32_t need = (acc + 63) / 64;  // chunks per lane for one row
+  if (need <= 1)
+    hipLaunchKernelGGL(compact_kernel<1>, grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g);
+  else if (need <= 2)
+    hipLaunchKernelGGL(compact_kernel<2>, grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g);
+  else if (need <= 4)
+    hipLaunchKernelGGL(compact_kernel<4>, grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g);
+  else if (need <= 8)
+    hipLaunchKernelGGL(compact_kernel<8>, grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g);
+  else if (need <= 12)
+    hipLaunchKernelGGL(compact_kernel<12>, grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g);
+  else
+    hipLaunchKernelGGL(compact_kernel<16>, grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g);
   return hipGetLastError();
 }
 
