@@ -79,7 +79,7 @@ hipError_t launch_row_norm(int dtype, const void* U, const int32_t* n_dev, int n
                            hipStream_t stream);
 
 // Decode attention (bf16, D in {64, 128}): g * n_new <= decode_max_rows().
-int decode_chunks(int B, int S_cap, int Hkv, int* chunk_out);
+int decode_chunks(int B, int S_cap, int Hkv, int* steps_out);
 size_t decode_workspace_bytes(int B, int S_cap, int Hkv, int D);
 int decode_max_rows();
 hipError_t launch_decode(int D, const void* Qd, const void* Kc, const void* Vc, const int32_t* n_kv, int B,

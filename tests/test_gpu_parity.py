@@ -604,11 +604,13 @@ def test_multi_shot_stack(dash, dtype, mode):
 
 @pytest.mark.parametrize("S,n_new,mode,Hq,Hkv,D", [(900, 1, "active", 28, 4, 128), (900, 4, "active", 28, 4, 128),
                                                    (700, 2, "all", 8, 2, 64), (8192, 1, "active", 28, 4, 128),
-                                                   (3000, 3, "all", 32, 8, 128)])
+                                                   (3000, 3, "all", 32, 8, 128), (600, 5, "all", 12, 2, 64),
+                                                   (70000, 1, "active", 8, 2, 64)])
 def test_decode_vs_oracle(dash, S, n_new, mode, Hq, Hkv, D):
     """B = 2 samples: the cache holds each sample's kept prefill rows (kv active) or
     all of them (kv all), then the new tokens' own K/V; every new token against the
-    oracle's decode step."""
+    oracle's decode step.  The cases span 6 to 30 rows per kv-head (g * n_new) and,
+    at S = 70000, caches long enough that each wave takes several 64-key steps."""
     B = 2
     w = WORKLOADS[1].scaled(S=S, Hq=Hq, Hkv=Hkv, D=D, hidden=Hq * D)
     pre = [layer_inputs(w, 70 + b, 0) for b in range(B)]
@@ -633,6 +635,42 @@ def test_decode_vs_oracle(dash, S, n_new, mode, Hq, Hkv, D):
     for b in range(B):
         ref = oracle.decode_step(new[b]["Q"], new[b]["K"], new[b]["V"], pre[b]["K"], pre[b]["V"], idx[b], mode)
         assert maxrel(host(Od)[b], ref) <= TOL_BF16
+
+
+def test_decode_graph_replay(dash):
+    """Decode calls captured in a HIP graph: every replay, with eager work and
+    synchronisations in between, gives the eager call's output bit for bit (the
+    library records no memsets, so nothing in the graph depends on replay order)."""
+    Hq, Hkv, D, rows = 28, 4, 128, 1500
+    g = torch.Generator(device="cpu").manual_seed(11)
+    Qd = torch.randn(1, 1, Hq, D, generator=g).to("cuda", torch.bfloat16)
+    Kc = torch.randn(1, rows, Hkv, D, generator=g).to("cuda", torch.bfloat16)
+    Vc = torch.randn(1, rows, Hkv, D, generator=g).to("cuda", torch.bfloat16)
+    n_kv = torch.tensor([rows - 7], dtype=torch.int32, device="cuda")
+    Od = torch.empty(1, 1, Hq * D, device="cuda", dtype=torch.bfloat16)
+    ws = dash.workspace(dash.DASH_OP_DECODE, dash.make_shape(1, rows, Hq, Hkv, D, Hq * D, dash.DASH_BF16), 1)
+    say("decode graph replay", rows)
+    dash.dash_decode(Qd, Kc, Vc, n_kv, Od, ws=ws)
+    torch.cuda.synchronize()
+    ref = Od.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dash.dash_decode(Qd, Kc, Vc, n_kv, Od, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(3):
+            dash.dash_decode(Qd, Kc, Vc, n_kv, Od, ws=ws)
+    other = torch.empty_like(Od)
+    for rep in range(4):
+        Od.zero_()
+        dash.dash_decode(Qd, Kc, Vc, torch.tensor([rows // 2], dtype=torch.int32, device="cuda"), other, ws=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Od, ref), rep
 
 
 # ---------------------------------------------------------------------------
