@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     DASH_SEL_ORDER_STAT, DASH_SEL_THRESHOLD, DASH_SEL_TOPK, DashError, EXPORTED, LIB_PATH,
     dash_attn_active, dash_attn_layer, dash_compact, dash_compact_many, dash_compact_batch, dash_score,
     dash_attn_layer_varlen, dash_select_ragged, dash_attn_active_varlen, dash_decode, DASH_OP_DECODE, dash_select, dash_workspace_size, effective_keep, load, make_shape,
-    version, workspace, trace_start, trace_stop, trace_read,
+    version, workspace, trace_start, trace_select, trace_stop, trace_read,
 )

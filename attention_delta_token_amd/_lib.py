@@ -27,7 +27,7 @@ EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "d
             "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
             "dash_attn_active", "dash_score", "dash_attn_layer_varlen", "dash_select_ragged",
             "dash_attn_active_varlen", "dash_decode",
-            "dash_trace_start", "dash_trace_stop", "dash_trace_read")
+            "dash_trace_start", "dash_trace_select", "dash_trace_stop", "dash_trace_read")
 TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact", "score", "decode")
 
 
@@ -107,6 +107,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_decode.restype = c_int
     lib.dash_trace_start.argtypes = [c_int]
     lib.dash_trace_start.restype = c_int
+    lib.dash_trace_select.argtypes = [ctypes.c_uint]
+    lib.dash_trace_select.restype = c_int
     lib.dash_trace_stop.argtypes = []
     lib.dash_trace_stop.restype = c_int
     lib.dash_trace_read.argtypes = [POINTER(c_int), POINTER(ctypes.c_float), c_int, POINTER(c_int)]
@@ -309,6 +311,14 @@ def dash_decode(Qd, Kc, Vc, n_kv, Od, ws=None, stream=None) -> None:
 def trace_start(capacity: int) -> None:
     """Start bracketing every library launch with HIP events (measurement only)."""
     _check(load().dash_trace_start(capacity))
+
+
+def trace_select(ops) -> None:
+    """Record only these launch-group kinds (names from TRACE_OPS) from now on."""
+    mask = 0
+    for name in ops:
+        mask |= 1 << TRACE_OPS.index(name)
+    _check(load().dash_trace_select(ctypes.c_uint(mask)))
 
 
 def trace_stop() -> None:

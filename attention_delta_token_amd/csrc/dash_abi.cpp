@@ -85,6 +85,7 @@ std::vector<hipEvent_t> g_tr_ev;  // 2 per record
 std::vector<int> g_tr_op;
 int g_tr_n = 0;
 bool g_tr_on = false;
+uint32_t g_tr_mask = ~0u;  // dash_trace_op kinds that are recorded
 
 void trace_release() {
   for (hipEvent_t e : g_tr_ev) (void)hipEventDestroy(e);
@@ -97,7 +98,7 @@ void trace_release() {
 int trace_open(int op, hipStream_t st) {
   if (!g_tr_on) return -1;
   std::lock_guard<std::mutex> lk(g_tr_mu);
-  if (!g_tr_on || g_tr_n >= static_cast<int>(g_tr_op.size())) return -1;
+  if (!g_tr_on || g_tr_n >= static_cast<int>(g_tr_op.size()) || !((g_tr_mask >> op) & 1u)) return -1;
   const int slot = g_tr_n++;
   g_tr_op[slot] = op;
   (void)hipEventRecord(g_tr_ev[2 * slot], st);
@@ -128,11 +129,18 @@ int dash_trace_start(int capacity) {
       }
     }
     g_tr_op.assign(static_cast<size_t>(capacity), -1);
+    g_tr_mask = ~0u;
     g_tr_on = true;
     return DASH_OK;
   } catch (...) {
     return fail(DASH_E_INVAL, "unexpected host exception");
   }
+}
+
+int dash_trace_select(unsigned op_mask) {
+  std::lock_guard<std::mutex> lk(g_tr_mu);
+  g_tr_mask = op_mask;
+  return DASH_OK;
 }
 
 int dash_trace_stop(void) {

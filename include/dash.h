@@ -273,8 +273,12 @@ int dash_attn_active(void* ctx, const dash_shape* s, const void* Qa, const int32
  * have been recorded or dash_trace_stop() is called.  dash_trace_read waits
  * for the recorded events and copies out, for up to `max` groups, the group
  * kind (dash_trace_op) and its elapsed milliseconds into host arrays; *n gets
- * the number copied.  Starting again discards earlier records.  Not
- * thread-safe with concurrent launches from several host threads. */
+ * the number copied.  Starting again discards earlier records.
+ * dash_trace_select(op_mask) restricts recording to the kinds whose bit
+ * (1u << dash_trace_op) is set, from the next launch on, so that a timed run
+ * pays for the event pairs of the groups it measures only; dash_trace_start
+ * resets the mask to every kind.  Not thread-safe with concurrent launches
+ * from several host threads. */
 typedef enum {
   DASH_TR_ATTN_LAYER = 0,   /* attention kernel of dash_attn_layer */
   DASH_TR_PROJ_LAYER = 1,   /* W_o GEMM (+ score finalize) of dash_attn_layer */
@@ -287,6 +291,7 @@ typedef enum {
 } dash_trace_op;
 
 int dash_trace_start(int capacity);
+int dash_trace_select(unsigned op_mask);
 int dash_trace_stop(void);
 int dash_trace_read(int* ops, float* ms, int max, int* n);
 

@@ -804,3 +804,21 @@ def test_qwen_s8192_one_shot_step(dash):
     torch.cuda.synchronize()
     assert torch.equal(U1, st.U) and torch.equal(s1, st.score) and torch.equal(i1, st.idx)
     assert torch.equal(Ua1, st.Ua)
+
+
+def test_trace_select_records_only_chosen_kinds(dash):
+    """dash_trace_select limits the event pairs to the chosen launch kinds (the
+    bench brackets only attention launches inside its timed steps)."""
+    x = _layer(300, 8, 2, 128, 256, seed=3)
+    say("trace select")
+    dash.trace_start(16)
+    dash.trace_select(("attn_layer",))
+    _run_layer(dash, x)
+    dash.trace_stop()
+    recs = dash.trace_read(16)
+    assert [op for op, _ in recs] == ["attn_layer"]
+    assert recs[0][1] > 0.0
+    dash.trace_start(16)  # a new start records every kind again
+    _run_layer(dash, x)
+    dash.trace_stop()
+    assert [op for op, _ in dash.trace_read(16)] == ["attn_layer", "proj_layer"]
