@@ -25,8 +25,6 @@ constexpr int kDecStep = kWave;       // keys per wave step (one per lane)
 constexpr int kDecMaxRows = 32;        // g * n_new rows per kv-head
 constexpr int kDecMaxChunks = 1024;    // key chunks per (sample, kv-head)
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
-
 // Wave-wide max / sum in registers: a rotate butterfly inside each 16-lane
 // row (DPP row_ror 8, 4, 2, 1), then the four row results through readlane,
 // combined in a fixed order so every lane gets the same value.

@@ -11,13 +11,18 @@
 //   summary "DASH：通过注意力动态监测实现长上下文高效预填充", sections
 //   层间更新动态监测 and 选择性停止机制.
 //
-// One workgroup of 1024 threads owns one row of scores.  Scores map to
-// order-preserving 32-bit keys; a three-pass radix select (11, 11 and 10 bits,
-// most significant first) over LDS histograms finds the cut key T and how many
-// keys equal to T must be taken.  A final pass with a workgroup prefix scan of
-// (greater-than-T, equal-to-T) counts emits the survivors in ascending order,
-// so ties resolve to the lower position without any sort.  Everything lives
-// in one launch: no host round trip, no global atomics, deterministic.
+// One workgroup of 1024 threads owns one row of scores (batches of at least
+// 256 rows of at most 8192 aligned scores take one wave per row instead).
+// Scores map to order-preserving 32-bit keys.  A radix select over LDS
+// histograms finds the cut key T and how many keys equal to T must be taken:
+// for rows held in registers and for a single long row, the bits shared by the
+// row's smallest and largest key are settled first, then digits of up to 11
+// bits follow, most significant first (long rows in a batch use 11-, 11- and
+// 10-bit digits).  A final pass with a
+// prefix scan of (greater-than-T, equal-to-T) counts emits the survivors in
+// ascending order, so ties resolve to the lower position without any sort.
+// Everything lives in one launch: no host round trip, no global atomics,
+// deterministic.
 #include "dash_common.h"
 #include "dash_kernels.h"
 
@@ -32,7 +37,6 @@ constexpr int kBins = 2048;
 // Each histogram is kept in kCopies copies, lane l counting into copy
 // l % kCopies: scores cluster in a few bins, and the copies cut same-address
 // LDS atomic conflicts by that factor.
-template <int NT>
 constexpr int kCopies = 4;
 
 // Order-preserving key: larger score -> larger key.  NaN -> 0 (below every
@@ -154,9 +158,9 @@ __device__ uint32_t radix_cut(ForKeys for_keys, uint32_t kk, uint32_t* hist, uin
     const int w = sh < 11 ? sh : 11;
     sh -= w;
     const uint32_t dm = (1u << w) - 1u;
-    for (int b = threadIdx.x; b < kCopies<NT> * kBins; b += NT) hist[b] = 0u;
+    for (int b = threadIdx.x; b < kCopies * kBins; b += NT) hist[b] = 0u;
     __syncthreads();
-    uint32_t* my_hist = hist + (threadIdx.x % kCopies<NT>) * kBins;
+    uint32_t* my_hist = hist + (threadIdx.x % kCopies) * kBins;
     for_keys([&](uint32_t key) {
       if ((key & pmask) == prefix) atomicAdd(&my_hist[(key >> sh) & dm], 1u);
     });
@@ -170,7 +174,7 @@ __device__ uint32_t radix_cut(ForKeys for_keys, uint32_t kk, uint32_t* hist, uin
       c[j] = 0u;
       if (b0 + j < nb) {
 #pragma unroll
-        for (int cp = 0; cp < kCopies<NT>; ++cp) c[j] += hist[cp * kBins + b0 + j];
+        for (int cp = 0; cp < kCopies; ++cp) c[j] += hist[cp * kBins + b0 + j];
       }
       mine += c[j];
     }
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(NT, 1)
 void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f_in, int l_in,
                  const int32_t* __restrict__ pos, int32_t* __restrict__ idx, const int32_t* __restrict__ cu_n,
                  const int32_t* __restrict__ cu_k) {
-  __shared__ uint32_t hist[kCopies<NT> * kBins];
+  __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
   const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k);
@@ -349,7 +353,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
                      const int32_t* __restrict__ pos, int32_t* __restrict__ idx, const int32_t* __restrict__ cu_n,
                      const int32_t* __restrict__ cu_k) {
   static_assert(ITEMS <= 32, "masks are 32-bit");
-  __shared__ uint32_t hist[kCopies<NT> * kBins];
+  __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
   const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k);
@@ -400,7 +404,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
 __global__ __launch_bounds__(kSelThreads, 1)
 void order_stat_kernel(const float* __restrict__ score, const int32_t* __restrict__ n_dev, int n_max,
                        int rank, float* __restrict__ tau_out) {
-  __shared__ uint32_t hist[kCopies<kSelThreads> * kBins];
+  __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   __shared__ uint32_t sh_cut[2];
   int n = n_dev ? *n_dev : n_max;

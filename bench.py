@@ -92,7 +92,7 @@ def read_traffic(digest):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU (the path is built and measured on one device); --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
