@@ -22,6 +22,12 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source additions.  The W_o GEMM measured 3-4% faster with the iterative
+# ILP machine scheduler; the attention kernel measured slower with it (and with
+# the other non-default strategies), so it keeps the default.
+EXTRA_FLAGS = {
+    "wo_gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def hipcc() -> str:
@@ -39,7 +45,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [cc, *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
