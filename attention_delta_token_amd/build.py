@@ -23,10 +23,12 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 # Per-source additions.  The W_o GEMM measured 3-4% faster with the iterative
-# ILP machine scheduler; the attention kernel measured slower with it (and with
-# the other non-default strategies), so it keeps the default.
+# ILP machine scheduler and the selection kernels about 4% faster with the
+# max-ILP one; the attention kernel measured slower with every non-default
+# strategy, so it keeps the default.
 EXTRA_FLAGS = {
     "wo_gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "select.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 
