@@ -111,6 +111,53 @@ class OneShotStack:
             else:
                 self.post_layer(l)
 
+    # -- gather once -------------------------------------------------------
+    # A model gathers the hidden states of the kept tokens once at the halting
+    # layer; every later layer's projections then produce compacted Q, K and V
+    # by themselves.  The synthetic layers here hold full-length Q/K/V, so
+    # run() gathers them per layer.  prepare_gather_once() takes the kept
+    # indices of one run, gathers each post-halt layer's inputs once (outside
+    # any timing), and run_gather_once() then does the step the way a model
+    # would: full-length layers, selection, one gather of an [S, hidden]
+    # hidden-state stand-in, post-halt layers on the already compacted inputs.
+
+    def prepare_gather_once(self) -> None:
+        if self.B != 1 or self.k == 0:
+            raise ValueError("gather-once mode supports one sample with k > 0")
+        self.run()
+        torch.cuda.synchronize()
+        dev, dt = self.O.device, self.O.dtype
+        self.H = torch.zeros(self.S, self.hidden, device=dev, dtype=dt)  # hidden-state stand-in
+        self.Ha = torch.empty(self.k, self.hidden, device=dev, dtype=dt)
+        self.pre = {}
+        for l in range(self.hl + 1, len(self.layers)):
+            x = self.layers[l]
+            Qa = torch.empty(self.k, self.Hq, self.D, device=dev, dtype=dt)
+            if self.kv_mode == L.DASH_KV_ACTIVE:
+                Ka = torch.empty(self.k, self.Hkv, self.D, device=dev, dtype=dt)
+                Va = torch.empty(self.k, self.Hkv, self.D, device=dev, dtype=dt)
+                L.dash_compact_many(self.idx, [(x.Q, Qa), (x.K, Ka), (x.V, Va)], n_max=self.k)
+                self.pre[l] = (Qa, Ka, Va)
+            else:
+                L.dash_compact(self.idx, x.Q, Qa, n_max=self.k)
+                self.pre[l] = (Qa, x.K, x.V)
+        torch.cuda.synchronize()
+
+    def run_gather_once(self) -> None:
+        for l in range(len(self.layers)):
+            if l <= self.hl:
+                self.full_layer(l, with_score=(l == self.hl))
+                if l == self.hl:
+                    self.select()
+                    L.dash_compact(self.idx, self.H, self.Ha, n_max=self.k)
+            else:
+                x, (Qa, Ka, Va) = self.layers[l], self.pre[l]
+                if self.kv_mode == L.DASH_KV_ACTIVE:
+                    L.dash_attn_active(Qa, Ka, Va, L.DASH_KV_ACTIVE, self.Oa, n_max=self.k, Wo=x.Wo, Ua=self.Ua)
+                else:
+                    L.dash_attn_active(Qa, Ka, Va, L.DASH_KV_ALL, self.Oa, q_pos=self.idx, n_max=self.k, Wo=x.Wo,
+                                       Ua=self.Ua, S=self.S)
+
 
 class RaggedOneShotStack:
     """One-shot halting for a packed batch of samples of different lengths:

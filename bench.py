@@ -182,6 +182,18 @@ def main():
             dense.run()
         dense_ms = timed(dense.run, args.steps)
 
+    # Gather-once step (one-shot policy): the kept rows' hidden states are
+    # gathered once at the halting layer ([S, hidden] stand-in) and the
+    # post-halt layers run on inputs compacted beforehand, as a model's own
+    # projections would produce them; the main step above instead gathers each
+    # post-halt layer's synthetic Q, K and V inside the step.
+    gather_once_ms = None
+    if w.mode != "threshold" and not args.profile_only and not args.no_dense:
+        step.prepare_gather_once()
+        for _ in range(args.warmup):
+            step.run_gather_once()
+        gather_once_ms = timed(step.run_gather_once, args.steps)
+
     S, Hq, Hkv, D, hid = w.S, w.Hq, w.Hkv, w.D, w.hidden
     by = {}
     for op, t in recs:
@@ -275,6 +287,11 @@ def main():
         "dense_tokens_per_s": (S / (dense_ms * 1e-3)) if dense_ms else None,
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
         "ideal_speedup_flops": dense_flops / dash_flops,
+        "gather_once": ({"ms_per_step": gather_once_ms, "tokens_per_s": S / (gather_once_ms * 1e-3),
+                         "speedup_vs_dense": (dense_ms / gather_once_ms) if dense_ms else None,
+                         "what": "one gather of an [S, hidden] bf16 hidden-state stand-in at the halting layer; "
+                                 "post-halt layers on inputs compacted beforehand"}
+                        if gather_once_ms else None),
         "all_traced_ms_per_step": ms_all_traced,
         "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
         "kernels": {

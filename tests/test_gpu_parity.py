@@ -497,6 +497,31 @@ def test_one_shot_step_batched(dash, dtype):
         assert maxrel(host(st.Ua)[b], oracle.output_projection(Oa, Wo[1])) <= tol
 
 
+@pytest.mark.parametrize("mode", ["active", "all"])
+def test_gather_once_step_matches_step(dash, mode):
+    """The gather-once step (one gather of a hidden-state stand-in at the halting
+    layer, post-halt layers on inputs compacted beforehand) gives the post-halt
+    outputs of the regular step bit for bit, and its gather is exact."""
+    from attention_delta_token_amd.stack import LayerTensors, OneShotStack
+    w = WORKLOADS[1].scaled(S=640, hidden=384, layers=3)
+    hostl = [layer_inputs(w, 40, l) for l in range(3)]
+    layers = [LayerTensors(*(dev_t(h[n]) for n in ("Q", "K", "V")), dev_t(h["Wo"].T)) for h in hostl]
+    kv = dash.DASH_KV_ACTIVE if mode == "active" else dash.DASH_KV_ALL
+    say("gather once", mode, w.S, w.k)
+    st = OneShotStack(layers, halt_layer=0, k=w.k, kv_mode=kv)
+    st.run()
+    torch.cuda.synchronize()
+    Ua_ref, idx_ref = st.Ua.clone(), st.idx.clone()
+    st.prepare_gather_once()
+    st.H.copy_(torch.randn(st.S, st.hidden, generator=torch.Generator().manual_seed(1)).to("cuda", torch.bfloat16))
+    st.Ua.zero_()
+    st.run_gather_once()
+    torch.cuda.synchronize()
+    assert torch.equal(st.idx, idx_ref)
+    assert torch.equal(st.Ua, Ua_ref)
+    assert torch.equal(st.Ha, st.H[st.idx.long()])
+
+
 def test_kv_all_at_halt_layer_equals_dense_rows(dash):
     """On the GPU: post-halt attention with all K/V at the halting layer equals the dense rows."""
     S, Hq, Hkv, D, hidden = 700, 8, 2, 128, 256
