@@ -167,6 +167,7 @@ def main():
     dash.trace_select(("attn_layer", "attn_active"))
     ms = timed(run_marked, args.steps)
     dash.trace_stop()
+    clocks = gpu_clocks()  # read right after the timed steps (context only)
     attn_recs = dash.trace_read(cap_attn)
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     cap_all = (8 * w.layers + 8) * args.steps  # every launch group of every layer and step
@@ -293,6 +294,7 @@ def main():
                                  "post-halt layers on inputs compacted beforehand"}
                         if gather_once_ms else None),
         "all_traced_ms_per_step": ms_all_traced,
+        "clocks_after_timed_steps": clocks,
         "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
         "kernels": {
             "attn_full_ms": (sum(t_full) / len(t_full)) if t_full else None,
@@ -319,6 +321,19 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, host_keep, step, k_rows)
 
     print(json.dumps(out), flush=True)
+
+
+def gpu_clocks():
+    """Current shader and memory clocks as rocm-smi reports them (clocks are
+    not pinned; recorded for context), or None when the tool is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception:  # noqa: BLE001 - best effort only
+        return None
+    card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
+    return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()} or None
 
 
 def select_sweep(dash, torch, dev, rows=256, n=65536):
@@ -357,8 +372,21 @@ def score_measurements(dash, torch, dev, step, layer):
     t = [ms for op, ms in dash.trace_read(64) if op == "score"]
     ms = sum(t) / len(t)
     gbps = rows * (hidden * U.element_size() + 4.0) / (ms * 1e-3) / 1e9
+    # cold: a 1 GiB write before each call evicts U from L2 and the MALL
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(5):
+        flush.fill_(i)
+        dash.trace_start(4)
+        dash.dash_score(U, score)
+        dash.trace_stop()
+        cold.extend(t for op, t in dash.trace_read(4) if op == "score")
+    del flush
+    ms_cold = sum(cold) / len(cold)
+    gbps_cold = rows * (hidden * U.element_size() + 4.0) / (ms_cold * 1e-3) / 1e9
     out = {"standalone_us": ms * 1e3, "standalone_GBps": gbps, "standalone_frac": gbps / PEAK_HBM_GBPS,
-           "rows": rows, "hidden": hidden}
+           "standalone_cold_us": ms_cold * 1e3, "standalone_cold_GBps": gbps_cold,
+           "standalone_cold_frac": gbps_cold / PEAK_HBM_GBPS, "rows": rows, "hidden": hidden}
     # fused: the same layer's W_o GEMM with the score and without it
     ws = step.ws
     proj = {}
