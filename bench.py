@@ -312,7 +312,8 @@ def main():
     }
 
     if not args.profile_only:
-        out["select_sweep"] = [select_sweep(dash, torch, dev, rows, n) for rows, n in ((2048, 8192), (256, 65536))]
+        out["select_sweep"] = [select_sweep(dash, torch, dev, rows, n)
+                               for rows, n in ((2048, 8192), (8192, 8192), (256, 65536))]
         out["score"] = score_measurements(dash, torch, dev, step, layers[0])
         if w.dtype == "bf16" and w.mode != "threshold":
             out["decode"] = decode_measurements(dash, torch, dev, w, layers[-1])
