@@ -123,10 +123,18 @@ def _check(rc: int) -> None:
 
 
 def _ptr(t) -> int | None:
+    """Device address of a tensor argument.  The kernels take dense row-major
+    device memory, so a host tensor or a strided view is refused here rather
+    than handed to a kernel (an int is taken as a raw device address)."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"tensor argument on {t.device}: the library takes device (cuda) tensors")
+    if not t.is_contiguous():
+        raise ValueError(f"tensor argument with strides {t.stride()} for shape {tuple(t.shape)}: "
+                         "the library takes contiguous (row-major) tensors")
     return t.data_ptr()
 
 

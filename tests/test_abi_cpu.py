@@ -233,3 +233,17 @@ def test_workspace_size(lib):
     assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(s), 8192) == 0
     assert lib.dash_workspace_size(None, 17, ctypes.byref(s), 8192) == 0
     assert lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(_shape(D=33)), 8192) == 0
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    """The Python binding hands only dense device memory to the library: a host
+    tensor or a strided view raises before anything reaches a kernel."""
+    import torch
+    import attention_delta_token_amd as dash
+    idx = torch.zeros(4, dtype=torch.int32)
+    X = torch.zeros(8, 16, dtype=torch.float32)
+    Xa = torch.zeros(4, 16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device"):
+        dash.dash_compact(idx, X, Xa)
+    with pytest.raises(ValueError, match="device"):
+        dash.dash_select(torch.zeros(16), torch.zeros(8, dtype=torch.int32), k=8)
