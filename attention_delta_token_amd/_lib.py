@@ -146,6 +146,17 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+def _need(t, numel: int, dtype, name: str) -> None:
+    """Check a tensor argument's element type and that it holds at least
+    `numel` elements (the kernels write or read that many); None passes."""
+    if t is None or isinstance(t, int):
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {numel} needed")
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return DASH_BF16
@@ -179,7 +190,12 @@ def dash_attn_layer(Q, K, V, Wo, O, U, score=None, ws=None, stream=None) -> None
     q = Q if Q.dim() == 4 else Q.unsqueeze(0)
     k = K if K.dim() == 4 else K.unsqueeze(0)
     B, S, Hq, D = q.shape
-    shape = make_shape(B, S, Hq, k.shape[2], D, Wo.shape[0], _dtype_code(Q))
+    Hkv, hidden = k.shape[2], Wo.shape[0]
+    for t, n, name in ((K, B * S * Hkv * D, "K"), (V, B * S * Hkv * D, "V"), (Wo, hidden * Hq * D, "Wo"),
+                       (O, B * S * Hq * D, "O"), (U, B * S * hidden, "U")):
+        _need(t, n, Q.dtype, name)
+    _need(score, B * S, torch.float32, "score")
+    shape = make_shape(B, S, Hq, Hkv, D, hidden, _dtype_code(Q))
     _check(load().dash_attn_layer(None, ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(Wo), _ptr(O),
                                   _ptr(U), _ptr(score), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream)))
@@ -192,6 +208,15 @@ def dash_select(score, idx=None, *, mode: int = DASH_SEL_TOPK, k: int = 0, rank:
     with forced retention, k is the total kept count (see effective_keep)."""
     if n_max is None:
         n_max = score.shape[-1] if score is not None else 0
+    _need(score, rows * n_max, torch.float32, "score")
+    _need(idx, rows * k if mode == DASH_SEL_TOPK else (n_max if mode == DASH_SEL_THRESHOLD else 0), torch.int32,
+          "idx")
+    _need(pos, n_max if mode != DASH_SEL_ORDER_STAT else 0, torch.int32, "pos")
+    _need(counters, 0, torch.uint8, "counters")
+    _need(n_dev, 1, torch.int32, "n_dev")
+    _need(n_out, 1, torch.int32, "n_out")
+    _need(tau, 1, torch.float32, "tau")
+    _need(tau_out, 1, torch.float32, "tau_out")
     sel = DashSel(mode, k, rank, _ptr(tau), patience, _ptr(counters), keep_first, keep_last)
     _check(load().dash_select(None, ctypes.byref(sel), _ptr(score), _ptr(pos), _ptr(n_dev), n_max, rows,
                               _ptr(idx), _ptr(n_out), _ptr(tau_out), None, 0, _stream(stream)))
@@ -211,6 +236,8 @@ def dash_compact(idx, X, Xa, n_dev=None, n_max: int | None = None, stream=None) 
     row_bytes = X[0].numel() * X.element_size() if S > 0 else Xa[0].numel() * Xa.element_size()
     if n_max is None:
         n_max = idx.shape[0]
+    _need(idx, n_max, torch.int32, "idx")
+    _need(Xa, n_max * row_bytes // X.element_size(), X.dtype, "Xa")
     _check(load().dash_compact(None, _ptr(idx), _ptr(n_dev), n_max, _ptr(X), S, row_bytes, _ptr(Xa),
                                _stream(stream)))
 
@@ -220,10 +247,12 @@ def dash_compact_many(idx, pairs, n_dev=None, n_max: int | None = None, stream=N
     in pairs, Xa[r] = X[idx[r]] for r < n (at most 4 pairs)."""
     if n_max is None:
         n_max = idx.shape[0]
+    _need(idx, n_max, torch.int32, "idx")
     arr = (DashGather * len(pairs))()
     for j, (X, Xa) in enumerate(pairs):
         S = X.shape[0]
         row_bytes = X[0].numel() * X.element_size() if S > 0 else Xa[0].numel() * Xa.element_size()
+        _need(Xa, n_max * row_bytes // X.element_size(), X.dtype, f"pairs[{j}] Xa")
         arr[j] = DashGather(_ptr(X), S, row_bytes, _ptr(Xa))
     _check(load().dash_compact_many(None, _ptr(idx), _ptr(n_dev), n_max, arr, len(pairs), _stream(stream)))
 
@@ -232,10 +261,12 @@ def dash_compact_batch(idx, pairs, stream=None) -> None:
     """Per-sample gathers of B samples in one launch: idx [B, k] local positions;
     for each (X [B, S, ...], Xa [B, k, ...]) in pairs, Xa[b, r] = X[b, idx[b, r]]."""
     B, k = idx.shape
+    _need(idx, 0, torch.int32, "idx")
     arr = (DashGather * len(pairs))()
     for j, (X, Xa) in enumerate(pairs):
         S = X.shape[1]
         row_bytes = X[0, 0].numel() * X.element_size() if S > 0 else Xa[0, 0].numel() * Xa.element_size()
+        _need(Xa, B * k * row_bytes // X.element_size(), X.dtype, f"pairs[{j}] Xa")
         arr[j] = DashGather(_ptr(X), S, row_bytes, _ptr(Xa))
     _check(load().dash_compact_batch(None, _ptr(idx), B, k, arr, len(pairs), _stream(stream)))
 
@@ -245,6 +276,7 @@ def dash_score(U, score, n_dev=None, n_max: int | None = None, stream=None) -> N
     if n_max is None:
         n_max = U.shape[0]
     hidden = U[0].numel() if U.shape[0] > 0 else U.shape[-1]
+    _need(score, n_max, torch.float32, "score")
     _check(load().dash_score(None, _ptr(U), _dtype_code(U), hidden, _ptr(n_dev), n_max, _ptr(score),
                              _stream(stream)))
 
@@ -267,6 +299,14 @@ def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: 
         S = kv_rows if kv_mode == DASH_KV_ALL else n_max
     if hidden is None:
         hidden = Wo.shape[0] if Wo is not None else Hq * D
+    _need(V, K.numel(), Qa.dtype, "V")
+    _need(K, 0, Qa.dtype, "K")
+    _need(Oa, B * n_max * Hq * D, Qa.dtype, "Oa")
+    _need(Wo, hidden * Hq * D, Qa.dtype, "Wo")
+    _need(Ua, B * n_max * hidden, Qa.dtype, "Ua")
+    _need(score, B * n_max, torch.float32, "score")
+    _need(q_pos, B * n_max, torch.int32, "q_pos")
+    _need(n_dev, 1, torch.int32, "n_dev")
     shape = make_shape(B, S, Hq, Hkv, D, hidden, _dtype_code(Qa))
     _check(load().dash_attn_active(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(n_dev), n_max, _ptr(K),
                                    _ptr(V), kv_mode, _ptr(Oa), _ptr(Wo), _ptr(Ua), _ptr(score), _ptr(ws),
@@ -277,7 +317,13 @@ def dash_attn_layer_varlen(Q, K, V, Wo, O, U, cu_seqlens, max_len: int, score=No
     """Packed batch: Q [T, Hq, D], K, V [T, Hkv, D], cu_seqlens [B+1] (device int32), max_len = longest sample."""
     T, Hq, D = Q.shape
     B = cu_seqlens.shape[0] - 1
-    shape = make_shape(B, max_len, Hq, K.shape[1], D, Wo.shape[0], _dtype_code(Q))
+    Hkv, hidden = K.shape[1], Wo.shape[0]
+    for t, n, name in ((K, T * Hkv * D, "K"), (V, T * Hkv * D, "V"), (Wo, hidden * Hq * D, "Wo"),
+                       (O, T * Hq * D, "O"), (U, T * hidden, "U")):
+        _need(t, n, Q.dtype, name)
+    _need(score, T, torch.float32, "score")
+    _need(cu_seqlens, B + 1, torch.int32, "cu_seqlens")
+    shape = make_shape(B, max_len, Hq, Hkv, D, hidden, _dtype_code(Q))
     _check(load().dash_attn_layer_varlen(None, ctypes.byref(shape), _ptr(cu_seqlens), T, _ptr(Q), _ptr(K), _ptr(V),
                                          _ptr(Wo), _ptr(O), _ptr(U), _ptr(score), _ptr(ws),
                                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
@@ -288,6 +334,10 @@ def dash_select_ragged(score, idx, cu_n, cu_k, max_n: int, keep_first: int = 0, 
     """Per-sample top-k of a packed score vector; idx receives packed row indices."""
     sel = DashSel(DASH_SEL_TOPK, 0, 0, None, 2, None, keep_first, keep_last)
     B = cu_n.shape[0] - 1
+    _need(score, 0, torch.float32, "score")
+    _need(idx, 0, torch.int32, "idx")
+    _need(cu_n, B + 1, torch.int32, "cu_n")
+    _need(cu_k, B + 1, torch.int32, "cu_k")
     _check(load().dash_select_ragged(None, ctypes.byref(sel), _ptr(score), score.shape[0], B, _ptr(cu_n), _ptr(cu_k),
                                      max_n, idx.shape[0], _ptr(idx), _stream(stream)))
 
@@ -298,6 +348,14 @@ def dash_attn_active_varlen(Qa, K, V, kv_mode: int, Oa, cu_q, max_rows: int, q_p
     n_total, Hq, D = Qa.shape
     B = cu_q.shape[0] - 1
     hidden = Wo.shape[0] if Wo is not None else Hq * D
+    _need(V, K.numel(), Qa.dtype, "V")
+    _need(Oa, n_total * Hq * D, Qa.dtype, "Oa")
+    _need(Wo, hidden * Hq * D, Qa.dtype, "Wo")
+    _need(Ua, n_total * hidden, Qa.dtype, "Ua")
+    _need(score, n_total, torch.float32, "score")
+    _need(q_pos, n_total, torch.int32, "q_pos")
+    _need(cu_q, B + 1, torch.int32, "cu_q")
+    _need(cu_kv, B + 1, torch.int32, "cu_kv")
     shape = make_shape(B, max_rows, Hq, K.shape[1], D, hidden, _dtype_code(Qa))
     _check(load().dash_attn_active_varlen(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(cu_q), n_total,
                                           _ptr(K), _ptr(V), kv_mode, _ptr(cu_kv), K.shape[0], _ptr(Oa), _ptr(Wo),
@@ -309,6 +367,10 @@ def dash_decode(Qd, Kc, Vc, n_kv, Od, ws=None, stream=None) -> None:
     """Decode attention: Qd [B, n_new, Hq, D]; Kc, Vc [B, S, Hkv, D] caches with n_kv [B] (device) rows."""
     B, n_new, Hq, D = Qd.shape
     S, Hkv = Kc.shape[1], Kc.shape[2]
+    _need(Kc, B * S * Hkv * D, Qd.dtype, "Kc")
+    _need(Vc, B * S * Hkv * D, Qd.dtype, "Vc")
+    _need(Od, B * n_new * Hq * D, Qd.dtype, "Od")
+    _need(n_kv, B, torch.int32, "n_kv")
     shape = make_shape(B, S, Hq, Hkv, D, Hq * D, _dtype_code(Qd))
     if ws is None:
         ws = workspace(DASH_OP_DECODE, shape, n_new, device=Qd.device)

@@ -247,3 +247,28 @@ def test_binding_refuses_host_and_strided_tensors():
         dash.dash_compact(idx, X, Xa)
     with pytest.raises(ValueError, match="device"):
         dash.dash_select(torch.zeros(16), torch.zeros(8, dtype=torch.int32), k=8)
+
+
+def test_binding_refuses_undersized_or_mistyped_buffers():
+    """An output smaller than the shape the binding derives, or an argument of
+    the wrong element type, raises before any pointer is taken (so before any
+    kernel could write past its end)."""
+    import torch
+    import attention_delta_token_amd as dash
+    idx = torch.zeros(4, dtype=torch.int32)
+    X = torch.zeros(8, 16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="at least"):
+        dash.dash_compact(idx, X, torch.zeros(3, 16, dtype=torch.float32))
+    with pytest.raises(ValueError, match="dtype"):
+        dash.dash_compact(idx.long(), X, torch.zeros(4, 16, dtype=torch.float32))
+    with pytest.raises(ValueError, match="at least"):
+        dash.dash_select(torch.zeros(16), torch.zeros(7, dtype=torch.int32), k=8)
+    B, S, Hq, Hkv, D, hidden = 1, 64, 4, 2, 64, 128
+    bf = dict(dtype=torch.bfloat16)
+    Q, K, V = torch.zeros(B, S, Hq, D, **bf), torch.zeros(B, S, Hkv, D, **bf), torch.zeros(B, S, Hkv, D, **bf)
+    Wo = torch.zeros(hidden, Hq * D, **bf)
+    O, U = torch.zeros(B, S, Hq, D, **bf), torch.zeros(B, S, hidden, **bf)
+    with pytest.raises(ValueError, match="U: .*at least"):
+        dash.dash_attn_layer(Q, K, V, Wo, O, U[:, :S - 1].contiguous(), torch.zeros(B, S))
+    with pytest.raises(ValueError, match="score: dtype"):
+        dash.dash_attn_layer(Q, K, V, Wo, O, U, torch.zeros(B, S, **bf))
