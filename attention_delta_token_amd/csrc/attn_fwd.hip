@@ -17,8 +17,9 @@
 // bf16 kernel: 256 threads = 4 waves, 128 queries of one q-head per workgroup
 // (32 per wave), 64 keys per step.  Scores are computed transposed,
 // S^T = K · Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one query and
-// 32 of the step's keys: the softmax max and sum stay in registers except for
-// one exchange with the partner half-wave.  The query is pre-scaled into exp2
+// 32 of the step's keys: the softmax max and sum stay in registers, and the
+// partner half-wave's maximum is fetched only on the rare steps where the lazy
+// reference maximum has to move.  The query is pre-scaled into exp2
 // units and the score accumulators start at -m, so P is a bare exp2.  The
 // output is accumulated transposed too, O^T += V^T · P^T, where P^T is fed
 // straight from the score accumulators (rounded to bf16) as the B operand and
@@ -120,7 +121,7 @@ struct TileLoader {
     }
   }
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, unsigned char* tile, uint32_t tile_off) const {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < C::kLoadsPerWave; ++i) {
       const int q = wave + (kAttnThreads / 64) * i;
@@ -223,6 +224,9 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
   float m_run = 0.f;  // reference maximum (exp2 units); score tiles hold S - m_run
+  f32x16 m_neg;       // -m_run in every element: the score MFMAs' initial accumulator
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m_neg[r] = 0.f;
   float l_run = 0.f;
 
   // K operand offsets: row kb*32 + l32, chunk 2*ks + hi (the kb term is an immediate).
@@ -242,19 +246,16 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   }
 
   // S^T - m for one key tile: 2 blocks of 32 keys x this wave's 32 queries; the
-  // accumulators start at -m (m = this lane's reference maximum), so the
-  // softmax numerator is a bare exp2.
-  auto qk = [&](const unsigned char* kst, f32x16 (&s)[2], float init) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = init;
+  // first MFMA of each block takes its accumulator from m_neg (-m, m = this
+  // lane's reference maximum, kept in a register block so no per-step fill is
+  // needed), so the softmax numerator is a bare exp2.
+  auto qk = [&](const unsigned char* kst, f32x16 (&s)[2], const f32x16& init) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + koff[ks] + kb * 32 * C::kRowBytes);
-        s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
+        s[kb] = mfma32x32x16(a, qreg[ks], ks == 0 ? init : s[kb]);
       }
   };
 
@@ -281,12 +282,17 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool grow = first || mx > kLazyLog2;
-    if (__any(grow)) {
+    // The two half-waves hold the same queries' other keys.  Only when some
+    // lane's own half exceeds the slack (or on the first tile) is the full
+    // row maximum needed, so the exchange sits inside the rare branch.
+    if (__any(first || mx > kLazyLog2)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const bool grow = first || mx > kLazyLog2;
       const float delta = grow ? mx : 0.f;
       const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-delta);
       m_run = first ? mx : m_run + delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m_neg[r] = -m_run;
       l_run *= alpha;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -355,7 +361,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // rather than competing for the same issue slots.
     if (j + 1 < j_mask) {  // steady state: tile j+1 fully visible
       __builtin_amdgcn_s_setprio(1);
-      qk(kbuf(j + 1), s_nxt, -m_run);
+      qk(kbuf(j + 1), s_nxt, m_neg);
       __builtin_amdgcn_s_setprio(0);
       softmax(s_cur);
       pv(s_cur, vbuf(j));
@@ -363,7 +369,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     } else {
       if (j + 1 < n_w) {
         __builtin_amdgcn_s_setprio(1);
-        qk(kbuf(j + 1), s_nxt, -m_run);
+        qk(kbuf(j + 1), s_nxt, m_neg);
         __builtin_amdgcn_s_setprio(0);
       }
       if (j < n_w) {
@@ -381,7 +387,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   __builtin_amdgcn_s_barrier();
   f32x16 sa[2], sb[2];
   if (n_w > 0) {
-    qk(kbuf(0), sa, 0.f);
+    qk(kbuf(0), sa, m_neg);
     if (j_mask == 0) mask(sa, 0);
     update_max(sa, true);
   }
