@@ -167,7 +167,9 @@ def main():
     dash.trace_select(("attn_layer", "attn_active"))
     ms = timed(run_marked, args.steps)
     dash.trace_stop()
-    clocks = gpu_clocks()  # read right after the timed steps (context only)
+    # read right after the timed steps (context only); not under a profiler,
+    # whose preloaded library would follow the rocm-smi child process
+    clocks = gpu_clocks() if not args.profile_only else None
     attn_recs = dash.trace_read(cap_attn)
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     cap_all = (8 * w.layers + 8) * args.steps  # every launch group of every layer and step
