@@ -26,7 +26,7 @@ DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE, DASH_OP_DECODE = 0, 1, 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
             "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
             "dash_attn_active", "dash_score", "dash_attn_layer_varlen", "dash_select_ragged",
-            "dash_attn_active_varlen", "dash_decode",
+            "dash_attn_active_varlen", "dash_attn_active_gather", "dash_decode",
             "dash_trace_start", "dash_trace_select", "dash_trace_stop", "dash_trace_read")
 TRACE_OPS = ("attn_layer", "proj_layer", "attn_active", "proj_active", "select", "compact", "score", "decode")
 
@@ -91,6 +91,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]
     lib.dash_attn_active.restype = c_int
+    lib.dash_attn_active_gather.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_int, c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_size_t, c_void_p]
+    lib.dash_attn_active_gather.restype = c_int
     lib.dash_attn_layer_varlen.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_int, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                            c_void_p]
@@ -311,6 +315,41 @@ def dash_attn_active(Qa, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: 
     _check(load().dash_attn_active(None, ctypes.byref(shape), _ptr(Qa), _ptr(q_pos), _ptr(n_dev), n_max, _ptr(K),
                                    _ptr(V), kv_mode, _ptr(Oa), _ptr(Wo), _ptr(Ua), _ptr(score), _ptr(ws),
                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dash_attn_active_gather(Q, q_rows, K, V, kv_mode: int, Oa, q_pos=None, n_dev=None, n_max: int | None = None,
+                            Wo=None, Ua=None, score=None, ws=None, hidden: int | None = None,
+                            stream=None) -> None:
+    """Post-halt attention reading its queries from the full-length Q through
+    q_rows (see include/dash.h).  Q [S,Hq,D] or [B,S,Hq,D]; q_rows [n] or
+    [B, n] (device int32); K, V [n or S, Hkv, D] (or with a leading B)."""
+    if Q.dim() == 4:
+        B, S, Hq, D = Q.shape
+        Hkv = K.shape[2]
+    else:
+        B = 1
+        S, Hq, D = Q.shape
+        Hkv = K.shape[1]
+    n_cap = q_rows.shape[-1]
+    if n_max is None:
+        n_max = n_cap
+    if hidden is None:
+        hidden = Wo.shape[0] if Wo is not None else Hq * D
+    _need(q_rows, B * n_max, torch.int32, "q_rows")
+    kv_rows = S if kv_mode == DASH_KV_ALL else n_max
+    _need(K, B * kv_rows * Hkv * D, Q.dtype, "K")
+    _need(V, B * kv_rows * Hkv * D, Q.dtype, "V")
+    _need(Oa, B * n_max * Hq * D, Q.dtype, "Oa")
+    _need(Wo, hidden * Hq * D, Q.dtype, "Wo")
+    _need(Ua, B * n_max * hidden, Q.dtype, "Ua")
+    _need(score, B * n_max, torch.float32, "score")
+    _need(q_pos, B * n_max, torch.int32, "q_pos")
+    _need(n_dev, 1, torch.int32, "n_dev")
+    shape = make_shape(B, S, Hq, Hkv, D, hidden, _dtype_code(Q))
+    _check(load().dash_attn_active_gather(None, ctypes.byref(shape), _ptr(Q), _ptr(q_rows), _ptr(q_pos),
+                                          _ptr(n_dev), n_max, _ptr(K), _ptr(V), kv_mode, _ptr(Oa), _ptr(Wo),
+                                          _ptr(Ua), _ptr(score), _ptr(ws),
+                                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dash_attn_layer_varlen(Q, K, V, Wo, O, U, cu_seqlens, max_len: int, score=None, ws=None, stream=None) -> None:

@@ -175,6 +175,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = min(qrow, n_q - 1);
+  const int q_src = bt.q_rows ? min(max(bt.q_rows[b * bt.qp_bs + qrow_c], 0), bt.q_rows_n - 1) : qrow_c;
   const int my_pos = q_pos ? q_pos[qrow_c] - pos_base : qrow_c;
   const int w_first = min(q0 + wave * 32, n_q - 1);
   const int w_last = min(q0 + wave * 32 + 31, n_q - 1);
@@ -209,7 +210,7 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // in exp2 units.
   bf16x8 qreg[D / 16];
   {
-    const uint16_t* qp = Q + static_cast<size_t>(qrow_c) * q_ld + h * D + hi * 8;
+    const uint16_t* qp = Q + static_cast<size_t>(q_src) * q_ld + h * D + hi * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const bf16x8 raw = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
@@ -453,13 +454,14 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
   V += static_cast<int64_t>(kvh) * D;
   const int qi = q0 + threadIdx.x;
   const int qc = min(qi, n_q - 1);
+  const int q_src = bt.q_rows ? min(max(bt.q_rows[b * bt.qp_bs + qc], 0), bt.q_rows_n - 1) : qc;
   const int my_pos = q_pos ? q_pos[qc] - pos_base : qc;
   const int last = min(q0 + 63, n_q - 1);
   const int pmax = q_pos ? q_pos[last] - pos_base : last;
   const int kv_end = min(n_kv, pmax + 1);
   float q[D], acc[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) { q[d] = Q[static_cast<size_t>(qc) * q_ld + h * D + d] * scale; acc[d] = 0.f; }
+  for (int d = 0; d < D; ++d) { q[d] = Q[static_cast<size_t>(q_src) * q_ld + h * D + d] * scale; acc[d] = 0.f; }
   float m = -__builtin_inff(), l = 0.f;
   for (int k0 = 0; k0 < kv_end; k0 += 64) {
     __syncthreads();

@@ -571,9 +571,15 @@ int dash_compact_batch(void* /*ctx*/, const int32_t* idx, int B, int k, const da
   return compact_many_impl(idx, nullptr, B * k, items, count, stream, k);
 }
 
-int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const int32_t* q_pos,
-                     const int32_t* n_dev, int n_max, const void* K, const void* V, int kv_mode, void* Oa,
-                     const void* Wo, void* Ua, float* score, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// Post-halt attention (+ optional W_o GEMM and score) on n_max active rows.
+// q_rows == nullptr: Q holds the compacted queries [B, n_max, Hq, D];
+// otherwise Q is the full [B, S, Hq, D] and query r reads row q_rows[b, r].
+int attn_active_impl(void* /*ctx*/, const dash_shape* s, const void* Qa, const int32_t* q_rows,
+                     const int32_t* q_pos, const int32_t* n_dev, int n_max, const void* K, const void* V,
+                     int kv_mode, void* Oa, const void* Wo, void* Ua, float* score, void* ws, size_t ws_bytes,
+                     void* stream) {
   try {
     int rc = check_shape(s, false);
     if (rc) return rc;
@@ -606,10 +612,12 @@ int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const i
     const int64_t kv_rows = kv_mode == DASH_KV_ACTIVE ? n_max : s->S;  // per sample
     int tr = trace_open(DASH_TR_ATTN_ACTIVE, st);
     dash::AttnBatch bt;
-    bt.q_bs = n_max * qd;
+    bt.q_bs = (q_rows ? static_cast<int64_t>(s->S) : n_max) * qd;
     bt.kv_bs = kv_rows * kvd;
     bt.o_bs = n_max * qd;
     bt.qp_bs = n_max;
+    bt.q_rows = q_rows;
+    bt.q_rows_n = s->S;
     hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Qa, K, V, Oa, qp, n_dev, n_max, n_kv, s->Hq,
                                           s->Hkv, bt, st);
     trace_close(tr, st);
@@ -626,6 +634,24 @@ int dash_attn_active(void* /*ctx*/, const dash_shape* s, const void* Qa, const i
   } catch (...) {
     return fail(DASH_E_INVAL, "unexpected host exception");
   }
+}
+
+}  // namespace
+
+int dash_attn_active(void* ctx, const dash_shape* s, const void* Qa, const int32_t* q_pos,
+                     const int32_t* n_dev, int n_max, const void* K, const void* V, int kv_mode, void* Oa,
+                     const void* Wo, void* Ua, float* score, void* ws, size_t ws_bytes, void* stream) {
+  return attn_active_impl(ctx, s, Qa, nullptr, q_pos, n_dev, n_max, K, V, kv_mode, Oa, Wo, Ua, score, ws, ws_bytes,
+                          stream);
+}
+
+int dash_attn_active_gather(void* ctx, const dash_shape* s, const void* Q, const int32_t* q_rows,
+                            const int32_t* q_pos, const int32_t* n_dev, int n_max, const void* K, const void* V,
+                            int kv_mode, void* Oa, const void* Wo, void* Ua, float* score, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!q_rows) return fail(DASH_E_INVAL, "q_rows is NULL");
+  return attn_active_impl(ctx, s, Q, q_rows, q_pos, n_dev, n_max, K, V, kv_mode, Oa, Wo, Ua, score, ws, ws_bytes,
+                          stream);
 }
 
 }  // extern "C"

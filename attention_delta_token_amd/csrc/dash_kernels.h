@@ -15,9 +15,14 @@ namespace dash {
 // rows, so a query's position within its sample is q_pos - cu_kv[b].  In both
 // cases n_kv < 0 makes the key count follow the query count (keys compacted
 // with the queries); a ragged batch otherwise takes it from cu_kv.
+// q_rows (fixed batch only): query r of sample b reads row q_rows[b*qp_bs + r]
+// of that sample's Q (clamped into [0, q_rows_n)) instead of row r, so the
+// queries are gathered on load rather than compacted beforehand.
 struct AttnBatch {
   int64_t q_bs = 0, kv_bs = 0, o_bs = 0;
   int qp_bs = 0;
+  const int32_t* q_rows = nullptr;
+  int q_rows_n = 0;
   const int32_t* cu_q = nullptr;
   const int32_t* cu_kv = nullptr;
   int q_total = 0, kv_total = 0;  // ragged: packed query / key rows; every sample is clamped into them

@@ -64,7 +64,6 @@ class OneShotStack:
         self.U = torch.empty(*lead, S, hidden, device=dev, dtype=dt)
         self.score = torch.empty(*lead, S, device=dev, dtype=torch.float32)
         self.idx = torch.empty(*lead, kk, device=dev, dtype=torch.int32)
-        self.Qa = torch.empty(*lead, kk, Hq, D, device=dev, dtype=dt)
         self.Ka = torch.empty(*lead, kk, Hkv, D, device=dev, dtype=dt)
         self.Va = torch.empty(*lead, kk, Hkv, D, device=dev, dtype=dt)
         self.Oa = torch.empty(*lead, kk, Hq * D, device=dev, dtype=dt)
@@ -86,21 +85,19 @@ class OneShotStack:
         if k == 0:
             return
         batched = x.Q.dim() == 4
+        # The queries are read from the full-length Q through the kept indices
+        # inside the attention kernel; only kv_mode active compacts K and V.
         if self.kv_mode == L.DASH_KV_ACTIVE:
-            pairs = [(x.Q, self.Qa), (x.K, self.Ka), (x.V, self.Va)]
+            pairs = [(x.K, self.Ka), (x.V, self.Va)]
             if batched:
                 L.dash_compact_batch(self.idx, pairs)
             else:
                 L.dash_compact_many(self.idx, pairs, n_max=k)
-            L.dash_attn_active(self.Qa, self.Ka, self.Va, L.DASH_KV_ACTIVE, self.Oa, n_max=k, Wo=x.Wo,
-                               Ua=self.Ua)
+            L.dash_attn_active_gather(x.Q, self.idx, self.Ka, self.Va, L.DASH_KV_ACTIVE, self.Oa, n_max=k,
+                                      Wo=x.Wo, Ua=self.Ua)
         else:
-            if batched:
-                L.dash_compact_batch(self.idx, [(x.Q, self.Qa)])
-            else:
-                L.dash_compact(self.idx, x.Q, self.Qa, n_max=k)
-            L.dash_attn_active(self.Qa, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=self.idx, n_max=k, Wo=x.Wo,
-                               Ua=self.Ua, S=self.S)
+            L.dash_attn_active_gather(x.Q, self.idx, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=self.idx, n_max=k,
+                                      Wo=x.Wo, Ua=self.Ua)
 
     def run(self) -> None:
         for l in range(len(self.layers)):
@@ -260,7 +257,6 @@ class MultiShotStack:
         self.U = torch.empty(S, hidden, device=dev, dtype=dt)
         self.score = torch.empty(S, device=dev, dtype=torch.float32)
         self.pos = [torch.empty(max(k, 1), device=dev, dtype=torch.int32) for _, k in self.schedule]
-        self.Qa = torch.empty(k1, Hq, D, device=dev, dtype=dt)
         self.Ka = torch.empty(k1, Hkv, D, device=dev, dtype=dt)
         self.Va = torch.empty(k1, Hkv, D, device=dev, dtype=dt)
         self.Oa = torch.empty(k1, Hq * D, device=dev, dtype=dt)
@@ -280,13 +276,14 @@ class MultiShotStack:
                 L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.score if decide else None, self.ws)
             elif n > 0:
                 if self.kv_mode == L.DASH_KV_ACTIVE:
-                    L.dash_compact_many(cur, [(x.Q, self.Qa), (x.K, self.Ka), (x.V, self.Va)], n_max=n)
-                    L.dash_attn_active(self.Qa[:n], self.Ka[:n], self.Va[:n], L.DASH_KV_ACTIVE, self.Oa, n_max=n,
-                                       Wo=x.Wo, Ua=self.Ua, score=self.score if decide else None, ws=self.ws)
+                    L.dash_compact_many(cur, [(x.K, self.Ka), (x.V, self.Va)], n_max=n)
+                    L.dash_attn_active_gather(x.Q, cur[:n], self.Ka[:n], self.Va[:n], L.DASH_KV_ACTIVE, self.Oa,
+                                              n_max=n, Wo=x.Wo, Ua=self.Ua, score=self.score if decide else None,
+                                              ws=self.ws)
                 else:
-                    L.dash_compact(cur, x.Q, self.Qa, n_max=n)
-                    L.dash_attn_active(self.Qa[:n], x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=cur, n_max=n, Wo=x.Wo,
-                                       Ua=self.Ua, score=self.score if decide else None, ws=self.ws, S=self.S)
+                    L.dash_attn_active_gather(x.Q, cur[:n], x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=cur, n_max=n,
+                                              Wo=x.Wo, Ua=self.Ua, score=self.score if decide else None,
+                                              ws=self.ws)
             if decide:
                 k = decisions[l]
                 nxt = self.pos[d]
@@ -298,8 +295,9 @@ class MultiShotStack:
 
 class ThresholdStack:
     """Layer 0 full length fixes tau (rank-th smallest score); every layer then
-    updates the counters and compacts the surviving queries; keys and values
-    stay full length (halted tokens keep their K/V)."""
+    updates the counters and runs on the surviving queries (read in place
+    through their positions); keys and values stay full length (halted tokens
+    keep their K/V)."""
 
     def __init__(self, layers: list[LayerTensors], tau_rank: int, patience: int = 2, record: bool = False,
                  record_outputs: bool = True):
@@ -316,7 +314,6 @@ class ThresholdStack:
         self.counters = torch.zeros(S, device=dev, dtype=torch.uint8)
         self.pos = [torch.empty(S, device=dev, dtype=torch.int32) for _ in range(2)]
         self.n = torch.zeros(2, 4, device=dev, dtype=torch.int32)
-        self.Qa = torch.empty(S, Hq, D, device=dev, dtype=dt)
         self.Oa = torch.empty(S, Hq * D, device=dev, dtype=dt)
         dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
         self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
@@ -338,9 +335,8 @@ class ThresholdStack:
         for l in range(1, len(self.layers)):
             x = self.layers[l]
             pos, n = self.pos[cur], self.n[cur]
-            L.dash_compact(pos, x.Q, self.Qa, n_dev=n, n_max=S)
-            L.dash_attn_active(self.Qa, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=pos, n_dev=n, n_max=S, Wo=x.Wo,
-                               Ua=self.U, score=self.score, ws=self.ws, S=S)
+            L.dash_attn_active_gather(x.Q, pos, x.K, x.V, L.DASH_KV_ALL, self.Oa, q_pos=pos, n_dev=n, n_max=S,
+                                      Wo=x.Wo, Ua=self.U, score=self.score, ws=self.ws)
             if self.record:
                 if self.record_outputs:
                     self.trace.append((pos.clone(), n.clone(), self.score.clone(), self.U.clone()))

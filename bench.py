@@ -4,8 +4,9 @@
 One step = one pass of the whole path over one synthetic sequence.  Default
 workload (Qwen2.5-7B shapes, S=8192, bf16): the halting layer at full length
 (causal GQA attention + W_o GEMM with the fused Δattn score), top-k selection
-(keep 0.5), compaction of the next layer's Q/K/V at the kept positions, and the
-post-halt layer on the kept rows (attention + W_o, kv active).  `--config`
+(keep 0.5), compaction of the next layer's K/V at the kept positions, and the
+post-halt layer on the kept rows (attention reading its queries through the
+kept indices + W_o, kv active).  `--config`
 selects the other workloads: 0 = S=512 fp32; 2 = S=32768, 28 layers, halt at
 layer 11; 3 = S=65536 Llama-3.1-8B shapes, 32 layers, threshold halting with
 full K/V; 4 = S=131072, 28 layers, clustered salience, keep 0.3.
@@ -236,20 +237,23 @@ def main():
     proj_flops_total = steps_traced * (n_full * proj_full + sum(proj_post_list))
     proj_tflops = proj_flops_total / ((sum(t_pl) + sum(t_pa)) * 1e-3) / 1e12 if (t_pl or t_pa) else None
     esz = 2 if w.dtype == "bf16" else 4
-    # select: 4 B per score read + 4 B per kept index (top-k); compaction: 2*row bytes + 4 B index per kept row
+    # select: 4 B per score read + 4 B per kept index (top-k); compaction: 2*row bytes + 4 B index per kept row.
+    # The post-halt attention reads its queries through the kept indices, so only kv_mode active compacts
+    # (K and V, in one launch); threshold mode (kv all) compacts nothing.
     if w.mode == "threshold":
         # order statistic: 4 B per layer-0 score; threshold step per active row: score 4 B + position 4 B
         # + counter read/write 2 B + surviving position 4 B
         sel_bytes_step = 4.0 * S + sum(14.0 * k for k in [S] + k_rows)
         n_sel_step = 2 + len(k_rows)
-        cmp_bytes_step = sum(k * (2 * esz * Hq * D + 4) for k in k_rows)
-        n_cmp_step = len(k_rows)
+        cmp_bytes_step, n_cmp_step = 0.0, 0
     else:
         sel_bytes_step = 4.0 * S + 4.0 * w.k
         n_sel_step = 1
-        # one launch gathers Q, K and V (kv active) at the kept rows, reading each index once
-        cmp_bytes_step = sum(k * (2 * esz * (Hq * D + 2 * Hkv * D) + 4) for k in k_rows)
-        n_cmp_step = len(k_rows)
+        if w.kv_mode == "active":
+            cmp_bytes_step = sum(k * (2 * esz * 2 * Hkv * D + 4) for k in k_rows)
+            n_cmp_step = len(k_rows)
+        else:
+            cmp_bytes_step, n_cmp_step = 0.0, 0
     t_sel, t_cmp = by.get("select", []), by.get("compact", [])
     sel_gbps = (steps_traced * sel_bytes_step) / (sum(t_sel) * 1e-3) / 1e9 if t_sel else None
     cmp_gbps = (steps_traced * cmp_bytes_step) / (sum(t_cmp) * 1e-3) / 1e9 if t_cmp else None

@@ -266,6 +266,22 @@ int dash_attn_active(void* ctx, const dash_shape* s, const void* Qa, const int32
                      void* Oa, const void* Wo, void* Ua, float* score,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* a4 folded into a5 (the pages ask for gathers without needless tensor
+ * copies: [P1] §3.3 closing note, §5.2 troubleshooting table): as
+ * dash_attn_active, but the queries are not
+ * compacted beforehand.  Q is the layer's full [B, S, Hq, D] (S = s->S) and
+ * active query i of sample b is read from row q_rows[b * n_max + i] of that
+ * sample (DEVICE int32 [B, n_max], values in [0, S); values outside are
+ * clamped into it).  With DASH_KV_ALL, q_rows is normally q_pos itself; with
+ * DASH_KV_ACTIVE only K and V need compacting (q_pos may be NULL).  Results
+ * are identical to compacting Q at q_rows and calling dash_attn_active.
+ * Errors and workspace as for dash_attn_active; DASH_E_INVAL if q_rows is
+ * NULL. */
+int dash_attn_active_gather(void* ctx, const dash_shape* s, const void* Q, const int32_t* q_rows,
+                            const int32_t* q_pos, const int32_t* n_dev, int n_max, const void* K,
+                            const void* V, int kv_mode, void* Oa, const void* Wo, void* Ua, float* score,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Launch tracing (measurement support, not on the hot path).
  * dash_trace_start(capacity) creates 2*capacity HIP events on the current
  * device and starts recording: every kernel group the library enqueues is

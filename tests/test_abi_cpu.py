@@ -226,6 +226,27 @@ def test_attn_active_validation(lib):
     assert call(s, args(n_max=0, Qa=None)) == L.DASH_OK
 
 
+def test_attn_active_gather_validation(lib):
+    """The gather variant rejects a missing q_rows and otherwise validates like
+    dash_attn_active (all before any launch)."""
+    f = lib.dash_attn_active_gather
+    s = _shape()
+    args = lambda **kw: dict(dict(Q=FAKE, q_rows=FAKE, q_pos=None, n_dev=None, n_max=32, K=FAKE, V=FAKE,
+                                  mode=L.DASH_KV_ACTIVE, Oa=FAKE, Wo=None, Ua=None, score=None, ws=None, wsb=0), **kw)
+    call = lambda shape, a: f(None, ctypes.byref(shape), a["Q"], a["q_rows"], a["q_pos"], a["n_dev"], a["n_max"],
+                               a["K"], a["V"], a["mode"], a["Oa"], a["Wo"], a["Ua"], a["score"], a["ws"], a["wsb"],
+                               None)
+    assert call(s, args(q_rows=None)) == L.DASH_E_INVAL
+    assert "q_rows" in _last(lib)
+    assert call(_shape(B=2), args(n_dev=FAKE)) == L.DASH_E_SHAPE
+    assert call(s, args(n_max=65)) == L.DASH_E_INVAL
+    assert call(s, args(mode=L.DASH_KV_ALL)) == L.DASH_E_INVAL
+    assert "q_pos" in _last(lib)
+    assert call(s, args(Wo=FAKE, Ua=FAKE, score=FAKE)) == L.DASH_E_WORKSPACE
+    assert call(s, args(Q=FAKE + 4)) == L.DASH_E_ALIGN
+    assert call(s, args(n_max=0, Q=None)) == L.DASH_OK
+
+
 def test_workspace_size(lib):
     s = _shape(hidden=3584, S=8192, Hq=28, Hkv=4)
     n = lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(s), 8192)

@@ -407,6 +407,66 @@ def test_attn_active(dash, dtype, mode, device_n):
     assert np.all(host(Oa)[n:] == 0) and np.all(host(Ua)[n:] == 0)
 
 
+@pytest.mark.parametrize("B,device_n", [(1, False), (1, True), (3, False)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["active", "all"])
+def test_attn_active_gather_matches_compacted(dash, dtype, mode, B, device_n):
+    """Queries read through q_rows inside the kernel give exactly what
+    compacting Q first and calling dash_attn_active gives (same kernels, same
+    inputs): O, U and score bit for bit; rows past the device count untouched.
+    In kv-active mode q_rows also carries two out-of-range entries, which read
+    the clamped rows."""
+    S, Hq, Hkv, D, hidden = 700, 8, 2, (128 if dtype == "bf16" else 64), 256
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xs = [_layer(S, Hq, Hkv, D, hidden, seed=21 + b, dtype=dtype) for b in range(B)]
+    k = 333
+    idx = np.stack([np.sort(np.random.default_rng(40 + b).choice(S, k, replace=False)) for b in range(B)])
+    idx = idx.astype(np.int32)
+    rows = idx.copy()
+    if mode == "active":
+        rows[0, 5], rows[-1, -1] = -3, S + 7  # clamped to 0 and S - 1
+    n = 250 if device_n else k
+    say("attn_active_gather", dtype, mode, "B", B, "device_n", device_n)
+    Qfull = dev_t(np.stack([x["Q"] for x in xs]), tdt)
+    Qa = dev_t(np.stack([x["Q"][np.clip(rows[b], 0, S - 1)] for b, x in enumerate(xs)]), tdt)
+    if mode == "active":
+        K = dev_t(np.stack([x["K"][idx[b]] for b, x in enumerate(xs)]), tdt)
+        V = dev_t(np.stack([x["V"][idx[b]] for b, x in enumerate(xs)]), tdt)
+    else:
+        K = dev_t(np.stack([x["K"] for x in xs]), tdt)
+        V = dev_t(np.stack([x["V"] for x in xs]), tdt)
+    Wo = dev_t(xs[0]["Wo"].T, tdt)
+    if B == 1:
+        Qfull, Qa, K, V = Qfull[0], Qa[0], K[0], V[0]
+    lead = (B,) if B > 1 else ()
+    dc = dash.DASH_BF16 if dtype == "bf16" else dash.DASH_F32
+    ws = dash.workspace(dash.DASH_OP_ATTN_ACTIVE, dash.make_shape(B, S, Hq, Hkv, D, hidden, dc), k)
+    km = dash.DASH_KV_ACTIVE if mode == "active" else dash.DASH_KV_ALL
+    q_pos = torch.from_numpy(idx if B > 1 else idx[0]).cuda()
+    q_rows = torch.from_numpy(rows if B > 1 else rows[0]).cuda()
+    nd = torch.tensor([n, 0, 0, 0], dtype=torch.int32, device="cuda") if device_n else None
+    outs = []
+    for gather in (False, True):
+        Oa = torch.zeros(*lead, k, Hq * D, device="cuda", dtype=tdt)
+        Ua = torch.zeros(*lead, k, hidden, device="cuda", dtype=tdt)
+        sc = torch.zeros(*lead, k, device="cuda", dtype=torch.float32)
+        qp = q_pos if mode == "all" else None
+        if gather:
+            dash.dash_attn_active_gather(Qfull, q_rows, K, V, km, Oa, q_pos=qp, n_dev=nd, n_max=k, Wo=Wo, Ua=Ua,
+                                         score=sc, ws=ws)
+        else:
+            dash.dash_attn_active(Qa, K, V, km, Oa, q_pos=qp, n_dev=nd, n_max=k, Wo=Wo, Ua=Ua, score=sc, ws=ws,
+                                  S=S if mode == "all" else None)
+        torch.cuda.synchronize()
+        outs.append((Oa, Ua, sc))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    Oa, Ua, _ = outs[1]
+    flat_O = Oa.reshape(-1, k, Hq * D)
+    assert torch.count_nonzero(flat_O[:, :n]) > 0
+    assert torch.count_nonzero(flat_O[:, n:]) == 0 and torch.count_nonzero(Ua.reshape(-1, k, hidden)[:, n:]) == 0
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode", ["active", "all"])
 def test_attn_active_batched(dash, dtype, mode):
