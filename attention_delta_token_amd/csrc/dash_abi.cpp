@@ -587,7 +587,7 @@ int attn_active_impl(void* /*ctx*/, const dash_shape* s, const void* Qa, const i
     if (kv_mode != DASH_KV_ACTIVE && kv_mode != DASH_KV_ALL) return fail(DASH_E_INVAL, "kv_mode %d unknown", kv_mode);
     if (n_max < 0 || n_max > s->S) return fail(DASH_E_INVAL, "n_max %d outside [0, S=%d]", n_max, s->S);
     if (n_max == 0) return DASH_OK;
-    rc = check_ptrs({{Qa, "Qa"}, {K, "K"}, {V, "V"}, {Oa, "Oa"}});
+    rc = check_ptrs({{Qa, q_rows ? "Q" : "Qa"}, {K, "K"}, {V, "V"}, {Oa, "Oa"}});
     if (rc) return rc;
     if (kv_mode == DASH_KV_ALL && !q_pos) return fail(DASH_E_INVAL, "kv_mode ALL needs q_pos");
     if (Wo) {

@@ -244,6 +244,8 @@ def test_attn_active_gather_validation(lib):
     assert "q_pos" in _last(lib)
     assert call(s, args(Wo=FAKE, Ua=FAKE, score=FAKE)) == L.DASH_E_WORKSPACE
     assert call(s, args(Q=FAKE + 4)) == L.DASH_E_ALIGN
+    assert call(s, args(Q=None)) == L.DASH_E_INVAL
+    assert "Q is NULL" in _last(lib)
     assert call(s, args(n_max=0, Q=None)) == L.DASH_OK
 
 
