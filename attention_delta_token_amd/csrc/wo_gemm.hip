@@ -50,6 +50,18 @@ __device__ __forceinline__ int gemm_slot(int row, int chunk) {
   return chunk ^ ((row / kRowsPerLine) % kRowChunks);
 }
 
+// Buffer resource over `bytes` bytes from `base` (capped at the 32-bit range,
+// which always covers one tile's rows): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, int64_t bytes) {
+  const int n = static_cast<int>(bytes > 0xffffffffll ? 0xffffffffll : (bytes < 0 ? 0 : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n, 0x00020000);
+}
+
+// Global->LDS loads of one stage through buffer loads: the A and W tiles get a
+// buffer resource each, starting at the tile's first row, so a lane's byte
+// offset (row, swizzled chunk) is fixed and the k step rides in the scalar
+// offset; rows past the matrix edge read zeros (their results are never
+// stored).  The wave index is made uniform so the LDS destinations stay scalar.
 template <int BN>
 struct GemmLoadPlan {
   static constexpr int kWBytes = BN * kRowBytes;
@@ -57,29 +69,33 @@ struct GemmLoadPlan {
   static constexpr int kChunks = kStage / 1024;                              // 1 KiB per wave-wide load
   static constexpr int kPerWave = (kChunks + kGemmThreads / 64 - 1) / (kGemmThreads / 64);
   static_assert(kStage % 1024 == 0, "whole KiB per stage");
-  const uint16_t* src[kPerWave];  // row start + swizzled chunk, at k = 0
+  __amdgpu_buffer_rsrc_t a_src, w_src;
+  uint32_t voff[kPerWave];  // this lane's row and swizzled chunk, at k = 0
   __device__ __forceinline__ void init(const uint16_t* A, const uint16_t* W, int m0, int n0, int M, int N, int K) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     constexpr int kRowsPerKiB = 1024 / kRowBytes;
+    a_src = gemm_rsrc(A + static_cast<size_t>(m0) * K, static_cast<int64_t>(M - m0) * K * 2);
+    w_src = gemm_rsrc(W + static_cast<size_t>(n0) * K, static_cast<int64_t>(N - n0) * K * 2);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int q = min(wave + 8 * i, kChunks - 1);  // 1 KiB chunk of the stage
       const int is_a = q < kATileBytes / 1024;
       const int local_row = (is_a ? q : q - kATileBytes / 1024) * kRowsPerKiB + lane / kRowChunks;
       const int chunk = gemm_slot(local_row, lane % kRowChunks);
-      // rows past the matrix edge re-read the last row (their results are never stored)
-      const int grow = is_a ? min(m0 + local_row, M - 1) : min(n0 + local_row, N - 1);
-      src[i] = (is_a ? A : W) + static_cast<size_t>(grow) * K + chunk * 8;
+      voff[i] = static_cast<uint32_t>(local_row) * static_cast<uint32_t>(K) * 2u + chunk * 16;
     }
   }
   __device__ __forceinline__ void issue(unsigned char* stage, int k0) const {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int q = wave + 8 * i;
-      if (kChunks % 8 == 0 || q < kChunks)  // wave-uniform
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + k0),
-                                         (__attribute__((address_space(3))) void*)(stage + q * 1024), 16, 0, 0);
+      // A chunks are q < 32 = 4 per wave: load i of every wave is an A chunk iff i < 4
+      static_assert((kATileBytes / 1024) % 8 == 0, "A chunks split evenly over the waves");
+      if (8 * (i + 1) <= kChunks || q < kChunks)  // only the last load can be missing (wave-uniform)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < kATileBytes / 1024 / 8 ? a_src : w_src,
+                                                 (__attribute__((address_space(3))) void*)(stage + q * 1024), 16,
+                                                 voff[i], k0 * 2, 0, 0);
     }
   }
 };
