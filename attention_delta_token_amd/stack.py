@@ -1,8 +1,11 @@
-"""Drivers that chain the four C-ABI calls into the DASH prefill stacks.
+"""Drivers that chain the C-ABI calls into the DASH prefill stacks.
 
 Only orchestration lives here (which call, on which buffers, in which
 order); every step runs inside libdash.so.  Buffers are allocated once, up
 front, so a step enqueues kernels only and never synchronises with the host.
+Post-halt layers read their queries from the full-length Q through the kept
+positions (dash_attn_active_gather); only a pruned KV cache (kv_mode active)
+is compacted.
 
 * One-shot policy (single-shot halting): layers 0..hl run at full length, the
   score of layer hl picks the k tokens to keep once, and layers hl+1..L-1 run
