@@ -407,16 +407,19 @@ def test_attn_active(dash, dtype, mode, device_n):
     assert np.all(host(Oa)[n:] == 0) and np.all(host(Ua)[n:] == 0)
 
 
-@pytest.mark.parametrize("B,device_n", [(1, False), (1, True), (3, False)])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,device_n,heads", [(1, False, (8, 2)), (1, True, (8, 2)), (3, False, (8, 2)),
+                                               (1, False, (6, 6))])
+@pytest.mark.parametrize("dtype", ["bf16", "bf16-d64", "f32"])
 @pytest.mark.parametrize("mode", ["active", "all"])
-def test_attn_active_gather_matches_compacted(dash, dtype, mode, B, device_n):
+def test_attn_active_gather_matches_compacted(dash, dtype, mode, B, device_n, heads):
     """Queries read through q_rows inside the kernel give exactly what
     compacting Q first and calling dash_attn_active gives (same kernels, same
     inputs): O, U and score bit for bit; rows past the device count untouched.
     In kv-active mode q_rows also carries two out-of-range entries, which read
     the clamped rows."""
-    S, Hq, Hkv, D, hidden = 700, 8, 2, (128 if dtype == "bf16" else 64), 256
+    (Hq, Hkv), D, hidden = heads, (128 if dtype == "bf16" else 64), 256
+    S = 700
+    dtype = "bf16" if dtype == "bf16-d64" else dtype
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     xs = [_layer(S, Hq, Hkv, D, hidden, seed=21 + b, dtype=dtype) for b in range(B)]
     k = 333
@@ -426,7 +429,7 @@ def test_attn_active_gather_matches_compacted(dash, dtype, mode, B, device_n):
     if mode == "active":
         rows[0, 5], rows[-1, -1] = -3, S + 7  # clamped to 0 and S - 1
     n = 250 if device_n else k
-    say("attn_active_gather", dtype, mode, "B", B, "device_n", device_n)
+    say("attn_active_gather", dtype, D, mode, "B", B, "device_n", device_n, "heads", heads)
     Qfull = dev_t(np.stack([x["Q"] for x in xs]), tdt)
     Qa = dev_t(np.stack([x["Q"][np.clip(rows[b], 0, S - 1)] for b, x in enumerate(xs)]), tdt)
     if mode == "active":
