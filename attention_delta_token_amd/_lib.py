@@ -8,7 +8,6 @@ is raised.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from ctypes import POINTER, Structure, c_char_p, c_int, c_size_t, c_void_p
 
@@ -23,7 +22,8 @@ DASH_KV_ACTIVE, DASH_KV_ALL = 0, 1
 DASH_SEL_TOPK, DASH_SEL_THRESHOLD, DASH_SEL_ORDER_STAT = 0, 1, 2
 DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE, DASH_OP_DECODE = 0, 1, 2, 3
 
-EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_workspace_size",
+EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_keep_count",
+            "dash_percentile_rank", "dash_workspace_size",
             "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
             "dash_attn_active", "dash_score", "dash_attn_layer_varlen", "dash_select_ragged",
             "dash_attn_active_varlen", "dash_attn_active_gather", "dash_decode",
@@ -42,7 +42,7 @@ class DashGather(Structure):
 
 class DashSel(Structure):
     _fields_ = [("mode", c_int), ("k", c_int), ("rank", c_int), ("tau", c_void_p), ("patience", c_int),
-                ("counters", c_void_p), ("keep_first", c_int), ("keep_last", c_int)]
+                ("counters", c_void_p), ("keep_first", c_int), ("keep_last", c_int), ("n_counters", c_int)]
 
 
 class DashError(RuntimeError):
@@ -70,6 +70,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_last_error.restype = c_char_p
     lib.dash_version.argtypes = []
     lib.dash_version.restype = c_char_p
+    lib.dash_keep_count.argtypes = [c_int, ctypes.c_double, c_int, c_int, POINTER(c_int)]
+    lib.dash_keep_count.restype = c_int
+    lib.dash_percentile_rank.argtypes = [c_int, c_int, POINTER(c_int)]
+    lib.dash_percentile_rank.restype = c_int
     lib.dash_workspace_size.argtypes = [c_void_p, c_int, POINTER(DashShape), c_int]
     lib.dash_workspace_size.restype = c_size_t
     lib.dash_attn_layer.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_void_p,
@@ -207,9 +211,12 @@ def dash_attn_layer(Q, K, V, Wo, O, U, score=None, ws=None, stream=None) -> None
 
 def dash_select(score, idx=None, *, mode: int = DASH_SEL_TOPK, k: int = 0, rank: int = 0, tau=None,
                 patience: int = 2, counters=None, pos=None, n_dev=None, n_max: int | None = None, rows: int = 1,
-                n_out=None, tau_out=None, keep_first: int = 0, keep_last: int = 0, stream=None) -> None:
+                n_out=None, tau_out=None, keep_first: int = 0, keep_last: int = 0, status=None,
+                stream=None) -> None:
     """Top-k / order statistic / threshold step (see include/dash.h).  For top-k
-    with forced retention, k is the total kept count (see effective_keep)."""
+    with forced retention, k is the total kept count (see keep_count).
+    status: optional int32 device tensor of at least `rows` entries that
+    receives each row's number of NaN scores (the call's workspace)."""
     if n_max is None:
         n_max = score.shape[-1] if score is not None else 0
     _need(score, rows * n_max, torch.float32, "score")
@@ -221,17 +228,32 @@ def dash_select(score, idx=None, *, mode: int = DASH_SEL_TOPK, k: int = 0, rank:
     _need(n_out, 1, torch.int32, "n_out")
     _need(tau, 1, torch.float32, "tau")
     _need(tau_out, 1, torch.float32, "tau_out")
-    sel = DashSel(mode, k, rank, _ptr(tau), patience, _ptr(counters), keep_first, keep_last)
+    _need(status, rows, torch.int32, "status")
+    n_counters = counters.numel() if counters is not None else 0
+    sel = DashSel(mode, k, rank, _ptr(tau), patience, _ptr(counters), keep_first, keep_last, n_counters)
+    ws_bytes = status.numel() * status.element_size() if status is not None else 0
     _check(load().dash_select(None, ctypes.byref(sel), _ptr(score), _ptr(pos), _ptr(n_dev), n_max, rows,
-                              _ptr(idx), _ptr(n_out), _ptr(tau_out), None, 0, _stream(stream)))
+                              _ptr(idx), _ptr(n_out), _ptr(tau_out), _ptr(status), ws_bytes, _stream(stream)))
 
 
-def effective_keep(T: int, keep: float, keep_first: int = 0, keep_last: int = 0) -> int:
-    """Kept count with forced retention: keep_first + keep_last plus floor(keep *
-    (T - keep_first - keep_last)) chosen by score (keep = 1 - pruning ratio)."""
-    if keep_first < 0 or keep_last < 0 or keep_first + keep_last > T:
-        raise ValueError("keep_first + keep_last must lie in [0, T]")
-    return keep_first + keep_last + int(math.floor(keep * (T - keep_first - keep_last)))
+def select_status(rows: int = 1, device="cuda") -> torch.Tensor:
+    """An int32 device buffer for dash_select's NaN counts (one word per row)."""
+    n = dash_workspace_size(DASH_OP_SELECT, make_shape(rows, 1, 1, 1, 1, 1, DASH_F32), 0)
+    return torch.zeros(max(n, 256) // 4, dtype=torch.int32, device=device)
+
+
+def keep_count(T: int, keep: float, keep_first: int = 0, keep_last: int = 0) -> int:
+    """Kept count of the one-shot policy, K_eff (dash_keep_count)."""
+    out = c_int(0)
+    _check(load().dash_keep_count(T, float(keep), keep_first, keep_last, ctypes.byref(out)))
+    return out.value
+
+
+def percentile_rank(n: int, pct: int) -> int:
+    """Rank of the nearest-rank pct-th percentile among n scores (dash_percentile_rank)."""
+    out = c_int(0)
+    _check(load().dash_percentile_rank(n, pct, ctypes.byref(out)))
+    return out.value
 
 
 def dash_compact(idx, X, Xa, n_dev=None, n_max: int | None = None, stream=None) -> None:

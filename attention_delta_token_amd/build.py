@@ -1,6 +1,13 @@
 """Build the DASH HIP library (libdash.so) in-tree for gfx950 with hipcc.
 
     python -m attention_delta_token_amd.build        # or: python attention_delta_token_amd/build.py
+    python -m attention_delta_token_amd.build --host-asan
+
+The second form builds _build/libdash_host_asan.so: the same sources with the
+host code (argument validation, workspace sizing, dispatch) instrumented by
+AddressSanitizer and UndefinedBehaviorSanitizer; device code is built as
+usual.  It is for running the CPU tests of the C ABI (see tests/conftest.py:
+DASH_TEST_LIB), never for the GPU.
 """
 from __future__ import annotations
 
@@ -39,15 +46,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdash.so)")
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+ASAN_LIB = os.path.join(os.path.dirname(HERE), "_build", "libdash_host_asan.so")
+
+
+def build(verbose: bool = False, jobs: int = 8, host_asan: bool = False) -> str:
     cc = hipcc()
+    out_lib = ASAN_LIB if host_asan else LIB
+    extra_all = HOST_SANITIZE if host_asan else []
+    os.makedirs(os.path.dirname(out_lib), exist_ok=True)
     tmp = tempfile.mkdtemp(prefix="dash_build_")
     try:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIPCC_FLAGS, *extra_all, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -65,14 +81,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 print(text)
         if failed:
             raise RuntimeError(f"hipcc failed on {failed}")
-        tmp_lib = LIB + ".tmp"
-        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp_lib]
+        tmp_lib = out_lib + ".tmp"
+        link_san = ["-shared-libsan", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"] \
+            if host_asan else []
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *link_san, *objs, "-o", tmp_lib]
         subprocess.run(cmd, check=True)
-        os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, out_lib)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out_lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_asan="--host-asan" in sys.argv))

@@ -4,6 +4,7 @@
 // enqueue nothing (and can be exercised without a GPU).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -55,6 +56,11 @@ int check_shape(const dash_shape* s, bool need_b1) {
   if (s->S > (1 << 24)) return fail(DASH_E_SHAPE, "S above 2^24 unsupported");
   if (static_cast<int64_t>(s->B) * s->S > (1ll << 26)) return fail(DASH_E_SHAPE, "B*S above 2^26 unsupported");
   if (s->Hq > 1024 || s->D > 1024 || s->hidden > (1 << 20)) return fail(DASH_E_SHAPE, "head count or width too large");
+  // the attention kernels address one sample's K and V with 32-bit buffer offsets
+  const int64_t esz = s->dtype == DASH_BF16 ? 2 : 4;
+  if (static_cast<int64_t>(s->S) * s->Hkv * s->D * esz >= (1ll << 32))
+    return fail(DASH_E_SHAPE, "one sample's K (S * Hkv * D * element size = %lld bytes) must stay below 4 GiB",
+                static_cast<long long>(static_cast<int64_t>(s->S) * s->Hkv * s->D * esz));
   if (s->dtype == DASH_BF16) {
     if (s->D != 64 && s->D != 128) return fail(DASH_E_SHAPE, "bf16 path supports D in {64, 128}, got %d", s->D);
     if (s->hidden % 8 != 0) return fail(DASH_E_SHAPE, "bf16 path needs hidden %% 8 == 0, got %d", s->hidden);
@@ -107,6 +113,29 @@ int trace_open(int op, hipStream_t st) {
 
 void trace_close(int slot, hipStream_t st) {
   if (slot >= 0) (void)hipEventRecord(g_tr_ev[2 * slot + 1], st);
+}
+
+// a1 + a2 on validated arguments; part holds the Σu² partials (score != NULL).
+int attn_layer_launch(const dash_shape* s, const void* Q, const void* K, const void* V, const void* Wo, void* O,
+                      void* U, float* score, float* part, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(s->B) * s->S;
+  const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
+  const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
+  int tr = trace_open(DASH_TR_ATTN_LAYER, st);
+  dash::AttnBatch bt;
+  bt.q_bs = s->S * qd;
+  bt.kv_bs = s->S * kvd;
+  bt.o_bs = s->S * qd;
+  hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Q, K, V, O, nullptr, nullptr, s->S, s->S, s->Hq,
+                                        s->Hkv, bt, st);
+  trace_close(tr, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  tr = trace_open(DASH_TR_PROJ_LAYER, st);
+  e = dash::launch_wo_gemm(s->dtype, O, Wo, U, score, part, nullptr, static_cast<int>(rows), s->hidden,
+                           static_cast<int>(qd), st);
+  trace_close(tr, st);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return DASH_OK;
 }
 
 }  // namespace
@@ -172,7 +201,29 @@ int dash_trace_read(int* ops, float* ms, int max, int* n) {
 
 const char* dash_last_error(void) { return g_last_error.c_str(); }
 
-const char* dash_version(void) { return "dash-mi355x 0.1.0 (gfx950)"; }
+const char* dash_version(void) { return "dash-mi355x 0.2.0 (gfx950)"; }
+
+int dash_keep_count(int T, double keep, int keep_first, int keep_last, int* k_out) {
+  if (!k_out) return fail(DASH_E_INVAL, "k_out is NULL");
+  if (T < 0) return fail(DASH_E_INVAL, "T = %d must be >= 0", T);
+  if (!(keep >= 0.0 && keep <= 1.0)) return fail(DASH_E_INVAL, "keep ratio %g outside [0, 1]", keep);
+  if (keep_first < 0 || keep_last < 0 || static_cast<int64_t>(keep_first) + keep_last > T)
+    return fail(DASH_E_INVAL, "forced counts keep_first %d + keep_last %d must lie in [0, T = %d]", keep_first,
+                keep_last, T);
+  const int rest = T - keep_first - keep_last;
+  const int chosen = static_cast<int>(std::floor(keep * static_cast<double>(rest)));
+  *k_out = keep_first + keep_last + (chosen < rest ? chosen : rest);
+  return DASH_OK;
+}
+
+int dash_percentile_rank(int n, int pct, int* rank_out) {
+  if (!rank_out) return fail(DASH_E_INVAL, "rank_out is NULL");
+  if (n < 1) return fail(DASH_E_INVAL, "n = %d must be >= 1", n);
+  if (pct < 0 || pct > 100) return fail(DASH_E_INVAL, "percentile %d outside [0, 100]", pct);
+  const int64_t r = (static_cast<int64_t>(pct) * n + 99) / 100;  // ceil(pct * n / 100)
+  *rank_out = r < 1 ? 1 : static_cast<int>(r);
+  return DASH_OK;
+}
 
 int dash_create(void** ctx, int device) {
   try {
@@ -203,8 +254,9 @@ size_t dash_workspace_size(void* /*ctx*/, int op, const dash_shape* s, int n_max
       case DASH_OP_ATTN_ACTIVE:
         if (check_shape(s, false) != DASH_OK || n_max < 0) return 0;
         return score_ws_bytes(s, static_cast<int64_t>(s->B) * n_max);
-      case DASH_OP_SELECT:
-        return 0;  // selection keeps its state in LDS
+      case DASH_OP_SELECT:  // one int32 NaN count per row (the selection state itself lives in LDS)
+        if (!s || s->B < 1 || s->B > (1 << 20)) return 0;
+        return align_up(static_cast<size_t>(s->B) * sizeof(int32_t));
       case DASH_OP_DECODE:
         if (check_shape(s, false) != DASH_OK || n_max < 1) return 0;
         return align_up(dash::decode_workspace_bytes(s->B, s->S, s->Hkv, s->D));
@@ -230,38 +282,29 @@ int dash_attn_layer(void* /*ctx*/, const dash_shape* s, const void* Q, const voi
       if (!ws || ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
       if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
     }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t qd = static_cast<int64_t>(s->Hq) * s->D;
-    const int64_t kvd = static_cast<int64_t>(s->Hkv) * s->D;
-    int tr = trace_open(DASH_TR_ATTN_LAYER, st);
-    dash::AttnBatch bt;
-    bt.q_bs = s->S * qd;
-    bt.kv_bs = s->S * kvd;
-    bt.o_bs = s->S * qd;
-    hipError_t e = dash::launch_attention(s->dtype, s->B, s->D, Q, K, V, O, nullptr, nullptr, s->S, s->S, s->Hq,
-                                          s->Hkv, bt, st);
-    trace_close(tr, st);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
-    tr = trace_open(DASH_TR_PROJ_LAYER, st);
-    e = dash::launch_wo_gemm(s->dtype, O, Wo, U, score, static_cast<float*>(ws), nullptr, static_cast<int>(rows),
-                             s->hidden, static_cast<int>(qd), st);
-    trace_close(tr, st);
-    if (e != hipSuccess) return hip_fail(e, "projection launch");
-    return DASH_OK;
+    return attn_layer_launch(s, Q, K, V, Wo, O, U, score, static_cast<float*>(ws), static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(DASH_E_INVAL, "unexpected host exception");
   }
 }
 
 int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int32_t* pos, const int32_t* n_dev,
-                int n_max, int rows, int32_t* idx, int32_t* n_out_dev, float* tau_out, void* /*ws*/,
-                size_t /*ws_bytes*/, void* stream) {
+                int n_max, int rows, int32_t* idx, int32_t* n_out_dev, float* tau_out, void* ws, size_t ws_bytes,
+                void* stream) {
   try {
     if (!p) return fail(DASH_E_INVAL, "selection parameters are NULL");
     if (p->mode != DASH_SEL_TOPK && (p->keep_first != 0 || p->keep_last != 0))
       return fail(DASH_E_INVAL, "keep_first / keep_last apply to top-k only and must be 0 here");
     if (n_max < 0 || n_max > (1 << 30)) return fail(DASH_E_INVAL, "n_max %d out of range", n_max);
     if (rows < 1 || rows > (1 << 20)) return fail(DASH_E_INVAL, "rows %d out of range", rows);
+    // NaN status: one int32 per row in the workspace, when one is given
+    int32_t* nan_out = nullptr;
+    if (ws) {
+      const size_t need = align_up(static_cast<size_t>(rows) * sizeof(int32_t));
+      if (ws_bytes < need) return fail(DASH_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+      if (!aligned4(ws)) return fail(DASH_E_ALIGN, "workspace is not 4-byte aligned");
+      nan_out = static_cast<int32_t*>(ws);
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     int tr = -1;
@@ -272,15 +315,18 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
             static_cast<int64_t>(p->keep_first) + p->keep_last > p->k)
           return fail(DASH_E_INVAL, "forced counts keep_first %d + keep_last %d must lie in [0, k = %d]",
                       p->keep_first, p->keep_last, p->k);
-        if (n_dev) return fail(DASH_E_INVAL, "top-k takes its length from n_max (n_dev must be NULL)");
+        if ((n_dev || n_out_dev) && rows != 1)
+          return fail(DASH_E_INVAL, "a device count (n_dev / n_out_dev) is supported for a single row only");
         if (pos && rows != 1) return fail(DASH_E_INVAL, "pos is supported for a single row only");
         if (static_cast<int64_t>(rows) * n_max > (1ll << 31) - 1)
           return fail(DASH_E_INVAL, "rows * n_max too large");
-        if (p->k == 0) return DASH_OK;
-        if (!score) return fail(DASH_E_INVAL, "score is NULL");
-        if (!idx) return fail(DASH_E_INVAL, "idx is NULL");
+        if (p->k == 0 && !n_out_dev && !nan_out) return DASH_OK;
+        if (!score && n_max > 0) return fail(DASH_E_INVAL, "score is NULL");
+        if (!idx && p->k > 0) return fail(DASH_E_INVAL, "idx is NULL");
+        if (n_max == 0 && !n_out_dev && !nan_out) return DASH_OK;
         tr = trace_open(DASH_TR_SELECT, st);
-        e = dash::launch_topk(score, rows, n_max, p->k, p->keep_first, p->keep_last, pos, idx, st);
+        e = dash::launch_topk(score, rows, n_max, p->k, p->keep_first, p->keep_last, pos, n_dev, idx, n_out_dev,
+                              nan_out, st);
         break;
       }
       case DASH_SEL_ORDER_STAT: {
@@ -289,19 +335,24 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
         if (p->rank < 1) return fail(DASH_E_INVAL, "rank must be >= 1");
         if (!n_dev && p->rank > n_max) return fail(DASH_E_INVAL, "rank %d exceeds n %d", p->rank, n_max);
         tr = trace_open(DASH_TR_SELECT, st);
-        e = dash::launch_order_stat(score, n_dev, n_max, p->rank, tau_out, st);
+        e = dash::launch_order_stat(score, n_dev, n_max, p->rank, tau_out, nan_out, st);
         break;
       }
       case DASH_SEL_THRESHOLD: {
         if (rows != 1) return fail(DASH_E_INVAL, "threshold selection supports one row");
         if (!p->tau || !p->counters) return fail(DASH_E_INVAL, "tau and counters are required");
+        if (p->n_counters < 1) return fail(DASH_E_INVAL, "n_counters = %d must be >= 1", p->n_counters);
         if (p->patience < 1 || p->patience > 255) return fail(DASH_E_INVAL, "patience must be in [1, 255]");
         if (!idx || !n_out_dev) return fail(DASH_E_INVAL, "idx and n_out_dev are required");
         if (n_max > 0 && !score) return fail(DASH_E_INVAL, "score is NULL");
+        if (!pos && n_max > p->n_counters)
+          return fail(DASH_E_INVAL, "without pos, rows are positions: n_max %d exceeds n_counters %d", n_max,
+                      p->n_counters);
         if (pos && static_cast<const void*>(pos) == static_cast<const void*>(idx))
           return fail(DASH_E_INVAL, "idx must not alias pos");
         tr = trace_open(DASH_TR_SELECT, st);
-        e = dash::launch_threshold(score, pos, n_dev, n_max, p->tau, p->patience, p->counters, idx, n_out_dev, st);
+        e = dash::launch_threshold(score, pos, n_dev, n_max, p->tau, p->patience, p->counters, p->n_counters, idx,
+                                   n_out_dev, nan_out, st);
         break;
       }
       default:

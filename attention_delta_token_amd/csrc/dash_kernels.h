@@ -66,8 +66,12 @@ int wo_gemm_parts(int dtype, int N);
 hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, float* score, float* part,
                           const int32_t* m_dev, int M_max, int N, int K, hipStream_t stream);
 
+// n_dev (rows == 1 only): the row's score count is min(*n_dev, n) and at most
+// that many are kept; n_out receives the kept count; nan_out[r] the number of
+// NaN scores of row r (each may be null).
 hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
-                       const int32_t* pos, int32_t* idx, hipStream_t stream);
+                       const int32_t* pos, const int32_t* n_dev, int32_t* idx, int32_t* n_out, int32_t* nan_out,
+                       hipStream_t stream);
 // Ragged top-k: sample b's scores are cu_n[b] .. cu_n[b+1]-1 of `score`
 // (n_total entries); it keeps cu_k[b+1] - cu_k[b] of them, written as packed
 // row indices to idx[cu_k[b] ..] (capacity k_cap); max_n bounds every
@@ -75,10 +79,11 @@ hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_firs
 hipError_t launch_topk_ragged(const float* score, int n_total, int B, const int32_t* cu_n, const int32_t* cu_k,
                               int max_n, int k_cap, int keep_first, int keep_last, int32_t* idx, hipStream_t stream);
 hipError_t launch_order_stat(const float* score, const int32_t* n_dev, int n_max, int rank, float* tau_out,
-                             hipStream_t stream);
+                             int32_t* nan_out, hipStream_t stream);
+// Rows whose position lies outside [0, n_counters) are dropped.
 hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,
-                            const float* tau, int patience, uint8_t* counters, int32_t* out, int32_t* n_out,
-                            hipStream_t stream);
+                            const float* tau, int patience, uint8_t* counters, int n_counters, int32_t* out,
+                            int32_t* n_out, int32_t* nan_out, hipStream_t stream);
 
 hipError_t launch_row_norm(int dtype, const void* U, const int32_t* n_dev, int n_max, int hidden, float* score,
                            hipStream_t stream);

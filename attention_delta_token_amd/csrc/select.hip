@@ -227,10 +227,11 @@ struct RowKeys {
 // Emit, in ascending position order, every i with key > cut plus the first
 // `take_eq` positions with key == cut, as first + i, or out_map[i] when
 // out_map != nullptr.  Writes stop at cap entries.
+// `nan` accumulates this thread's count of NaN scores (key 0).
 template <int NT>
 __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut, uint32_t take_eq,
                               const int32_t* __restrict__ out_map, int first, int32_t* __restrict__ out,
-                              uint32_t cap, uint64_t* sh_scan) {
+                              uint32_t cap, uint64_t* sh_scan, uint32_t& nan) {
   constexpr int E = 8;  // consecutive elements per thread per chunk
   uint32_t eq_before = 0u, sel_before = 0u;
   for (int base = 0; base < n; base += NT * E) {
@@ -242,6 +243,7 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
       const int i = i0 + e;
       if (i < n) {
         const uint32_t key = score_key(row[i]);
+        nan += key == 0u;
         if (key > cut) { ++gt; flags |= 1u << e; }
         else if (key == cut) { ++eq; flags |= 1u << (8 + e); }
       }
@@ -274,16 +276,18 @@ __device__ void emit_selected(const float* __restrict__ row, int n, uint32_t cut
 }
 
 // Row b of the selection.  Fixed rows: n_row scores at b * n_row, k_total
-// outputs at b * k_total, positions 0..n_row-1.  Ragged rows (packed samples):
-// scores cu_n[b] .. cu_n[b+1]-1, outputs cu_k[b] .. cu_k[b+1]-1, and the
-// written positions are packed row indices (cu_n[b] + local position).  A
-// ragged row asks for at most its length and at least its forced ends; counts
-// outside that are clamped (the unused outputs are left untouched).
+// outputs at b * k_total, positions 0..n_row-1; with a device count (one row),
+// the row holds min(*n_dev, n_row) scores and keeps at most that many.  Ragged
+// rows (packed samples): scores cu_n[b] .. cu_n[b+1]-1, outputs cu_k[b] ..
+// cu_k[b+1]-1, and the written positions are packed row indices (cu_n[b] +
+// local position).  A row asks for at most its length and at least its forced
+// ends; counts outside that are clamped (the unused outputs are left
+// untouched).
 struct SelRow {
   int64_t in_off, out_off;
   int n, k, f, l, base;
   __device__ __forceinline__ SelRow(int64_t b, int n_row, int k_total, int f_, int l_, const int32_t* cu_n,
-                                    const int32_t* cu_k) {
+                                    const int32_t* cu_k, const int32_t* n_dev) {
     if (cu_n) {  // n_row / k_total are then the packed score count / output capacity; rows are clamped into them
       in_off = min(max(cu_n[b], 0), n_row);
       n = max(0, min(cu_n[b + 1], n_row) - static_cast<int>(in_off));
@@ -294,15 +298,40 @@ struct SelRow {
       base = static_cast<int>(in_off);
     } else {
       in_off = b * n_row;
-      n = n_row;
       out_off = b * k_total;
-      k = k_total;
-      f = f_;
-      l = l_;
       base = 0;
+      if (n_dev) {
+        n = min(max(*n_dev, 0), n_row);
+        k = min(k_total, n);
+        f = min(f_, k);
+        l = min(l_, k - f);
+      } else {
+        n = n_row;
+        k = k_total;
+        f = f_;
+        l = l_;
+      }
     }
   }
 };
+
+// NaN scores among the forced ends of a row (positions 0..f-1 and n-l..n-1),
+// this thread's share.
+template <int NT>
+__device__ __forceinline__ uint32_t forced_nans(const float* __restrict__ row, int n, int f, int l) {
+  uint32_t c = 0u;
+  for (int i = threadIdx.x; i < f; i += NT) c += score_key(row[i]) == 0u;
+  for (int j = threadIdx.x; j < l; j += NT) c += score_key(row[n - l + j]) == 0u;
+  return c;
+}
+
+// Workgroup total of a per-thread count, written by thread 0 to *out.
+template <int NT>
+__device__ __forceinline__ void write_block_total(uint32_t mine, uint64_t* sh_scan, int32_t* out) {
+  uint64_t tot;
+  (void)block_excl_scan<NT>(mine, sh_scan, tot);
+  if (threadIdx.x == 0) *out = static_cast<int32_t>(tot);
+}
 
 // Forced retention: the first f and last l positions of a row of n_row
 // scores are written to the two ends of its k_total outputs; the caller then
@@ -324,23 +353,33 @@ template <int NT, bool Adaptive>
 __global__ __launch_bounds__(NT, 1)
 void topk_kernel(const float* __restrict__ score, int n_row, int k_total, int f_in, int l_in,
                  const int32_t* __restrict__ pos, int32_t* __restrict__ idx, const int32_t* __restrict__ cu_n,
-                 const int32_t* __restrict__ cu_k) {
+                 const int32_t* __restrict__ cu_k, const int32_t* __restrict__ n_dev, int32_t* __restrict__ n_out,
+                 int32_t* __restrict__ nan_out) {
   __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
-  const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k);
+  const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k, n_dev);
   const int f = rw.f, l = rw.l;
   int32_t* out = idx + rw.out_off;
+  if (n_out && threadIdx.x == 0) *n_out = rw.k;
   emit_forced<NT>(rw.n, rw.k, f, l, pos, rw.base, out);
   const int n = rw.n - f - l;
   const int k = rw.k - f - l;
-  if (k <= 0) return;
   const float* r = score + rw.in_off + f;
+  uint32_t nan = nan_out ? forced_nans<NT>(score + rw.in_off, rw.n, f, l) : 0u;
+  if (k <= 0) {
+    if (nan_out) {
+      for (int i = threadIdx.x; i < n; i += NT) nan += score_key(r[i]) == 0u;
+      write_block_total<NT>(nan, sh_scan, nan_out + blockIdx.x);
+    }
+    return;
+  }
   uint32_t take_eq;
   const uint32_t cut =
       radix_cut<NT, Adaptive>(RowKeys<NT>{r, n}, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
   emit_selected<NT>(r, n, cut, take_eq, pos ? pos + f : nullptr, rw.base + f, out + f, static_cast<uint32_t>(k),
-                   sh_scan);
+                   sh_scan, nan);
+  if (nan_out) write_block_total<NT>(nan, sh_scan, nan_out + blockIdx.x);
 }
 
 // Rows of up to NT * ITEMS scores: each thread loads its ITEMS consecutive
@@ -351,18 +390,19 @@ template <int NT, int ITEMS>
 __global__ __launch_bounds__(NT, 1)
 void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, int f_in, int l_in,
                      const int32_t* __restrict__ pos, int32_t* __restrict__ idx, const int32_t* __restrict__ cu_n,
-                     const int32_t* __restrict__ cu_k) {
+                     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ n_dev,
+                     int32_t* __restrict__ n_out, int32_t* __restrict__ nan_out) {
   static_assert(ITEMS <= 32, "masks are 32-bit");
   __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
-  const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k);
+  const SelRow rw(blockIdx.x, n_row, k_total, f_in, l_in, cu_n, cu_k, n_dev);
   const int f = rw.f, l = rw.l;
   int32_t* out = idx + rw.out_off;
+  if (n_out && threadIdx.x == 0) *n_out = rw.k;
   emit_forced<NT>(rw.n, rw.k, f, l, pos, rw.base, out);
   const int n = min(rw.n - f - l, NT * ITEMS);  // rows longer than the launch assumed are cut (never read past)
   const int k = rw.k - f - l;
-  if (k <= 0) return;
   const float* r = score + rw.in_off + f;
   out += f;
   const int i0 = threadIdx.x * ITEMS;
@@ -370,6 +410,16 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) keys[e] = (i0 + e < n) ? score_key(r[i0 + e]) : 0u;
   const int valid = n - i0;  // keys e < valid exist
+  uint32_t nan = 0u;
+  if (nan_out) {
+    nan = forced_nans<NT>(score + rw.in_off, rw.n, f, l);
+#pragma unroll
+    for (int e = 0; e < ITEMS; ++e) nan += (e < valid && keys[e] == 0u) ? 1u : 0u;
+  }
+  if (k <= 0) {
+    if (nan_out) write_block_total<NT>(nan, sh_scan, nan_out + blockIdx.x);
+    return;
+  }
   auto for_keys = [&](auto&& fn) {
 #pragma unroll
     for (int e = 0; e < ITEMS; ++e)
@@ -399,16 +449,23 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
       ++o;
     }
   }
+  if (nan_out) write_block_total<NT>(nan, sh_scan, nan_out + blockIdx.x);
 }
 
 __global__ __launch_bounds__(kSelThreads, 1)
 void order_stat_kernel(const float* __restrict__ score, const int32_t* __restrict__ n_dev, int n_max,
-                       int rank, float* __restrict__ tau_out) {
+                       int rank, float* __restrict__ tau_out, int32_t* __restrict__ nan_out) {
   __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   __shared__ uint32_t sh_cut[2];
   int n = n_dev ? *n_dev : n_max;
   if (n > n_max) n = n_max;
+  if (n < 0) n = 0;
+  if (nan_out) {
+    uint32_t nan = 0u;
+    for (int i = threadIdx.x; i < n; i += kSelThreads) nan += score_key(score[i]) == 0u;
+    write_block_total<kSelThreads>(nan, sh_scan, nan_out);
+  }
   if (rank < 1 || rank > n) {
     if (threadIdx.x == 0) *tau_out = __uint_as_float(0x7fc00000u);
     return;
@@ -424,15 +481,15 @@ void order_stat_kernel(const float* __restrict__ score, const int32_t* __restric
 __global__ __launch_bounds__(kSelThreads, 1)
 void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict__ pos,
                       const int32_t* __restrict__ n_dev, int n_max, const float* __restrict__ tau_p,
-                      int patience, uint8_t* __restrict__ counters, int32_t* __restrict__ out,
-                      int32_t* __restrict__ n_out) {
+                      int patience, uint8_t* __restrict__ counters, int n_counters, int32_t* __restrict__ out,
+                      int32_t* __restrict__ n_out, int32_t* __restrict__ nan_out) {
   __shared__ uint64_t sh_scan[2 * kSelWaves + 8];
   int n = n_dev ? *n_dev : n_max;
   if (n > n_max) n = n_max;
   if (n < 0) n = 0;
   const float tau = *tau_p;
   constexpr int E = 16;  // consecutive rows per thread per chunk; all loads issued before use
-  uint32_t before = 0u;
+  uint32_t before = 0u, nan = 0u;
   for (int base = 0; base < n; base += kSelThreads * E) {
     const int i0 = base + threadIdx.x * E;
     uint32_t keep_bits = 0u, cnt = 0u;
@@ -444,6 +501,11 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
       const int i = i0 + e;
       p[e] = i < n ? (pos ? pos[i] : i) : -1;
       sc[e] = i < n ? score[i] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      nan += (i0 + e < n && score_key(sc[e]) == 0u) ? 1u : 0u;
+      if (p[e] >= n_counters) p[e] = -1;  // position outside the counters: the row is dropped
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) c0[e] = p[e] >= 0 ? counters[p[e]] : 0;
@@ -467,6 +529,7 @@ void threshold_kernel(const float* __restrict__ score, const int32_t* __restrict
     before += static_cast<uint32_t>(tot);
   }
   if (threadIdx.x == 0) *n_out = static_cast<int32_t>(before);
+  if (nan_out) write_block_total<kSelThreads>(nan, sh_scan, nan_out);
 }
 
 }  // namespace
@@ -486,7 +549,8 @@ __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOM
 
 template <int J>
 __global__ __launch_bounds__(kWaveRowsPerBlock * kWave)
-void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, int32_t* __restrict__ idx) {
+void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, int32_t* __restrict__ idx,
+                      int32_t* __restrict__ nan_out) {
   __shared__ uint32_t hist_all[kWaveRowsPerBlock * kBins];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -506,6 +570,16 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
     for (int e = 0; e < 4; ++e) keys[j][e] = score_key(__uint_as_float(v[e]));
   }
   auto valid = [&](int j) { return j * kWave + lane < n4; };
+  if (nan_out) {
+    uint32_t nan = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (valid(j))
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nan += keys[j][e] == 0u;
+    nan = wave_incl_scan32(nan);
+    if (lane == kWave - 1) nan_out[row] = static_cast<int32_t>(nan);
+  }
 
   // Bits shared by every key of the row are settled first (wave min/max of the
   // keys in registers); digits of up to 11 bits then start right below them, so
@@ -618,45 +692,52 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
 }
 
 // n: the row length (ragged: the packed score count); n_longest: the longest
-// row (picks the kernel); cu_n / cu_k: ragged layout or null.
+// row (picks the kernel); cu_n / cu_k: ragged layout or null; n_dev: device
+// count of a single fixed row or null.
 template <int NT>
 void launch_topk_nt(const float* score, int rows, int n, int k, int f, int l, const int32_t* pos, int32_t* idx,
-                    const int32_t* cu_n, const int32_t* cu_k, hipStream_t stream, int n_longest = -1) {
+                    const int32_t* cu_n, const int32_t* cu_k, const int32_t* n_dev, int32_t* n_out,
+                    int32_t* nan_out, hipStream_t stream, int n_longest = -1) {
   const int n_mid = cu_n ? n_longest : n - f - l;
   const dim3 g(rows), b(NT);
+#define DASH_TOPK_ARGS score, n, k, f, l, pos, idx, cu_n, cu_k, n_dev, n_out, nan_out
   if (n_mid <= NT * 4)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 4>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 4>), g, b, 0, stream, DASH_TOPK_ARGS);
   else if (n_mid <= NT * 8)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 8>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 8>), g, b, 0, stream, DASH_TOPK_ARGS);
   else if (n_mid <= NT * 16)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 16>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 16>), g, b, 0, stream, DASH_TOPK_ARGS);
   else if (n_mid <= NT * 32)
-    hipLaunchKernelGGL((topk_reg_kernel<NT, 32>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
+    hipLaunchKernelGGL((topk_reg_kernel<NT, 32>), g, b, 0, stream, DASH_TOPK_ARGS);
   else if (rows == 1)
-    hipLaunchKernelGGL((topk_kernel<NT, true>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
+    hipLaunchKernelGGL((topk_kernel<NT, true>), g, b, 0, stream, DASH_TOPK_ARGS);
   else
-    hipLaunchKernelGGL((topk_kernel<NT, false>), g, b, 0, stream, score, n, k, f, l, pos, idx, cu_n, cu_k);
+    hipLaunchKernelGGL((topk_kernel<NT, false>), g, b, 0, stream, DASH_TOPK_ARGS);
+#undef DASH_TOPK_ARGS
 }
 
 }  // namespace
 
-// Many rows of at most 8192 aligned scores without forced ends or a position
-// map: one wave per row.  Otherwise one 1024-thread workgroup per row.
+// Many rows of at most 8192 aligned scores without forced ends, a position
+// map or a device count: one wave per row.  Otherwise one 1024-thread
+// workgroup per row.  k == 0 still launches when a count is to be written.
 hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
-                       const int32_t* pos, int32_t* idx, hipStream_t stream) {
-  if (rows == 0 || k == 0) return hipSuccess;
-  const bool wave_rows = rows >= kWaveRowsMin && !pos && keep_first == 0 && keep_last == 0 && n % 4 == 0 &&
-                         n <= 8192 && (reinterpret_cast<uintptr_t>(score) & 15u) == 0;
+                       const int32_t* pos, const int32_t* n_dev, int32_t* idx, int32_t* n_out, int32_t* nan_out,
+                       hipStream_t stream) {
+  if (rows == 0 || (k == 0 && !n_out && !nan_out)) return hipSuccess;
+  const bool wave_rows = rows >= kWaveRowsMin && !pos && !n_dev && keep_first == 0 && keep_last == 0 &&
+                         n % 4 == 0 && n <= 8192 && (reinterpret_cast<uintptr_t>(score) & 15u) == 0;
   if (wave_rows) {
     const dim3 grid((rows + kWaveRowsPerBlock - 1) / kWaveRowsPerBlock), block(kWaveRowsPerBlock * kWave);
     if (n <= 2048)
-      hipLaunchKernelGGL(topk_wave_kernel<8>, grid, block, 0, stream, score, rows, n, k, idx);
+      hipLaunchKernelGGL(topk_wave_kernel<8>, grid, block, 0, stream, score, rows, n, k, idx, nan_out);
     else if (n <= 4096)
-      hipLaunchKernelGGL(topk_wave_kernel<16>, grid, block, 0, stream, score, rows, n, k, idx);
+      hipLaunchKernelGGL(topk_wave_kernel<16>, grid, block, 0, stream, score, rows, n, k, idx, nan_out);
     else
-      hipLaunchKernelGGL(topk_wave_kernel<32>, grid, block, 0, stream, score, rows, n, k, idx);
+      hipLaunchKernelGGL(topk_wave_kernel<32>, grid, block, 0, stream, score, rows, n, k, idx, nan_out);
   } else {
-    launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, nullptr, nullptr, stream);
+    launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, nullptr, nullptr, n_dev, n_out,
+                                nan_out, stream);
   }
   return hipGetLastError();
 }
@@ -664,23 +745,23 @@ hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_firs
 hipError_t launch_topk_ragged(const float* score, int n_total, int B, const int32_t* cu_n, const int32_t* cu_k,
                               int max_n, int k_cap, int keep_first, int keep_last, int32_t* idx, hipStream_t stream) {
   if (B == 0 || max_n == 0 || k_cap == 0 || n_total == 0) return hipSuccess;
-  launch_topk_nt<kSelThreads>(score, B, n_total, k_cap, keep_first, keep_last, nullptr, idx, cu_n, cu_k, stream,
-                              max_n);
+  launch_topk_nt<kSelThreads>(score, B, n_total, k_cap, keep_first, keep_last, nullptr, idx, cu_n, cu_k, nullptr,
+                              nullptr, nullptr, stream, max_n);
   return hipGetLastError();
 }
 
 hipError_t launch_order_stat(const float* score, const int32_t* n_dev, int n_max, int rank, float* tau_out,
-                             hipStream_t stream) {
+                             int32_t* nan_out, hipStream_t stream) {
   hipLaunchKernelGGL(order_stat_kernel, dim3(1), dim3(kSelThreads), 0, stream, score, n_dev, n_max, rank,
-                     tau_out);
+                     tau_out, nan_out);
   return hipGetLastError();
 }
 
 hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,
-                            const float* tau, int patience, uint8_t* counters, int32_t* out,
-                            int32_t* n_out, hipStream_t stream) {
+                            const float* tau, int patience, uint8_t* counters, int n_counters, int32_t* out,
+                            int32_t* n_out, int32_t* nan_out, hipStream_t stream) {
   hipLaunchKernelGGL(threshold_kernel, dim3(1), dim3(kSelThreads), 0, stream, score, pos, n_dev, n_max, tau,
-                     patience, counters, out, n_out);
+                     patience, counters, n_counters, out, n_out, nan_out);
   return hipGetLastError();
 }
 

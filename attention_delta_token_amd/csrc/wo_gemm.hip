@@ -18,8 +18,7 @@
 // workspace and a finalize kernel adds the partials in a fixed order and takes
 // the square root, so the score is bit-reproducible run to run (no atomics).
 // A 224-column variant (below) is picked when it fills the chip better.
-#include <cstdlib>
-#include <cstring>
+#include <atomic>
 
 #include "dash_common.h"
 #include "dash_kernels.h"
@@ -481,27 +480,24 @@ void score_finalize_kernel(const float* __restrict__ part, int n_parts, int part
 
 namespace {
 
+// Compute units of the current device, queried once per device.
 int device_cus() {
-  static int cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    return n;
-  }();
-  return cus;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // Column tile for the bf16 path: the width whose whole waves of workgroups
 // (one per CU) cost least, a wave of 224-wide tiles counting 224/256 of a
-// wave of 256-wide ones.
-// DASH_WO_TILE_N=224 or 256 in the environment forces one of the two (tests
-// use it to cover both kernels at small sizes).
+// wave of 256-wide ones.  (With 256 CUs: 8192 x 3584 takes 224-wide tiles,
+// 4096 x 4096 and 131072 x 3584 take 256-wide ones.)
 int bf16_tile_n(int M, int N) {
-  if (const char* f = std::getenv("DASH_WO_TILE_N")) {
-    if (std::strcmp(f, "224") == 0) return kBN224;
-    if (std::strcmp(f, "256") == 0) return kBN;
-  }
   const long tm = (M + kBM - 1) / kBM;
   const long cus = device_cus();
   const long w256 = (tm * ((N + kBN - 1) / kBN) + cus - 1) / cus;

@@ -49,16 +49,19 @@ class OneShotStack:
     """Layers 0..hl full length, top-k at hl (optionally forcing the first
     keep_first and last keep_last tokens in), layers hl+1..L-1 on the kept rows.
     Layers may hold one sample (Q [S, Hq, D]) or B samples of equal length
-    (Q [B, S, Hq, D]); every sample keeps k tokens."""
+    (Q [B, S, Hq, D]); every sample keeps k = dash_keep_count(S, keep,
+    keep_first, keep_last) tokens.  `status` receives each sample's count of
+    NaN scores at the decision."""
 
-    def __init__(self, layers: list[LayerTensors], halt_layer: int, k: int, kv_mode: int = L.DASH_KV_ACTIVE,
+    def __init__(self, layers: list[LayerTensors], halt_layer: int, keep: float, kv_mode: int = L.DASH_KV_ACTIVE,
                  keep_first: int = 0, keep_last: int = 0):
         self.layers = layers
         self.hl = halt_layer
-        self.k = k  # total kept per sample, forced ends included
         self.kv_mode = kv_mode
         self.keep_first, self.keep_last = keep_first, keep_last
         B, S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        k = L.keep_count(S, keep, keep_first, keep_last)
+        self.k = k  # total kept per sample, forced ends included
         dev, dt = layers[0].Q.device, layers[0].Q.dtype
         self.B, self.S, self.Hq, self.Hkv, self.D, self.hidden = B, S, Hq, Hkv, D, hidden
         lead = (B,) if layers[0].Q.dim() == 4 else ()
@@ -73,6 +76,9 @@ class OneShotStack:
         self.Ua = torch.empty(*lead, kk, hidden, device=dev, dtype=dt)
         dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
         self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(B, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
+        self.status = L.select_status(B, device=dev)
+        self.record_post = False  # keep a copy of every post-halt layer's Oa and Ua (tests)
+        self.trace = []
 
     def full_layer(self, l: int, with_score: bool) -> None:
         x = self.layers[l]
@@ -80,7 +86,7 @@ class OneShotStack:
 
     def select(self) -> None:
         L.dash_select(self.score, self.idx, mode=L.DASH_SEL_TOPK, k=self.k, n_max=self.S, rows=self.B,
-                      keep_first=self.keep_first, keep_last=self.keep_last)
+                      keep_first=self.keep_first, keep_last=self.keep_last, status=self.status)
 
     def post_layer(self, l: int) -> None:
         x = self.layers[l]
@@ -103,6 +109,7 @@ class OneShotStack:
                                       Wo=x.Wo, Ua=self.Ua)
 
     def run(self) -> None:
+        self.trace = []
         for l in range(len(self.layers)):
             if l <= self.hl:
                 self.full_layer(l, with_score=(l == self.hl))
@@ -110,6 +117,8 @@ class OneShotStack:
                     self.select()
             else:
                 self.post_layer(l)
+                if self.record_post:
+                    self.trace.append((l, self.Oa.clone(), self.Ua.clone()))
 
     # -- gather once -------------------------------------------------------
     # A model gathers the hidden states of the kept tokens once at the halting
@@ -163,8 +172,9 @@ class RaggedOneShotStack:
     """One-shot halting for a packed batch of samples of different lengths:
     layers hold packed tensors (Q [T, Hq, D] ...) with the samples back to back
     (`lengths` on the host).  Every sample keeps its own
-    k_b = effective_keep(len_b, keep, keep_first, keep_last) tokens; the kept
-    rows stay packed (sample by sample) through the post-halt layers."""
+    k_b = dash_keep_count(len_b, keep, keep_first, keep_last) tokens (forced
+    counts clamped to the sample); the kept rows stay packed (sample by
+    sample) through the post-halt layers."""
 
     def __init__(self, layers: list[LayerTensors], lengths, halt_layer: int, keep: float,
                  kv_mode: int = L.DASH_KV_ACTIVE, keep_first: int = 0, keep_last: int = 0):
@@ -173,7 +183,7 @@ class RaggedOneShotStack:
         self.kv_mode = kv_mode
         self.keep_first, self.keep_last = keep_first, keep_last
         self.lengths = [int(n) for n in lengths]
-        self.ks = [L.effective_keep(n, keep, min(keep_first, n), min(keep_last, n - min(keep_first, n)))
+        self.ks = [L.keep_count(n, keep, min(keep_first, n), min(keep_last, n - min(keep_first, n)))
                    for n in self.lengths]
         _, T, Hq, Hkv, D, hidden = _shape_of(layers[0])
         if T != sum(self.lengths):
@@ -297,17 +307,18 @@ class MultiShotStack:
 
 
 class ThresholdStack:
-    """Layer 0 full length fixes tau (rank-th smallest score); every layer then
-    updates the counters and runs on the surviving queries (read in place
-    through their positions); keys and values stay full length (halted tokens
-    keep their K/V)."""
+    """Layer 0 full length fixes tau (the nearest-rank tau_pct-th percentile of
+    its scores, dash_percentile_rank); every layer then updates the counters
+    and runs on the surviving queries (read in place through their positions);
+    keys and values stay full length (halted tokens keep their K/V).
+    `status` receives the NaN counts of the last selection call."""
 
-    def __init__(self, layers: list[LayerTensors], tau_rank: int, patience: int = 2, record: bool = False,
+    def __init__(self, layers: list[LayerTensors], tau_pct: int, patience: int = 2, record: bool = False,
                  record_outputs: bool = True):
         self.layers = layers
-        self.rank = tau_rank
         self.patience = patience
         _, S, Hq, Hkv, D, hidden = _shape_of(layers[0])
+        self.rank = L.percentile_rank(S, tau_pct)
         dev, dt = layers[0].Q.device, layers[0].Q.dtype
         self.S = S
         self.O = torch.empty(S, Hq * D, device=dev, dtype=dt)
@@ -320,6 +331,7 @@ class ThresholdStack:
         self.Oa = torch.empty(S, Hq * D, device=dev, dtype=dt)
         dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
         self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
+        self.status = L.select_status(1, device=dev)
         self.record = record                  # keep per-layer host-visible copies (tests, measurement)
         self.record_outputs = record_outputs  # ... including scores and U, not only the active sets
         self.trace = []
@@ -331,7 +343,7 @@ class ThresholdStack:
         L.dash_attn_layer(x.Q, x.K, x.V, x.Wo, self.O, self.U, self.score, self.ws)
         L.dash_select(self.score, mode=L.DASH_SEL_ORDER_STAT, rank=self.rank, n_max=S, tau_out=self.tau)
         L.dash_select(self.score, self.pos[0], mode=L.DASH_SEL_THRESHOLD, tau=self.tau, patience=self.patience,
-                      counters=self.counters, n_max=S, n_out=self.n[0])
+                      counters=self.counters, n_max=S, n_out=self.n[0], status=self.status)
         if self.record:
             self.trace.append((None, self.score.clone() if self.record_outputs else None))
         cur = 0
@@ -348,7 +360,7 @@ class ThresholdStack:
             nxt = cur ^ 1
             L.dash_select(self.score, self.pos[nxt], mode=L.DASH_SEL_THRESHOLD, tau=self.tau,
                           patience=self.patience, counters=self.counters, pos=pos, n_dev=n, n_max=S,
-                          n_out=self.n[nxt])
+                          n_out=self.n[nxt], status=self.status)
             cur = nxt
         self.final = cur
 

@@ -2,20 +2,20 @@
 """Benchmark of the DASH prefill hot path on one MI355X.
 
 One step = one pass of the whole path over one synthetic sequence.  Default
-workload (Qwen2.5-7B shapes, S=8192, bf16): the halting layer at full length
-(causal GQA attention + W_o GEMM with the fused Δattn score), top-k selection
-(keep 0.5), compaction of the next layer's K/V at the kept positions, and the
-post-halt layer on the kept rows (attention reading its queries through the
-kept indices + W_o, kv active).  `--config`
-selects the other workloads: 0 = S=512 fp32; 2 = S=32768, 28 layers, halt at
-layer 11; 3 = S=65536 Llama-3.1-8B shapes, 32 layers, threshold halting with
-full K/V; 4 = S=131072, 28 layers, clustered salience, keep 0.3.
+workload (the largest one, Qwen2.5-7B shapes, bf16): S=131072 tokens, 28
+layers, clustered salience; layers 0..11 at full length (causal GQA attention
++ W_o GEMM, with the fused Δattn score at layer 11), top-k selection (keep
+0.3, k=39321), then layers 12..27 on the kept rows (K/V gathered at the kept
+positions, attention reading its queries through the kept indices, W_o on the
+kept rows).  `--config` selects the other workloads: 0 = S=512 fp32; 1 =
+S=8192, halt layer + one post-halt layer; 2 = S=32768, 28 layers, halt at 11;
+3 = S=65536 Llama-3.1-8B shapes, 32 layers, threshold halting with full K/V.
 
 Prints one JSON line: prefill tokens/s of the step, the dense (no halting)
-stack on the same kernels, a roofline entry for the dominant kernel (the
-attention kernel, from HIP events the library records on its launch stream),
-per-kernel timings, and the CPU oracle timed on this host as a reported
-baseline.
+stack on the same kernels timed in alternation with the step, a roofline
+entry for the dominant kernel (the attention kernel, from HIP events the
+library records on its launch stream), per-kernel timings, and the CPU oracle
+timed on this host as a reported baseline.
 """
 from __future__ import annotations
 
@@ -38,17 +38,14 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "attention_delta_token_amd", "csrc", "attn_fwd.hip")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_qwen_s8192_traffic.md")
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # ~30 steps (~30 ms at S=8192) bring the GPU to steady clocks; with 3 the
-    # first timed steps run about 6% slow
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -74,11 +71,15 @@ def source_digest(path):
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def read_traffic(digest):
-    """HBM bytes per attention launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
+def traffic_profile(w):
+    return os.path.join(ROOT, "profiles", f"attn_fwd_{w.name}_s{w.S}_traffic.md")
+
+
+def read_traffic(w, digest):
+    """HBM bytes per attention launch from the committed counter summary of this
+    workload, if it was taken on the current kernel source; else None."""
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(traffic_profile(w)).read()
     except OSError:
         return None
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
@@ -108,33 +109,52 @@ def main():
     w = WORKLOADS[args.config]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
-    # Inputs: generated on the host layer by layer, uploaded, kept resident in HBM.
+    # Inputs: generated on the host layer by layer, narrowed to the element
+    # type on the host (the values are exact in it), uploaded, kept resident.
+    t_gen = time.perf_counter()
     keep_host = not args.no_cpu_baseline and not args.profile_only
     layers, host_keep = [], {}
     for l in range(w.layers):
         h = layer_inputs(w, args.seed, l)
-        layers.append(LayerTensors(*(torch.from_numpy(h[n]).to(dev, tdt) for n in ("Q", "K", "V")),
-                                   torch.from_numpy(np.ascontiguousarray(h["Wo"].T)).to(dev, tdt)))
-        if keep_host and (l <= w.halt_layer + 1 or (w.mode == "threshold" and l <= 1)):
+        layers.append(LayerTensors(*(torch.from_numpy(h[n]).to(tdt).to(dev) for n in ("Q", "K", "V")),
+                                   torch.from_numpy(np.ascontiguousarray(h["Wo"].T)).to(tdt).to(dev)))
+        if keep_host and (l in (w.halt_layer, w.halt_layer + 1) or (w.mode == "threshold" and l <= 1)):
             host_keep[l] = h
         del h
+    torch.cuda.synchronize()
+    print(f"# {w.name}: {w.layers} layers generated and uploaded in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
 
     if w.mode == "threshold":
-        step = ThresholdStack(layers, tau_rank=w.tau_rank, patience=w.patience)
+        step = ThresholdStack(layers, tau_pct=w.tau_pct, patience=w.patience)
     else:
-        step = OneShotStack(layers, halt_layer=w.halt_layer, k=w.k)
+        step = OneShotStack(layers, halt_layer=w.halt_layer, keep=w.keep)
 
-    def timed(fn, steps):
-        if torch.distributed.is_available() and torch.distributed.is_initialized():
-            torch.distributed.barrier()
+    def timed(fn, steps, clocks=False):
+        """Wall-clock ms per step over `steps` calls bracketed by synchronisations.
+        clocks: a side thread reads rocm-smi 2 s into the region (context only;
+        the timed thread never waits for it)."""
+        import threading
+        got = {}
+
+        def sample():
+            time.sleep(2.0)
+            got["clocks"] = gpu_clocks()
+            got["at_s"] = time.perf_counter() - t0
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        th = threading.Thread(target=sample, daemon=True) if clocks else None
+        if th:
+            th.start()
         for _ in range(steps):
             fn()
-        if torch.distributed.is_available() and torch.distributed.is_initialized():
-            torch.distributed.barrier()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
+        elapsed = time.perf_counter() - t0
+        c = None
+        if th:
+            th.join()
+            c = {"rocm_smi": got.get("clocks"), "read_at_s": got.get("at_s"), "timed_region_s": elapsed}
+        return elapsed * 1e3 / steps, c
 
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -151,8 +171,8 @@ def main():
     # (median and minimum step beside the mean) and the library's pair around
     # each attention launch, whose durations give the roofline entry.  Only the
     # attention launches are bracketed there, so the events cost the step as
-    # little as possible; the per-kernel breakdown comes from the same steps
-    # run again with every launch group bracketed.
+    # little as possible; the per-kernel breakdown comes from a few more steps
+    # run with every launch group bracketed.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
 
     def run_marked():
@@ -166,37 +186,53 @@ def main():
     cap_attn = (w.layers + 1) * args.steps  # at most one attention launch per layer and step
     dash.trace_start(cap_attn)
     dash.trace_select(("attn_layer", "attn_active"))
-    ms = timed(run_marked, args.steps)
+    # not under a profiler: its preloaded library would follow the rocm-smi child
+    ms, clocks = timed(run_marked, args.steps, clocks=not args.profile_only)
     dash.trace_stop()
-    # read right after the timed steps (context only); not under a profiler,
-    # whose preloaded library would follow the rocm-smi child process
-    clocks = gpu_clocks() if not args.profile_only else None
     attn_recs = dash.trace_read(cap_attn)
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    cap_all = (8 * w.layers + 8) * args.steps  # every launch group of every layer and step
+    n_traced = max(1, min(args.steps, 3))
+    cap_all = (8 * w.layers + 8) * n_traced  # every launch group of every layer and step
     dash.trace_start(cap_all)
-    ms_all_traced = timed(step.run, args.steps)
+    ms_all_traced, _ = timed(step.run, n_traced)
     dash.trace_stop()
     recs = dash.trace_read(cap_all)
 
-    dense_ms = None
+    # Dense comparison: the dense stack (every layer at full length, same
+    # kernels) and the DASH step in alternation, so both see the same clock
+    # and thermal state; each step bracketed by events on the launch stream.
+    cmp = None
     if not args.no_dense and not args.profile_only:
         dense = DenseStack(layers)
-        for _ in range(max(1, args.warmup)):
+        dense.run()
+        pairs = max(2, min(args.steps, 6))
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * pairs)]
+        torch.cuda.synchronize()
+        for i in range(pairs):
+            evs[4 * i].record()
+            step.run()
+            evs[4 * i + 1].record()
+            evs[4 * i + 2].record()
             dense.run()
-        dense_ms = timed(dense.run, args.steps)
+            evs[4 * i + 3].record()
+        torch.cuda.synchronize()
+        d_ms = [evs[4 * i].elapsed_time(evs[4 * i + 1]) for i in range(pairs)]
+        n_ms = [evs[4 * i + 2].elapsed_time(evs[4 * i + 3]) for i in range(pairs)]
+        cmp = {"pairs": pairs, "dash_ms": sum(d_ms) / pairs, "dense_ms": sum(n_ms) / pairs,
+               "speedup": sum(n_ms) / sum(d_ms)}
+        del dense
 
     # Gather-once step (one-shot policy): the kept rows' hidden states are
     # gathered once at the halting layer ([S, hidden] stand-in) and the
     # post-halt layers run on inputs compacted beforehand, as a model's own
     # projections would produce them; the main step above instead gathers each
-    # post-halt layer's synthetic Q, K and V inside the step.
+    # post-halt layer's synthetic K and V inside the step.
     gather_once_ms = None
     if w.mode != "threshold" and not args.profile_only and not args.no_dense:
         step.prepare_gather_once()
-        for _ in range(args.warmup):
-            step.run_gather_once()
-        gather_once_ms = timed(step.run_gather_once, args.steps)
+        step.run_gather_once()
+        gather_once_ms, _ = timed(step.run_gather_once, max(1, min(args.steps, 3)))
+        step.pre, step.H, step.Ha = {}, None, None
 
     S, Hq, Hkv, D, hid = w.S, w.Hq, w.Hkv, w.D, w.hidden
     by = {}
@@ -212,29 +248,27 @@ def main():
     proj_full = 2.0 * S * (Hq * D) * hid
     if w.mode == "threshold":
         # post-halt launches: queries = active set before each layer, keys = all positions <= query
-        pos_trace = active_sets(step, layers)
-        f_post_list = [4.0 * D * Hq * float(np.sum(p.astype(np.float64) + 1.0)) for p in pos_trace]
-        f_post_layers = f_post_list
+        pos_trace = active_sets(step)
+        f_post_layers = [4.0 * D * Hq * float(np.sum(p.astype(np.float64) + 1.0)) for p in pos_trace]
         proj_post_list = [2.0 * p.shape[0] * (Hq * D) * hid for p in pos_trace]
         n_full, k_rows = 1, [p.shape[0] for p in pos_trace]
     else:
         n_full = w.halt_layer + 1
         n_post = w.layers - n_full
-        f_post_layers = [attn_flops(D, Hq, w.k)] * n_post
-        proj_post_list = [2.0 * w.k * (Hq * D) * hid] * n_post
-        k_rows = [w.k] * n_post
+        f_post_layers = [attn_flops(D, Hq, step.k)] * n_post
+        proj_post_list = [2.0 * step.k * (Hq * D) * hid] * n_post
+        k_rows = [step.k] * n_post
     # attention: the launches of the timed steps themselves
     by_attn = {}
     for op, t in attn_recs:
         by_attn.setdefault(op, []).append(t)
     t_full, t_post = by_attn.get("attn_layer", []), by_attn.get("attn_active", [])
-    steps_traced = args.steps
-    attn_flops_total = steps_traced * (n_full * f_full + sum(f_post_layers))
+    attn_flops_total = args.steps * (n_full * f_full + sum(f_post_layers))
     attn_ms_total = sum(t_full) + sum(t_post)
     attn_launches = len(t_full) + len(t_post)
     attn_tflops = attn_flops_total / (attn_ms_total * 1e-3) / 1e12
     t_pl, t_pa = by.get("proj_layer", []), by.get("proj_active", [])
-    proj_flops_total = steps_traced * (n_full * proj_full + sum(proj_post_list))
+    proj_flops_total = n_traced * (n_full * proj_full + sum(proj_post_list))
     proj_tflops = proj_flops_total / ((sum(t_pl) + sum(t_pa)) * 1e-3) / 1e12 if (t_pl or t_pa) else None
     esz = 2 if w.dtype == "bf16" else 4
     # select: 4 B per score read + 4 B per kept index (top-k); compaction: 2*row bytes + 4 B index per kept row.
@@ -247,7 +281,7 @@ def main():
         n_sel_step = 2 + len(k_rows)
         cmp_bytes_step, n_cmp_step = 0.0, 0
     else:
-        sel_bytes_step = 4.0 * S + 4.0 * w.k
+        sel_bytes_step = 4.0 * S + 4.0 * step.k
         n_sel_step = 1
         if w.kv_mode == "active":
             cmp_bytes_step = sum(k * (2 * esz * 2 * Hkv * D + 4) for k in k_rows)
@@ -255,8 +289,8 @@ def main():
         else:
             cmp_bytes_step, n_cmp_step = 0.0, 0
     t_sel, t_cmp = by.get("select", []), by.get("compact", [])
-    sel_gbps = (steps_traced * sel_bytes_step) / (sum(t_sel) * 1e-3) / 1e9 if t_sel else None
-    cmp_gbps = (steps_traced * cmp_bytes_step) / (sum(t_cmp) * 1e-3) / 1e9 if t_cmp else None
+    sel_gbps = (n_traced * sel_bytes_step) / (sum(t_sel) * 1e-3) / 1e9 if t_sel else None
+    cmp_gbps = (n_traced * cmp_bytes_step) / (sum(t_cmp) * 1e-3) / 1e9 if t_cmp else None
 
     dense_flops = w.layers * (f_full + proj_full)
     dash_flops = n_full * (f_full + proj_full) + sum(f_post_layers) + sum(proj_post_list)
@@ -264,10 +298,8 @@ def main():
     bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     digest = source_digest(ATTN_SRC)
-    traffic = None
-    tr = read_traffic(digest) if (args.config == 1) else None
-    if tr is not None:
-        traffic = tr["bytes_per_launch_avg"]
+    tr = read_traffic(w, digest)
+    traffic = tr["bytes_per_launch_avg"] if tr is not None else None
 
     out = {
         "metric": METRIC,
@@ -282,7 +314,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, lognormal V row scales, N(0,1/hidden) W_o; no trained weights)",
-        "config": {"workload": describe(w), "global_batch": 1, "seq_len": S, "parallelism": "single GPU"},
+        "config": {"workload": describe(w, step), "global_batch": 1, "seq_len": S, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if bf16 else "alu",
                      "kernel": f"attn_fwd_{'bf16' if bf16 else 'f32'}_kernel<{D}>",
                      "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
@@ -290,23 +322,27 @@ def main():
                      "launches": attn_launches, "avg_launch_ms": attn_ms_total / max(1, attn_launches),
                      "flops_per_launch_avg": attn_flops_total / max(1, attn_launches),
                      "attn_src_sha256_16": digest},
-        "dense_ms_per_step": dense_ms,
-        "dense_tokens_per_s": (S / (dense_ms * 1e-3)) if dense_ms else None,
-        "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
+        "dense_ms_per_step": cmp["dense_ms"] if cmp else None,
+        "dense_tokens_per_s": (S / (cmp["dense_ms"] * 1e-3)) if cmp else None,
+        "speedup_vs_dense": cmp["speedup"] if cmp else None,
+        "dense_comparison": ({"how": f"{cmp['pairs']} DASH steps and {cmp['pairs']} dense steps in alternation, "
+                                     "HIP events around each",
+                              "dash_ms": cmp["dash_ms"], "dense_ms": cmp["dense_ms"]} if cmp else None),
         "ideal_speedup_flops": dense_flops / dash_flops,
         "gather_once": ({"ms_per_step": gather_once_ms, "tokens_per_s": S / (gather_once_ms * 1e-3),
-                         "speedup_vs_dense": (dense_ms / gather_once_ms) if dense_ms else None,
+                         "speedup_vs_dense": (cmp["dense_ms"] / gather_once_ms) if cmp else None,
                          "what": "one gather of an [S, hidden] bf16 hidden-state stand-in at the halting layer; "
                                  "post-halt layers on inputs compacted beforehand"}
                         if gather_once_ms else None),
         "all_traced_ms_per_step": ms_all_traced,
-        "clocks_after_timed_steps": clocks,
+        "clocks_during_timed_steps": clocks,
         "step_ms_median": per_step[len(per_step) // 2], "step_ms_min": per_step[0],
         "kernels": {
             "attn_full_ms": (sum(t_full) / len(t_full)) if t_full else None,
             "attn_post_ms": (sum(t_post) / len(t_post)) if t_post else None,
             "attn_full_tflops": (f_full / (sum(t_full) / len(t_full) * 1e-3) / 1e12) if t_full else None,
-            "attn_post_tflops": (steps_traced * sum(f_post_layers) / (sum(t_post) * 1e-3) / 1e12) if t_post else None,
+            "attn_full_frac": (f_full / (sum(t_full) / len(t_full) * 1e-3) / 1e12 / peak) if t_full else None,
+            "attn_post_tflops": (args.steps * sum(f_post_layers) / (sum(t_post) * 1e-3) / 1e12) if t_post else None,
             "proj_full_ms": avg("proj_layer"), "proj_post_ms": avg("proj_active"),
             "proj_tflops": proj_tflops, "proj_frac": (proj_tflops / peak) if proj_tflops else None,
             "select_ms": avg("select"), "select_calls_per_step": n_sel_step, "select_GBps": sel_gbps,
@@ -320,9 +356,9 @@ def main():
     if not args.profile_only:
         out["select_sweep"] = [select_sweep(dash, torch, dev, rows, n)
                                for rows, n in ((2048, 8192), (8192, 8192), (256, 65536))]
-        out["score"] = score_measurements(dash, torch, dev, step, layers[0])
+        out["score"] = score_measurements(dash, torch, dev, step, layers[w.halt_layer if w.mode != "threshold" else 0])
         if w.dtype == "bf16" and w.mode != "threshold":
-            out["decode"] = decode_measurements(dash, torch, dev, w, layers[-1])
+            out["decode"] = decode_measurements(dash, torch, dev, w, layers[-1], step.k)
 
     if not args.no_cpu_baseline and not args.profile_only:
         out["cpu_baseline"] = cpu_baseline(w, host_keep, step, k_rows)
@@ -344,9 +380,8 @@ def gpu_clocks():
 
 
 def select_sweep(dash, torch, dev, rows=256, n=65536):
-    """Top-k over a batch of independent score rows (one workgroup per row), the
-    regime where selection is bandwidth-bound: 4 B read per score + 4 B written
-    per kept index."""
+    """Top-k over a batch of independent score rows, the regime where selection
+    is bandwidth-bound: 4 B read per score + 4 B written per kept index."""
     k = n // 2
     g = torch.Generator(device=dev).manual_seed(0)
     score = torch.rand(rows, n, device=dev, generator=g)
@@ -364,9 +399,10 @@ def select_sweep(dash, torch, dev, rows=256, n=65536):
 
 
 def score_measurements(dash, torch, dev, step, layer):
-    """The score two ways on the full-length layer: standalone (||U_t|| read back
-    from a stored U: hidden * element size B read + 4 B written per row, HBM
-    bound) and fused (the W_o GEMM with and without the sum of squares)."""
+    """The score two ways on the scored full-length layer: standalone
+    (||U_t|| read back from a stored U: hidden * element size B read + 4 B
+    written per row, HBM bound) and fused (the W_o GEMM with and without the
+    sum of squares)."""
     U = step.U
     rows, hidden = U.shape
     score = torch.empty(rows, dtype=torch.float32, device=dev)
@@ -399,7 +435,7 @@ def score_measurements(dash, torch, dev, step, layer):
     proj = {}
     for with_score in (True, False, True, False):
         dash.trace_start(64)
-        for _ in range(10):
+        for _ in range(3):
             dash.dash_attn_layer(layer.Q, layer.K, layer.V, layer.Wo, step.O, step.U,
                                  step.score if with_score else None, ws)
         dash.trace_stop()
@@ -411,7 +447,7 @@ def score_measurements(dash, torch, dev, step, layer):
     return out
 
 
-def decode_measurements(dash, torch, dev, w, layer):
+def decode_measurements(dash, torch, dev, w, layer, k):
     """One decode token per sample against the cache a prefill leaves: the k kept
     rows (pruned) versus all S rows (dense), same kernels; the cache read (K and
     V of every cached row) is the algorithmic traffic.  A decode loop issues
@@ -421,7 +457,7 @@ def decode_measurements(dash, torch, dev, w, layer):
     res = {}
     Hkv, D, Hq = w.Hkv, w.D, w.Hq
     Qd = layer.Q[:1].reshape(1, 1, Hq, D).contiguous()
-    for name, rows in (("pruned", w.k), ("dense", w.S)):  # cache rows, the new token's own included
+    for name, rows in (("pruned", k), ("dense", w.S)):  # cache rows, the new token's own included
         Kc = layer.K[:rows].reshape(1, rows, Hkv, D)
         Vc = layer.V[:rows].reshape(1, rows, Hkv, D)
         n_kv = torch.tensor([rows], dtype=torch.int32, device=dev)
@@ -465,18 +501,17 @@ def decode_measurements(dash, torch, dev, w, layer):
     return res
 
 
-def describe(w):
+def describe(w, step):
     s = (f"{w.name}: S={w.S}, Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, hidden={w.hidden}, {w.layers} layers, ")
     if w.mode == "threshold":
         return s + (f"threshold halting (tau = {w.tau_pct}th-percentile layer-0 score, patience {w.patience}), "
                     f"kv_mode={w.kv_mode}")
-    return s + f"one-shot halt at layer {w.halt_layer}, top-k keep {w.keep} (k={w.k}), kv_mode={w.kv_mode}" + (
+    return s + f"one-shot halt at layer {w.halt_layer}, top-k keep {w.keep} (k={step.k}), kv_mode={w.kv_mode}" + (
         ", clustered salience" if w.clustered else "")
 
 
-def active_sets(step, layers):
+def active_sets(step):
     """Active query positions of each post-halt layer of the last threshold run (host copies)."""
-    import torch  # noqa: F401
     st = step
     # Replay the run once, recording only the per-layer active sets.
     st.record, st.record_outputs = True, False
@@ -491,23 +526,44 @@ def active_sets(step, layers):
     return out
 
 
-def cpu_baseline(w, host_keep, step, k_rows):
-    """The CPU oracle (float64 NumPy, as it stands) on the same seeded inputs."""
-    import oracle
+def blas_info():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": int(i.get("num_threads", 1))}
+    except Exception:  # noqa: BLE001 - report what is known
+        pass
+    return {"vendor": None, "version": None, "threads": 1}
+
+
+def cpu_baseline(w, host_keep, step, k_rows):
+    """The CPU oracle (float64 NumPy, as it stands) on the same seeded inputs.
+
+    Short sequences: whole steps.  Long ones: the oracle on uniformly sampled
+    blocks of 128 consecutive query rows (its own block size, so each block
+    costs what it costs inside a whole-layer call) of one full-length layer and
+    of one post-halt layer, scaled by the number of blocks, then by the layer
+    counts (labelled extrapolated)."""
+    import oracle
+    blas = blas_info()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    base = {"unit": "tokens/s", "cores": blas["threads"], "kind": "oracle", "affinity_cores": affinity,
+            "blas": blas}
     if w.S <= 8192:
         # whole steps (halting layer at full length + top-k + post-halt layer(s)), repeated until
         # about 10 s of CPU work has been timed (at most 4 repetitions)
+        k = oracle.topk_count(w.S, w.keep)
         reps, t = 0, 0.0
         while reps < 4 and (reps == 0 or t < 10.0):
             t0 = time.perf_counter()
             x = host_keep[w.halt_layer]
             _, _, s = oracle.attention_layer(x["Q"], x["K"], x["V"], x["Wo"])
-            idx = oracle.select_topk(s, w.k)
+            idx = oracle.select_topk(s, k)
             for l in range(w.halt_layer + 1, w.layers):
                 y = host_keep[l]
                 oa = oracle.attn_active(y["Q"], y["K"], y["V"], idx, w.kv_mode)
@@ -515,44 +571,44 @@ def cpu_baseline(w, host_keep, step, k_rows):
             t += time.perf_counter() - t0
             reps += 1
         per = t / reps
-        est = per * (w.layers / (1 + (w.layers - w.halt_layer - 1))) if w.halt_layer > 0 else per
         sample = (f"{reps} whole step(s) of the same seeded workload (halt layer at full length + top-k + "
                   f"{w.layers - w.halt_layer - 1} post-halt layer), float64, {t:.1f} s in total")
-        return {"value": w.S / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-                "sample": sample, "seconds": t}
-    # Long sequences: time the oracle on a uniform sample of query rows of one full-length layer
-    # and of one post-halt layer, and extrapolate to the stack.
+        return dict(base, value=w.S / per, sample=sample, seconds=t)
     rng = np.random.default_rng(0)
-    R = 64
-    x = host_keep[w.halt_layer]
-    rows = np.sort(rng.choice(w.S, R, replace=False))
-    t0 = time.perf_counter()
-    O = oracle.causal_gqa_attention(x["Q"][rows], x["K"], x["V"], q_pos=rows)
-    oracle.delta_attn(oracle.output_projection(O, x["Wo"]))
-    t_full_row = (time.perf_counter() - t0) / R
-    y = host_keep[w.halt_layer + 1]
-    if w.mode == "threshold":
-        post_rows = np.sort(rng.choice(w.S, R, replace=False))
+    BR = 128
+    nb = 12  # sampled blocks per layer kind
+
+    def blocks_time(Q, K, V, Wo, q_pos_all, kv_pos, n_rows):
+        n_blk = (n_rows + BR - 1) // BR
+        pick = np.sort(rng.choice(n_blk, min(nb, n_blk), replace=False))
         t0 = time.perf_counter()
-        O = oracle.causal_gqa_attention(y["Q"][post_rows], y["K"], y["V"], q_pos=post_rows)
-        oracle.output_projection(O, y["Wo"])
-        t_post_row = (time.perf_counter() - t0) / R
+        for b in pick:
+            r = np.arange(b * BR, min(n_rows, (b + 1) * BR))
+            O = oracle.causal_gqa_attention(Q[r], K, V, q_pos=q_pos_all[r], kv_pos=kv_pos)
+            oracle.delta_attn(oracle.output_projection(O, Wo))
+        return (time.perf_counter() - t0) * n_blk / pick.size, pick.size
+
+    x = host_keep[w.halt_layer if w.mode != "threshold" else 0]
+    t_full, b_full = blocks_time(x["Q"], x["K"], x["V"], x["Wo"], np.arange(w.S), None, w.S)
+    y = host_keep[w.halt_layer + 1 if w.mode != "threshold" else 1]
+    if w.mode == "threshold":
+        # a post-halt layer over its active rows (kv all), the GPU run's trajectory for the counts
+        n = k_rows[0]
+        pos = np.sort(rng.choice(w.S, n, replace=False)) if n < w.S else np.arange(w.S)
+        t_p, b_post = blocks_time(y["Q"][pos], y["K"], y["V"], y["Wo"], pos, None, n)
+        est = t_full + sum(t_p * (kr / max(1, n)) for kr in k_rows)
         n_full = 1
     else:
-        k = w.k
-        kidx = np.sort(rng.choice(w.S, k, replace=False))
-        qsel = np.sort(rng.choice(k, R, replace=False))
-        Ka, Va = y["K"][kidx], y["V"][kidx]
-        t0 = time.perf_counter()
-        O = oracle.causal_gqa_attention(y["Q"][kidx[qsel]], Ka, Va, q_pos=qsel)
-        oracle.output_projection(O, y["Wo"])
-        t_post_row = (time.perf_counter() - t0) / R
+        k = step.k
+        idx = np.sort(rng.choice(w.S, k, replace=False))
+        t_p, b_post = blocks_time(y["Q"][idx], y["K"][idx], y["V"][idx], y["Wo"], idx, idx, k)
         n_full = w.halt_layer + 1
-    est = n_full * w.S * t_full_row + sum(k_rows) * t_post_row
-    return {"value": w.S / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"{R} uniformly sampled query rows of one full-length layer and of one post-halt layer "
-                       f"(float64), extrapolated to the {w.layers}-layer stack: {est:.0f} s"),
-            "extrapolated": True}
+        est = n_full * t_full + (w.layers - n_full) * t_p
+    return dict(base, value=w.S / est,
+                sample=(f"{b_full} and {b_post} uniformly sampled blocks of {BR} query rows of one full-length "
+                        f"and one post-halt layer (float64), scaled to whole layers and extrapolated to the "
+                        f"{w.layers}-layer stack: {est:.0f} s"),
+                extrapolated=True)
 
 
 if __name__ == "__main__":

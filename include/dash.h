@@ -36,6 +36,10 @@
  *     Element type of Q, K, V, O, Wo and U is `dtype` (fp32 or bf16);
  *     arithmetic accumulates in fp32.
  *   - q-head h reads kv-head h / (Hq / Hkv); softmax scale is 1/sqrt(D).
+ *   - Size limits checked by every call that takes a dash_shape: S <= 2^24,
+ *     B * S <= 2^26, and one sample's K (and V), S * Hkv * D * element size
+ *     bytes, below 4 GiB (the attention kernels address K and V through
+ *     32-bit buffer offsets); DASH_E_SHAPE otherwise.
  */
 #ifndef DASH_H
 #define DASH_H
@@ -73,13 +77,14 @@ typedef struct {
  *   ORDER_STAT:  rank (1-based) of the order statistic among ascending scores.
  *   THRESHOLD:   tau (DEVICE pointer to one float), patience (consecutive
  *                layers below tau before a token halts), counters (DEVICE
- *                uint8 array indexed by original position, length >= every
- *                position that appears).
+ *                uint8 array indexed by original position) holding n_counters
+ *                entries.  A row whose position lies outside [0, n_counters)
+ *                is dropped: it is not emitted and no counter is touched.
  *   keep_first / keep_last: TOPK only (0 for the other modes): forced
  *                retention of the first f and last l positions of every row
  *                ([P1] §3.1 and §3.2: keep_first_n / keep_last_n).  k stays
- *                the total kept count (K_eff = f + l + floor(keep * (n - f - l))
- *                in [P1]'s terms) and 0 <= f + l <= k is required. */
+ *                the total kept count (dash_keep_count gives it from the keep
+ *                ratio) and 0 <= f + l <= k is required. */
 typedef struct {
   int mode; /* dash_sel_mode */
   int k;
@@ -88,6 +93,7 @@ typedef struct {
   int patience;
   uint8_t* counters;
   int keep_first, keep_last;
+  int n_counters; /* THRESHOLD: entries of counters; unused otherwise */
 } dash_sel;
 
 /* Library context: remembers the device and its compute-unit count.
@@ -100,6 +106,22 @@ const char* dash_last_error(void);
 
 /* Library version string. */
 const char* dash_version(void);
+
+/* Kept count of the one-shot policy ([P1] §3.1 step 3 and §3.2: K =
+ * floor(keep * T) with keep = 1 - ρ; with forced retention of the first f =
+ * keep_first and last l = keep_last tokens, K_eff = f + l + floor(keep * (T -
+ * f - l))).  The product is formed in double precision and truncated, so
+ * T = 131072, keep = 0.3 gives 39321.  Requires T >= 0, 0 <= keep <= 1 and
+ * f, l >= 0 with f + l <= T (else DASH_E_INVAL and *k_out untouched). */
+int dash_keep_count(int T, double keep, int keep_first, int keep_last, int* k_out);
+
+/* Rank of the halting threshold of the selective-halting policy ([P2]
+ * 层间更新动态监测: a token halts once its update stays below a preset
+ * threshold): the nearest-rank pct-th percentile of n scores, rank =
+ * ceil(pct * n / 100) in integer arithmetic and at least 1 (n = 65536,
+ * pct = 30 gives 19661).  It is the `rank` of DASH_SEL_ORDER_STAT.  Requires
+ * n >= 1 and 0 <= pct <= 100. */
+int dash_percentile_rank(int n, int pct, int* rank_out);
 
 /* Workspace bytes needed by `op` (dash_op) for shape s with up to n_max rows
  * (n_max is the sequence length for DASH_OP_ATTN_LAYER and the row capacity
@@ -115,8 +137,7 @@ size_t dash_workspace_size(void* ctx, int op, const dash_shape* s, int n_max);
  * Supported: dtype bf16 with D in {64, 128}; dtype fp32 with D <= 128 and
  * D % 4 == 0 (reference-speed kernels).  hidden % 4 == 0; Hq % Hkv == 0.
  * The bf16 W_o GEMM picks 224- or 256-column tiles, whichever fills the
- * chip's compute units in fewer tile-widths of work; the environment variable
- * DASH_WO_TILE_N=224 or =256 forces one (read at every launch; for tests).
+ * chip's compute units in fewer tile-widths of work.
  * Workspace: dash_workspace_size(DASH_OP_ATTN_LAYER, s, S). */
 int dash_attn_layer(void* ctx, const dash_shape* s,
                     const void* Q, const void* K, const void* V, const void* Wo,
@@ -128,21 +149,32 @@ int dash_attn_layer(void* ctx, const dash_shape* s,
  *               largest score, ties to the lower position, NaN below every
  *               number, -0 == +0, written in ascending order.  If pos != NULL
  *               (rows == 1 only) the kept entries are pos[i] instead of i.
- *               n_dev must be NULL (n = n_max).  With keep_first f and
- *               keep_last l, positions 0..f-1 and n-l..n-1 are always kept and
- *               the other k - f - l are the top ones among positions f..n-l-1
- *               under the same order; the output is still ascending.
+ *               n = n_max, or n = min(*n_dev, n_max) for rows == 1 when n_dev
+ *               != NULL (a count left on the device by an earlier step); then
+ *               min(k, n) positions are kept (f and l shrink likewise: f' =
+ *               min(f, k'), l' = min(l, k' - f')) and idx entries past them
+ *               are left untouched.  n_out_dev, if not NULL (rows == 1), gets
+ *               the kept count.  With keep_first f and keep_last l, positions
+ *               0..f-1 and n-l..n-1 are always kept and the other k - f - l
+ *               are the top ones among positions f..n-l-1 under the same
+ *               order; the output is still ascending.
  *   ORDER_STAT: rows == 1; n = *n_dev (or n_max); *tau_out (device) = the
  *               rank-th smallest of score[0..n) under the same order (NaN
  *               lowest), a zero returned as +0.  rank <= n is required when n
  *               comes from the device; otherwise tau_out is set to NaN.
  *   THRESHOLD:  rows == 1; n = *n_dev (or n_max); row i belongs to position
- *               p = pos[i] (pos == NULL ⇒ p = i; pos ascending).  For each row:
- *               counters[p] = score[i] < *tau ? counters[p] + 1 : 0 and the row
- *               stays active iff counters[p] < patience.  Surviving positions
- *               are written ascending to idx (capacity n_max) and their number
- *               to *n_out_dev (device int).  idx must not alias pos.
- * Workspace: dash_workspace_size(DASH_OP_SELECT, {B = rows, ...}, n_max). */
+ *               p = pos[i] (pos == NULL ⇒ p = i; pos ascending).  For each row
+ *               with 0 <= p < n_counters: counters[p] = score[i] < *tau ?
+ *               counters[p] + 1 : 0 (saturating at 255) and the row stays
+ *               active iff counters[p] < patience.  A NaN score is not below
+ *               tau, so it resets the counter.  Surviving positions are written
+ *               ascending to idx (capacity n_max) and their number to
+ *               *n_out_dev (device int).  idx must not alias pos.
+ * NaN status: when ws != NULL, row r's count of NaN scores (among the n it
+ *   ranks or updates, forced ends included) is written to the int32 word r of
+ *   ws; ws == NULL skips the count.
+ * Workspace: dash_workspace_size(DASH_OP_SELECT, {B = rows, ...}, n_max)
+ * bytes (4 per row, at least 256) when the NaN status is wanted. */
 int dash_select(void* ctx, const dash_sel* p, const float* score, const int32_t* pos,
                 const int32_t* n_dev, int n_max, int rows,
                 int32_t* idx, int32_t* n_out_dev, float* tau_out,

@@ -11,6 +11,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU oracle check")
+    # CPU runs of the C-ABI tests against another build of the library (the
+    # host-sanitizer build: python -m attention_delta_token_amd.build --host-asan)
+    lib = os.environ.get("DASH_TEST_LIB")
+    if lib:
+        from attention_delta_token_amd import _lib
+        _lib.load(lib)
 
 
 @pytest.fixture(scope="session")

@@ -76,36 +76,103 @@ def test_attn_layer_validation(lib):
     assert f(None, ctypes.byref(_shape()), *p, FAKE, FAKE, need - 1, None) == L.DASH_E_WORKSPACE
 
 
+def _sel(mode, k=0, rank=0, tau=None, patience=2, counters=None, f=0, l=0, n_counters=0):
+    return L.DashSel(mode, k, rank, tau, patience, counters, f, l, n_counters)
+
+
 def test_select_validation(lib):
+    """Every case here fails validation (or has nothing to do), so no kernel is
+    launched on the placeholder pointers."""
     f = lib.dash_select
-    sel = L.DashSel(L.DASH_SEL_TOPK, 5, 0, None, 2, None, 0, 0)
+    sel = _sel(L.DASH_SEL_TOPK, k=5)
     assert f(None, None, FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
     assert f(None, ctypes.byref(sel), FAKE, None, None, 4, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
     assert "outside" in _last(lib)
-    assert f(None, ctypes.byref(sel), FAKE, None, FAKE, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    # a device count (or a kept-count output) with several rows
+    assert f(None, ctypes.byref(sel), FAKE, None, FAKE, 10, 2, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+    assert "single row" in _last(lib)
+    assert f(None, ctypes.byref(sel), FAKE, None, None, 10, 2, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
     assert f(None, ctypes.byref(sel), FAKE, FAKE, None, 10, 2, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
     assert f(None, ctypes.byref(sel), None, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
-    sel0 = L.DashSel(L.DASH_SEL_TOPK, 0, 0, None, 2, None, 0, 0)
+    sel0 = _sel(L.DASH_SEL_TOPK)
     assert f(None, ctypes.byref(sel0), None, None, None, 10, 1, None, None, None, None, 0, None) == L.DASH_OK
-    forced = L.DashSel(L.DASH_SEL_TOPK, 5, 0, None, 2, None, 64, 0)
+    # the NaN status needs 4 bytes per row of workspace (256 at least)
+    assert f(None, ctypes.byref(sel), FAKE, None, None, 10, 1, FAKE, None, None, FAKE, 255, None) == \
+        L.DASH_E_WORKSPACE
+    assert f(None, ctypes.byref(sel), FAKE, None, None, 10, 100, FAKE, None, None, FAKE, 256, None) == \
+        L.DASH_E_WORKSPACE
+    assert f(None, ctypes.byref(sel), FAKE, None, None, 10, 1, FAKE, None, None, FAKE + 2, 256, None) == \
+        L.DASH_E_ALIGN
+    forced = _sel(L.DASH_SEL_TOPK, k=5, f=64)
     assert f(None, ctypes.byref(forced), FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
     # forced retention: f + l must not exceed k; negative counts rejected; top-k only
     for kf, kl in ((3, 3), (-1, 0), (0, -2)):
-        bad_f = L.DashSel(L.DASH_SEL_TOPK, 5, 0, None, 2, None, kf, kl)
+        bad_f = _sel(L.DASH_SEL_TOPK, k=5, f=kf, l=kl)
         assert f(None, ctypes.byref(bad_f), FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
     assert "keep_first" in _last(lib)
-    os_f = L.DashSel(L.DASH_SEL_ORDER_STAT, 0, 3, None, 2, None, 1, 0)
+    os_f = _sel(L.DASH_SEL_ORDER_STAT, rank=3, f=1)
     assert f(None, ctypes.byref(os_f), FAKE, None, None, 10, 1, None, None, FAKE, None, 0, None) == L.DASH_E_INVAL
     assert "top-k only" in _last(lib)
-    os_ = L.DashSel(L.DASH_SEL_ORDER_STAT, 0, 11, None, 2, None, 0, 0)
+    os_ = _sel(L.DASH_SEL_ORDER_STAT, rank=11)
     assert f(None, ctypes.byref(os_), FAKE, None, None, 10, 1, None, None, FAKE, None, 0, None) == L.DASH_E_INVAL
-    th = L.DashSel(L.DASH_SEL_THRESHOLD, 0, 0, FAKE, 0, FAKE, 0, 0)
+    th = _sel(L.DASH_SEL_THRESHOLD, tau=FAKE, patience=0, counters=FAKE, n_counters=10)
     assert f(None, ctypes.byref(th), FAKE, None, None, 10, 1, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
-    th = L.DashSel(L.DASH_SEL_THRESHOLD, 0, 0, FAKE, 2, FAKE, 0, 0)
+    assert "patience" in _last(lib)
+    th = _sel(L.DASH_SEL_THRESHOLD, tau=FAKE, counters=FAKE, n_counters=0)
+    assert f(None, ctypes.byref(th), FAKE, None, None, 10, 1, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
+    assert "n_counters" in _last(lib)
+    th = _sel(L.DASH_SEL_THRESHOLD, tau=FAKE, counters=FAKE, n_counters=9)  # rows are positions 0..9
+    assert f(None, ctypes.byref(th), FAKE, None, None, 10, 1, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
+    assert "n_counters" in _last(lib)
+    th = _sel(L.DASH_SEL_THRESHOLD, tau=FAKE, counters=FAKE, n_counters=10)
     assert f(None, ctypes.byref(th), FAKE, FAKE, None, 10, 1, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
     assert "alias" in _last(lib)
-    bad = L.DashSel(9, 0, 0, None, 2, None, 0, 0)
+    bad = _sel(9)
     assert f(None, ctypes.byref(bad), FAKE, None, None, 10, 1, FAKE, None, None, None, 0, None) == L.DASH_E_INVAL
+
+
+def test_keep_count_matches_the_oracle(lib, golden_dir):
+    """dash_keep_count / dash_percentile_rank against the hand-worked counts and
+    the oracle's K_eff (which the fixtures pin)."""
+    import json
+    import oracle
+    c = json.load(open(os.path.join(golden_dir, "counts.json")))
+    for e in c["keep"]:
+        assert dash.keep_count(e["S"], e["keep"]) == e["k"]
+    for e in c["rank"]:
+        assert dash.percentile_rank(e["S"], e["pct"]) == e["r"]
+    for e in c.get("forced", []):
+        assert dash.keep_count(e["T"], e["keep"], e["f"], e["l"]) == e["k"]
+    for T in (0, 1, 7, 96, 97, 512, 8192, 131072):
+        for keep in (0.0, 0.3, 0.333, 0.5, 0.667, 1.0):
+            for fl in ((0, 0), (64, 32), (1, 0), (0, 1)):
+                if sum(fl) <= T:
+                    assert dash.keep_count(T, keep, *fl) == oracle.effective_keep_count(T, keep, *fl)
+        if T >= 1:
+            for pct in (0, 1, 30, 50, 99, 100):
+                assert dash.percentile_rank(T, pct) == oracle.percentile_rank(T, pct)
+    out = ctypes.c_int(-5)
+    assert lib.dash_keep_count(10, 1.5, 0, 0, ctypes.byref(out)) == L.DASH_E_INVAL and out.value == -5
+    assert lib.dash_keep_count(10, 0.5, 6, 5, ctypes.byref(out)) == L.DASH_E_INVAL
+    assert lib.dash_keep_count(-1, 0.5, 0, 0, ctypes.byref(out)) == L.DASH_E_INVAL
+    assert lib.dash_keep_count(10, float("nan"), 0, 0, ctypes.byref(out)) == L.DASH_E_INVAL
+    assert lib.dash_keep_count(10, 0.5, 0, 0, None) == L.DASH_E_INVAL
+    assert lib.dash_percentile_rank(0, 30, ctypes.byref(out)) == L.DASH_E_INVAL
+    assert lib.dash_percentile_rank(10, 101, ctypes.byref(out)) == L.DASH_E_INVAL
+
+
+def test_kv_extent_limit(lib):
+    """One sample's K must stay below 4 GiB (32-bit buffer offsets in the
+    attention kernel): S * Hkv * D * 2 = 2^32 is refused, one row less passes the
+    shape check (and then fails on the NULL pointers)."""
+    f = lib.dash_attn_layer
+    big = _shape(S=1 << 21, Hq=8, Hkv=8, D=128, hidden=1024)
+    assert f(None, ctypes.byref(big), *([FAKE] * 6), None, None, 0, None) == L.DASH_E_SHAPE
+    assert "4 GiB" in _last(lib)
+    ok = _shape(S=(1 << 21) - 1, Hq=8, Hkv=8, D=128, hidden=1024)
+    assert f(None, ctypes.byref(ok), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == L.DASH_E_INVAL
+    f32 = _shape(S=1 << 20, Hq=8, Hkv=8, D=128, hidden=1024, dtype=L.DASH_F32)
+    assert f(None, ctypes.byref(f32), *([FAKE] * 6), None, None, 0, None) == L.DASH_E_SHAPE
 
 
 def test_compact_validation(lib):
@@ -173,8 +240,8 @@ def test_ragged_validation(lib):
     assert f(None, ctypes.byref(s), FAKE, 100, *ptrs, FAKE, None, 0, None) == L.DASH_E_WORKSPACE
     assert f(None, ctypes.byref(s), FAKE, 0, *ptrs, None, None, 0, None) == L.DASH_OK
     g = lib.dash_select_ragged
-    top = L.DashSel(L.DASH_SEL_TOPK, 0, 0, None, 2, None, 0, 0)
-    assert g(None, ctypes.byref(L.DashSel(L.DASH_SEL_ORDER_STAT, 0, 1, None, 2, None, 0, 0)), FAKE, 10, 2, FAKE,
+    top = _sel(L.DASH_SEL_TOPK)
+    assert g(None, ctypes.byref(_sel(L.DASH_SEL_ORDER_STAT, rank=1)), FAKE, 10, 2, FAKE,
              FAKE, 8, 5, FAKE, None) == L.DASH_E_INVAL
     assert g(None, ctypes.byref(top), FAKE, 10, 2, FAKE, FAKE, 11, 5, FAKE, None) == L.DASH_E_INVAL  # max_n > n_total
     assert g(None, ctypes.byref(top), FAKE, 10, 2, None, FAKE, 8, 5, FAKE, None) == L.DASH_E_INVAL
@@ -253,7 +320,9 @@ def test_workspace_size(lib):
     s = _shape(hidden=3584, S=8192, Hq=28, Hkv=4)
     n = lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(s), 8192)
     assert n >= 8192 * 4
-    assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(s), 8192) == 0
+    # selection: one int32 NaN count per row (B rows), at least 256 bytes
+    assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(_shape(B=1)), 8192) == 256
+    assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(_shape(B=100)), 8192) == 512
     assert lib.dash_workspace_size(None, 17, ctypes.byref(s), 8192) == 0
     assert lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(_shape(D=33)), 8192) == 0
 

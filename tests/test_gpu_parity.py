@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_par
 from workload import WORKLOADS, SCORE_KINDS, layer_inputs, round_bf16, score_vector
 
 pytestmark = pytest.mark.gpu
@@ -123,7 +124,7 @@ def test_topk_forced_bit_exact(dash, kind, n):
     s = score_vector(kind, n, seed=7 * n + 3)
     sd = torch.from_numpy(s).cuda()
     for f, l in _forced_cases(n):
-        ks = {f + l, min(n, f + l + 1), dash.effective_keep(n, 0.333, f, l), n}
+        ks = {f + l, min(n, f + l + 1), oracle.effective_keep_count(n, 0.333, f, l), n}
         for k in sorted(ks):
             say("topk forced", kind, n, f, l, k)
             idx = torch.full((max(k, 1),), -7, dtype=torch.int32, device="cuda")
@@ -135,8 +136,8 @@ def test_topk_forced_bit_exact(dash, kind, n):
 @pytest.mark.parametrize("rows", [24, 70])
 def test_topk_forced_batched_and_pos(dash, rows):
     n, f, l = 3000, 64, 32
-    k = dash.effective_keep(n, 0.333, f, l)
-    assert k == oracle.effective_keep_count(n, 0.333, f, l)
+    k = oracle.effective_keep_count(n, 0.333, f, l)
+    assert k == dash.keep_count(n, 0.333, f, l)
     s = np.stack([score_vector("fewvalues" if r % 2 else "normal", n, seed=100 + r) for r in range(rows)])
     idx = torch.empty(rows, k, dtype=torch.int32, device="cuda")
     say("topk forced batched", rows, n, k)
@@ -242,6 +243,105 @@ def test_threshold_chain_of_layers(dash):
         np.testing.assert_array_equal(cd.cpu().numpy(), c_h)
 
 
+def test_threshold_positions_outside_counters_are_dropped(dash):
+    """A row whose position lies outside the counters array is not emitted and
+    touches no counter; the other rows follow the threshold step unchanged."""
+    n, n_counters = 3000, 2500
+    rng = np.random.default_rng(21)
+    pos = np.sort(rng.choice(3400, n, replace=False)).astype(np.int32)  # some positions >= n_counters
+    s = score_vector("normal", n, seed=21)
+    counters = rng.integers(0, 2, n_counters).astype(np.uint8)
+    tau = np.float32(0.6)
+    cd = torch.from_numpy(counters.copy()).cuda()
+    out = torch.full((n,), -5, dtype=torch.int32, device="cuda")
+    nout = torch.zeros(4, dtype=torch.int32, device="cuda")
+    dash.dash_select(torch.from_numpy(s).cuda(), out, mode=dash.DASH_SEL_THRESHOLD,
+                     tau=torch.tensor([tau], device="cuda"), patience=2, counters=cd,
+                     pos=torch.from_numpy(pos).cuda(), n_max=n, n_out=nout)
+    torch.cuda.synchronize()
+    inside = pos < n_counters
+    assert not np.all(inside)
+    exp_pos, exp_c = oracle.threshold_step(s[inside], pos[inside], counters, float(tau), 2)
+    m = int(nout[0].item())
+    assert m == exp_pos.shape[0]
+    np.testing.assert_array_equal(out.cpu().numpy()[:m], exp_pos)
+    np.testing.assert_array_equal(cd.cpu().numpy(), exp_c)
+
+
+@pytest.mark.parametrize("n_max", [5000, 70000])
+def test_topk_device_count(dash, n_max):
+    """Top-k over the first n = *n_dev scores of a row of capacity n_max: min(k, n)
+    kept (forced ends shrink with it), the kept count written to n_out, the
+    outputs past it untouched; bit-exact against the oracle on the first n."""
+    s = score_vector("bf16ties", n_max, seed=n_max)
+    sd = torch.from_numpy(s).cuda()
+    for n in (0, 1, 777, n_max - 1234, n_max, n_max + 9):
+        for k, f, l in ((100, 0, 0), (2000, 64, 32), (n_max - 1, 0, 0), (0, 0, 0), (40, 30, 10)):
+            nc = min(max(n, 0), n_max)
+            kk = min(k, nc)
+            ff = min(f, kk)
+            ll = min(l, kk - ff)
+            say("topk device count", n_max, n, k, f, l)
+            idx = torch.full((max(k, 1),), -7, dtype=torch.int32, device="cuda")
+            nd = torch.tensor([n], dtype=torch.int32, device="cuda")
+            nout = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+            st = dash.select_status(1)
+            dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, n_dev=nd, n_max=n_max, n_out=nout,
+                             keep_first=f, keep_last=l, status=st)
+            torch.cuda.synchronize()
+            assert int(nout[0].item()) == kk
+            got = idx.cpu().numpy()
+            np.testing.assert_array_equal(got[:kk], oracle.select_topk_forced(s[:nc], kk, ff, ll))
+            assert np.all(got[kk:k] == -7)
+            assert int(st[0].item()) == 0
+
+
+def test_select_nan_status(dash):
+    """The NaN count of every selection mode (one int32 per row in the
+    workspace) equals the number of NaN scores the call ranks or updates."""
+    def nans(a):
+        return int(np.isnan(a).sum())
+    # single rows: register-resident (<= 32768) and long rows, plain and forced
+    for n in (1, 4097, 32768, 65536 + 17):
+        s = score_vector("special", n, seed=n + 3)
+        sd = torch.from_numpy(s).cuda()
+        for k, f, l in ((n // 2, 0, 0), (n, 0, 0), (min(n, 200), min(n, 64), 0), (0, 0, 0)):
+            st = torch.full((64,), -1, dtype=torch.int32, device="cuda")
+            idx = torch.empty(max(k, 1), dtype=torch.int32, device="cuda")
+            dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, keep_first=f, keep_last=l, status=st)
+            torch.cuda.synchronize()
+            assert int(st[0].item()) == nans(s), (n, k, f)
+            if k:
+                np.testing.assert_array_equal(idx.cpu().numpy()[:k], oracle.select_topk_forced(s, k, f, l))
+        tau = torch.empty(1, dtype=torch.float32, device="cuda")
+        st = torch.full((64,), -1, dtype=torch.int32, device="cuda")
+        dash.dash_select(sd, mode=dash.DASH_SEL_ORDER_STAT, rank=max(1, n // 3), tau_out=tau, status=st)
+        torch.cuda.synchronize()
+        assert int(st[0].item()) == nans(s)
+        st = torch.full((64,), -1, dtype=torch.int32, device="cuda")
+        out = torch.empty(n, dtype=torch.int32, device="cuda")
+        nout = torch.zeros(1, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(n, dtype=torch.uint8, device="cuda")
+        dash.dash_select(sd, out, mode=dash.DASH_SEL_THRESHOLD, tau=torch.tensor([0.3], device="cuda"), patience=2,
+                         counters=cnt, n_max=n, n_out=nout, status=st)
+        torch.cuda.synchronize()
+        assert int(st[0].item()) == nans(s)
+        exp_pos, exp_c = oracle.threshold_step(s, np.arange(n), np.zeros(n, np.uint8), 0.3, 2)
+        np.testing.assert_array_equal(out.cpu().numpy()[:int(nout[0].item())], exp_pos)
+    # batches: one wave per row (>= 256 rows of <= 8192) and one workgroup per row
+    for rows, n in ((300, 2048), (40, 3000)):
+        s = np.stack([score_vector("special" if r % 3 else "normal", n, seed=r) for r in range(rows)])
+        st = dash.select_status(rows)
+        idx = torch.empty(rows, n // 2, dtype=torch.int32, device="cuda")
+        dash.dash_select(torch.from_numpy(s).cuda(), idx, mode=dash.DASH_SEL_TOPK, k=n // 2, n_max=n, rows=rows,
+                         status=st)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(st.cpu().numpy()[:rows], np.isnan(s).sum(axis=1))
+        got = idx.cpu().numpy()
+        for r in range(0, rows, 7):
+            np.testing.assert_array_equal(got[r], oracle.select_topk(s[r], n // 2))
+
+
 # ---------------------------------------------------------------------------
 # compaction (bit-exact)
 # ---------------------------------------------------------------------------
@@ -335,19 +435,22 @@ def _run_layer(dash, x, dtype=torch.bfloat16, with_score=True):
     return host(O), host(U), (host(score) if with_score else None)
 
 
-@pytest.mark.parametrize("tile_n", ["auto", "224", "256"])
 @pytest.mark.parametrize("S,Hq,Hkv,D,hidden", [
     (1, 2, 1, 128, 256), (77, 4, 2, 64, 128), (300, 8, 2, 128, 384), (640, 28, 4, 128, 3584),
     (1000, 32, 8, 128, 4096), (129, 7, 7, 64, 200),
+    # 4096 rows x 4096 columns: the W_o GEMM launcher takes its 256-wide tiles
+    # (the 224-wide grid would spill into a second wave of workgroups); the
+    # shapes above take the 224-wide ones
+    (4096, 32, 8, 128, 4096),
 ])
-def test_attn_layer_bf16(dash, monkeypatch, S, Hq, Hkv, D, hidden, tile_n):
-    """tile_n forces the W_o GEMM's 224- or 256-column tile kernel (auto: the launcher's choice)."""
-    if tile_n != "auto":
-        monkeypatch.setenv("DASH_WO_TILE_N", tile_n)
+def test_attn_layer_bf16(dash, S, Hq, Hkv, D, hidden):
     x = _layer(S, Hq, Hkv, D, hidden, seed=S)
-    say("attn_layer bf16", S, Hq, Hkv, D, hidden, "tile_n", tile_n)
+    say("attn_layer bf16", S, Hq, Hkv, D, hidden)
     O, U, score = _run_layer(dash, x)
-    O_ref, U_ref, s_ref = oracle.attention_layer(x["Q"], x["K"], x["V"], x["Wo"])
+    if S >= 2048:
+        O_ref, U_ref, s_ref = oracle_par.layer_rows(x, np.arange(S))
+    else:
+        O_ref, U_ref, s_ref = oracle.attention_layer(x["Q"], x["K"], x["V"], x["Wo"])
     assert maxrel(O, O_ref) <= TOL_BF16
     assert maxrel(U, U_ref) <= TOL_BF16
     assert np.all(np.abs(score - s_ref) <= TOL_SCORE * s_ref)
@@ -544,8 +647,10 @@ def test_one_shot_step_batched(dash, dtype):
     Wo = [hostl[l][0]["Wo"] for l in range(2)]  # one weight per layer, shared by the batch
     layers = [LayerTensors(*(dev_t(np.stack([h[n] for h in hostl[l]]), tdt) for n in ("Q", "K", "V")),
                            dev_t(Wo[l].T, tdt)) for l in range(2)]
-    say("one-shot batched", dtype, w.S, w.k)
-    st = OneShotStack(layers, halt_layer=0, k=w.k)
+    k = oracle.topk_count(w.S, w.keep)
+    say("one-shot batched", dtype, w.S, k)
+    st = OneShotStack(layers, halt_layer=0, keep=w.keep)
+    assert st.k == k
     st.run()
     torch.cuda.synchronize()
     for b in range(B):
@@ -555,9 +660,10 @@ def test_one_shot_step_batched(dash, dtype):
         score = host(st.score)[b]
         assert np.all(np.abs(score - s_ref) <= TOL_SCORE * s_ref)
         idx = st.idx.cpu().numpy()[b]
-        np.testing.assert_array_equal(idx, oracle.select_topk(score, w.k))
+        np.testing.assert_array_equal(idx, oracle.select_topk(score, k))
         Oa = oracle.attn_active(x1["Q"], x1["K"], x1["V"], idx, "active")
         assert maxrel(host(st.Ua)[b], oracle.output_projection(Oa, Wo[1])) <= tol
+    assert np.all(st.status.cpu().numpy()[:B] == 0)  # no NaN score at the decision
 
 
 @pytest.mark.parametrize("mode", ["active", "all"])
@@ -570,8 +676,8 @@ def test_gather_once_step_matches_step(dash, mode):
     hostl = [layer_inputs(w, 40, l) for l in range(3)]
     layers = [LayerTensors(*(dev_t(h[n]) for n in ("Q", "K", "V")), dev_t(h["Wo"].T)) for h in hostl]
     kv = dash.DASH_KV_ACTIVE if mode == "active" else dash.DASH_KV_ALL
-    say("gather once", mode, w.S, w.k)
-    st = OneShotStack(layers, halt_layer=0, k=w.k, kv_mode=kv)
+    say("gather once", mode, w.S, w.keep)
+    st = OneShotStack(layers, halt_layer=0, keep=w.keep, kv_mode=kv)
     st.run()
     torch.cuda.synchronize()
     Ua_ref, idx_ref = st.Ua.clone(), st.idx.clone()
@@ -618,7 +724,9 @@ def test_tiny_fp32_one_shot_step(dash, seed):
     w = WORKLOADS[0]
     hostl, devl = _stack_inputs(w, seed, "f32")
     say("tiny fp32 step seed", seed)
-    st = OneShotStack(devl, halt_layer=0, k=w.k)
+    k = oracle.topk_count(w.S, w.keep)
+    st = OneShotStack(devl, halt_layer=0, keep=w.keep)
+    assert st.k == k
     st.run()
     torch.cuda.synchronize()
     O_ref, U_ref, s_ref = oracle.attention_layer(hostl[0]["Q"], hostl[0]["K"], hostl[0]["V"], hostl[0]["Wo"])
@@ -626,8 +734,8 @@ def test_tiny_fp32_one_shot_step(dash, seed):
     score = host(st.score)
     assert np.all(np.abs(score - s_ref) <= TOL_SCORE * s_ref)
     idx = st.idx.cpu().numpy()
-    np.testing.assert_array_equal(idx, oracle.select_topk(score, w.k))
-    selection_within_cut(idx, s_ref, w.k)
+    np.testing.assert_array_equal(idx, oracle.select_topk(score, k))
+    selection_within_cut(idx, s_ref, k)
     Oa = oracle.attn_active(hostl[1]["Q"], hostl[1]["K"], hostl[1]["V"], idx, "active")
     Ua = oracle.output_projection(Oa, hostl[1]["Wo"])
     assert maxrel(host(st.Oa), Oa) <= TOL_F32
@@ -641,8 +749,9 @@ def test_tiny_fp32_one_shot_step_forced(dash):
     w = WORKLOADS[0]
     hostl, devl = _stack_inputs(w, 0, "f32")
     k = oracle.effective_keep_count(w.S, w.keep, 64, 32)
-    assert k == dash.effective_keep(w.S, w.keep, 64, 32) == 304
-    st = OneShotStack(devl, halt_layer=0, k=k, keep_first=64, keep_last=32)
+    assert k == 304
+    st = OneShotStack(devl, halt_layer=0, keep=w.keep, keep_first=64, keep_last=32)
+    assert st.k == k
     st.run()
     torch.cuda.synchronize()
     score, idx = host(st.score), st.idx.cpu().numpy()
@@ -871,7 +980,9 @@ def test_qwen_s8192_one_shot_step(dash, seed):
     w = WORKLOADS[1]
     hostl, devl = _stack_inputs(w, seed, "bf16")
     say("qwen s8192 step seed", seed)
-    st = OneShotStack(devl, halt_layer=0, k=w.k)
+    k = oracle.topk_count(w.S, w.keep)
+    st = OneShotStack(devl, halt_layer=0, keep=w.keep)
+    assert st.k == k
     st.run()
     torch.cuda.synchronize()
     score, idx = host(st.score), st.idx.cpu().numpy()
@@ -880,8 +991,8 @@ def test_qwen_s8192_one_shot_step(dash, seed):
     assert maxrel(host(st.O), O_ref) <= TOL_BF16
     assert maxrel(U, U_ref) <= TOL_BF16
     assert np.all(np.abs(score - s_ref) <= TOL_SCORE * s_ref)
-    np.testing.assert_array_equal(idx, oracle.select_topk(score, w.k))
-    nd = selection_within_cut(idx, s_ref, w.k)
+    np.testing.assert_array_equal(idx, oracle.select_topk(score, k))
+    nd = selection_within_cut(idx, s_ref, k)
     say("qwen s8192: tokens differing from the oracle selection:", nd)
     Oa = oracle.attn_active(hostl[1]["Q"], hostl[1]["K"], hostl[1]["V"], idx, "active")
     Ua = oracle.output_projection(Oa, hostl[1]["Wo"])

@@ -56,21 +56,11 @@ class Workload:
     layers: int
     mode: str             # "topk" (one-shot) or "threshold"
     halt_layer: int = 0   # one-shot: layers 0..halt_layer run full length
-    keep: float = 0.5     # one-shot keep ratio
+    keep: float = 0.5     # one-shot keep ratio (the kept count is the method's to derive)
     kv_mode: str = "active"
-    tau_pct: int = 30            # threshold: tau = nearest-rank percentile of layer-0 scores
+    tau_pct: int = 30            # threshold: tau = this percentile of the layer-0 scores
     patience: int = 2            # threshold: consecutive layers below tau before halting
     clustered: bool = False
-
-    @property
-    def k(self) -> int:
-        """Kept count for the one-shot policy: floor(keep * S), computed in double."""
-        return int(math.floor(self.keep * self.S))
-
-    @property
-    def tau_rank(self) -> int:
-        """1-based rank of the threshold among ascending layer-0 scores: ceil(pct * S / 100)."""
-        return max(1, -(-self.tau_pct * self.S // 100))
 
     def scaled(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -98,8 +88,12 @@ def _stream(seed: int, cfg_id: int, layer: int, tensor_id: int) -> np.random.See
     return np.random.SeedSequence([seed, cfg_id, layer, tensor_id])
 
 
-def normal_f32(ss: np.random.SeedSequence, n: int, std: float = 1.0) -> np.ndarray:
-    """n iid N(0, std^2) float32 values, chunked so the result is thread-count independent."""
+def normal_f32(ss: np.random.SeedSequence, n: int, std: float = 1.0, finish=None) -> np.ndarray:
+    """n iid N(0, std^2) float32 values, chunked so the result is thread-count independent.
+
+    finish(lo, hi, x), if given, is applied in place to each chunk x = out[lo:hi]
+    right after it is drawn (on the worker thread that drew it); it must be
+    elementwise, so the result does not depend on the chunking."""
     out = np.empty(n, dtype=np.float32)
     nchunks = max(1, (n + CHUNK - 1) // CHUNK)
     kids = ss.spawn(nchunks)
@@ -110,6 +104,8 @@ def normal_f32(ss: np.random.SeedSequence, n: int, std: float = 1.0) -> np.ndarr
         g.standard_normal(hi - lo, dtype=np.float32, out=out[lo:hi])
         if std != 1.0:
             out[lo:hi] *= np.float32(std)
+        if finish is not None:
+            finish(lo, hi, out[lo:hi])
 
     if nchunks == 1:
         fill(0)
@@ -129,8 +125,12 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return r.view(np.float32)
 
 
-def _finish(w: Workload, x: np.ndarray) -> np.ndarray:
-    return round_bf16(x) if w.dtype == "bf16" else x
+def _round_bf16_inplace(lo: int, hi: int, x: np.ndarray) -> None:
+    x[:] = round_bf16(x)
+
+
+def _finish(w: Workload):
+    return _round_bf16_inplace if w.dtype == "bf16" else None
 
 
 def span_slots(w: Workload, seed: int) -> np.ndarray:
@@ -155,20 +155,34 @@ def v_row_scale(w: Workload, seed: int, layer: int) -> np.ndarray:
 
 
 def layer_inputs(w: Workload, seed: int, layer: int, parts=("Q", "K", "V", "Wo")) -> dict:
-    """Q [S,Hq,D], K and V [S,Hkv,D], Wo [Hq*D, hidden] (U = O @ Wo), all float32 arrays."""
+    """Q [S,Hq,D], K and V [S,Hkv,D], Wo [Hq*D, hidden] (U = O @ Wo), all float32 arrays.
+
+    bf16 workloads: every value rounded to the nearest bf16 (V after its row
+    scale is applied)."""
     out = {}
     S, Hq, Hkv, D, hid = w.S, w.Hq, w.Hkv, w.D, w.hidden
+    fin = _finish(w)
     if "Q" in parts:
-        out["Q"] = _finish(w, normal_f32(_stream(seed, w.cfg_id, layer, T_Q), S * Hq * D)).reshape(S, Hq, D)
+        out["Q"] = normal_f32(_stream(seed, w.cfg_id, layer, T_Q), S * Hq * D, finish=fin).reshape(S, Hq, D)
     if "K" in parts:
-        out["K"] = _finish(w, normal_f32(_stream(seed, w.cfg_id, layer, T_K), S * Hkv * D)).reshape(S, Hkv, D)
+        out["K"] = normal_f32(_stream(seed, w.cfg_id, layer, T_K), S * Hkv * D, finish=fin).reshape(S, Hkv, D)
     if "V" in parts:
-        v = normal_f32(_stream(seed, w.cfg_id, layer, T_V), S * Hkv * D).reshape(S, Hkv, D)
-        v *= v_row_scale(w, seed, layer)[:, None, None]
-        out["V"] = _finish(w, v)
+        scale = v_row_scale(w, seed, layer)
+        row = Hkv * D
+
+        def scale_then_round(lo: int, hi: int, x: np.ndarray) -> None:
+            # element e of the flat [S, Hkv, D] array belongs to token e // (Hkv * D)
+            tok = np.arange(lo, hi, dtype=np.int64) // row
+            x *= scale[tok]
+            if fin is not None:
+                fin(lo, hi, x)
+
+        out["V"] = normal_f32(_stream(seed, w.cfg_id, layer, T_V), S * Hkv * D,
+                              finish=scale_then_round).reshape(S, Hkv, D)
     if "Wo" in parts:
         std = 1.0 / math.sqrt(hid)
-        out["Wo"] = _finish(w, normal_f32(_stream(seed, w.cfg_id, layer, T_WO), Hq * D * hid, std)).reshape(Hq * D, hid)
+        out["Wo"] = normal_f32(_stream(seed, w.cfg_id, layer, T_WO), Hq * D * hid, std,
+                               finish=fin).reshape(Hq * D, hid)
     return out
 
 
