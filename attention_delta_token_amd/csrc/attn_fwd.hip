@@ -14,23 +14,27 @@
 //     longer queries) — forum summary "DASH：通过注意力动态监测实现长上下文高效预填充",
 //     section 选择性停止机制.
 //
-// bf16 kernel: 256 threads = 4 waves, 128 queries of one q-head per workgroup
-// (32 per wave), 64 keys per step.  Scores are computed transposed,
-// S^T = K · Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one query and
-// 32 of the step's keys: the softmax max and sum stay in registers, and the
-// partner half-wave's maximum is fetched only on the rare steps where the lazy
-// reference maximum has to move.  The query is pre-scaled into exp2
+// bf16 kernel: 512 threads = 8 waves, 256 queries of one q-head per workgroup
+// (32 per wave), 64 keys per step, one workgroup per CU.  Scores are computed
+// transposed, S^T = K · Q^T on v_mfma_f32_32x32x16_bf16, so each lane owns one
+// query and 32 of the step's keys: the softmax max and sum stay in registers,
+// and the partner half-wave's maximum is fetched only on the rare steps where
+// the lazy reference maximum has to move.  The query is pre-scaled into exp2
 // units and the score accumulators start at -m, so P is a bare exp2.  The
-// output is accumulated transposed too, O^T += V^T · P^T, where P^T is fed
-// straight from the score accumulators (rounded to bf16) as the B operand and
-// V^T comes from transposing LDS reads (ds_read_b64_tr_b16) of the V tile.
-// K and V tiles go from global memory straight into LDS (buffer loads to LDS,
-// no register staging; rows past the key count read as zeros through the
-// buffer range) into a ring of two K and two V tiles, K two steps ahead and V
-// one; rows are XOR-swizzled so the operand reads are free of bank conflicts,
-// and one barrier separates steps.  Workgroups are ordered heaviest-first
-// (causal work grows with the query position) and the q-heads that share a
-// kv-head are placed on the same XCD so they share its L2.
+// output is accumulated transposed too, O^T += V^T · P^T, with P^T (rounded to
+// bf16) as the B operand and V^T from transposing LDS reads
+// (ds_read_b64_tr_b16).  The eight waves form two groups that alternate, one
+// phase apart, between matrix phases (the scores of the next tile and P V of
+// the current one) and softmax phases, so the two waves sharing a SIMD keep
+// its matrix pipe fed in turn (details at the kernel).  K and V tiles go from
+// global memory straight into LDS (buffer loads to LDS, no register staging;
+// rows past the key count read as zeros through the buffer range); rows are
+// XOR-swizzled so the operand reads are free of bank conflicts.  Workgroups
+// are ordered heaviest-first (causal work grows with the query position) and
+// the q-heads that share a kv-head are placed on the same XCD so they share
+// its L2.
+#include <type_traits>
+
 #include "dash_common.h"
 #include "dash_kernels.h"
 
@@ -38,8 +42,6 @@ namespace dash {
 
 namespace {
 
-constexpr int kAttnThreads = 256;
-constexpr int kBQ = 128;  // queries per workgroup
 constexpr int kBKV = 64;  // keys per step
 constexpr float kLazyLog2 = 8.0f;  // slack of the lazily updated softmax maximum
 
@@ -79,10 +81,7 @@ struct AttnCfg {
   static constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
   static constexpr int kRowsPerLine = 256 / kRowBytes;  // rows per 64-bank line
   static constexpr int kTileBytes = kBKV * kRowBytes;   // one K or V tile
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / (kAttnThreads / 64);
   static constexpr int kRowsPerKiB = 1024 / kRowBytes;
-  static constexpr int kTotal = 4 * kTileBytes;         // K[2] + V[2]
-  static constexpr int kORow = D + 8;                   // output staging row (bf16 elements)
 };
 
 // K rows: chunk c of row r sits at slot c ^ ((r / kRowsPerLine) % kChunks), so
@@ -102,60 +101,107 @@ __device__ __forceinline__ int v_slot(int r, int c) {
   return c ^ (4 * ((r / C::kRowsPerLine) % (C::kChunks / 4)));
 }
 
-// Direct global->LDS loads of one K or V tile: each wave moves kLoadsPerWave
-// KiB; lane l of a 1 KiB load lands at byte 16*l, i.e. row l / kChunks, slot
-// l % kChunks, and fetches the chunk the swizzle puts there.
-template <int D, bool IsV>
-struct TileLoader {
-  using C = AttnCfg<D>;
-  uint32_t voff[C::kLoadsPerWave];
-  __device__ __forceinline__ void init(int kv_ld) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      const int q = wave + (kAttnThreads / 64) * i;
-      const int row = q * C::kRowsPerKiB + lane / C::kChunks;
-      const int slot = lane % C::kChunks;
-      const int chunk = IsV ? v_slot<D>(row, slot) : k_slot<D>(row, slot);
-      voff[i] = static_cast<uint32_t>(row * kv_ld * 2 + chunk * 16);
-    }
-  }
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, unsigned char* tile, uint32_t tile_off) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-    for (int i = 0; i < C::kLoadsPerWave; ++i) {
-      const int q = wave + (kAttnThreads / 64) * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(tile + q * 1024), 16,
-                                               voff[i], tile_off, 0, 0);
-    }
-  }
-};
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel, two wave groups in alternation.  512 threads = 8 waves, 256
+// queries of one q-head per workgroup (32 per wave), one workgroup per CU, so
+// each SIMD holds two waves; they are made one wave of group 0 and one of
+// group 1.  Every wave runs the same sequence of phases for key tile j:
+//   M(j): the scores of tile j+1 (S^T = K Q^T, 16 MFMAs) and O^T += V^T P^T
+//         for tile j (16 MFMAs), at raised wave priority;
+//   V(j+1): mask, lazy maximum, exp2, bf16 packing and row sum of tile j+1
+//         (vector ALU only), plus this group's share of the tile loads;
+// with a workgroup barrier after each phase.  Group 1 starts one phase later
+// than group 0, so while one wave of a SIMD issues matrix instructions its
+// partner runs the softmax of the other group; the matrix pipe sees the two
+// waves' MFMA phases back to back.
+// K and V tiles sit in rings of three LDS buffers each, every buffer its own
+// __shared__ array and the loop unrolled by three so each buffer is fixed at
+// compile time: the compiler then sees that a transposing V read does not
+// touch the buffer a tile load is filling and does not wait for the load.
+// Group 0 loads K tiles during its V phases (K(t+2) while publishing K(t+1));
+// group 1 loads V tiles (V(t+2), publishing V(t+1)).
+// ---------------------------------------------------------------------------
+constexpr int kPPThreads = 512;
+constexpr int kPPQ = 256;  // queries per workgroup
+
+// A K or V tile moved by one group of four waves: the wave in group slot gw
+// moves 1 KiB pieces gw, gw + 4, ...: lane l of a piece lands at byte 16*l,
+// i.e. row l / kChunks, slot l % kChunks, and fetches the chunk the swizzle
+// puts there.  One loader per wave, set up for the tiles its group moves.
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2)
-void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                          const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_dev, int n_q_max,
-                          int n_kv, int Hq, int Hkv, float c_log2, AttnBatch bt) {
+struct GroupTileLoader {
   using C = AttnCfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kTotal];
+  static constexpr int kLoads = C::kTileBytes / 1024 / 4;
+  uint32_t voff[kLoads];
+  int gw;  // this wave's slot (0-3) within its group
+  __device__ __forceinline__ void init(int kv_ld, bool is_v, int slot_in_group) {
+    gw = slot_in_group;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int q = gw + 4 * i;
+      const int row = q * C::kRowsPerKiB + lane / C::kChunks;
+      const int slot = lane % C::kChunks;
+      const int chunk = is_v ? v_slot<D>(row, slot) : k_slot<D>(row, slot);
+      voff[i] = static_cast<uint32_t>(row * kv_ld * 2 + chunk * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t src, unsigned char* tile, uint32_t tile_off) const {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int q = gw + 4 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(tile + q * 1024), 16,
+                                               voff[i], tile_off, 0, 0);
+    }
+  }
+};
+
+template <int N>
+using Slot = std::integral_constant<int, N>;
+
+template <int D>
+__global__ __launch_bounds__(kPPThreads, 2)
+void attn_fwd_bf16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                             const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                             const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_dev, int n_q_max,
+                             int n_kv, int Hq, int Hkv, float c_log2, AttnBatch bt) {
+  using C = AttnCfg<D>;
+  // The LDS allocator places these arrays in name order: the V ring (named to
+  // come first) then sits below 64 KiB, so its transposing reads carry the
+  // buffer's place as an immediate offset instead of an address add.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a_v0[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a_v1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a_v2[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b_k0[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b_k1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b_k2[C::kTileBytes];
+  auto kbuf = [&](auto n) -> unsigned char* {
+    if constexpr (decltype(n)::value == 0) return lds_b_k0;
+    else if constexpr (decltype(n)::value == 1) return lds_b_k1;
+    else return lds_b_k2;
+  };
+  auto vbuf = [&](auto n) -> unsigned char* {
+    if constexpr (decltype(n)::value == 0) return lds_a_v0;
+    else if constexpr (decltype(n)::value == 1) return lds_a_v1;
+    else return lds_a_v2;
+  };
 
   const int64_t b = blockIdx.y;
   const int q_ld = Hq * D;
   const int kv_ld = Hkv * D;
   int n_q, pos_base;
   bt.locate(b, n_dev, n_q_max, n_kv, q_ld, kv_ld, Q, O, q_pos, K, V, n_q, pos_base);
-  const int n_qt = (n_q_max + kBQ - 1) / kBQ;
+  const int n_qt = (n_q_max + kPPQ - 1) / kPPQ;
   const int g = Hq / Hkv;
   int qt, h;
   attn_tile_of(blockIdx.x, n_qt, Hkv, g, qt, h);
-  const int q0 = qt * kBQ;
+  const int q0 = qt * kPPQ;
   if (q0 >= n_q) return;
   const int kvh = h / g;
   K += static_cast<int64_t>(kvh) * D;
@@ -173,6 +219,36 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
+  // Groups by SIMD: the two waves the hardware placed on each SIMD become one
+  // wave of group 0 and one of group 1 (lower wave index first), and the SIMD
+  // index is the wave's slot within its group.  The SIMD of a wave is read from
+  // the HW_ID register (bits 5:4).  Should the waves not pair up two per SIMD,
+  // the split falls back to waves 0-3 / 4-7.
+  __shared__ int simd_of[kPPThreads / 64];
+  const int my_simd = static_cast<int>((__builtin_amdgcn_s_getreg((4) | (4 << 6) | ((2 - 1) << 11))) & 3u);
+  if (lane == 0) simd_of[wave] = my_simd;
+  __syncthreads();
+  int grp = wave >> 2, gslot = wave & 3;
+  {
+    bool paired = true;
+    int rank = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      int cnt = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kPPThreads / 64; ++w2) cnt += simd_of[w2] == s2;
+      paired = paired && cnt == 2;
+    }
+#pragma unroll
+    for (int w2 = 0; w2 < kPPThreads / 64; ++w2) rank += (w2 < wave && simd_of[w2] == my_simd);
+    if (paired) {
+      grp = rank;
+      gslot = my_simd;
+    }
+  }
+  grp = __builtin_amdgcn_readfirstlane(grp);
+  gslot = __builtin_amdgcn_readfirstlane(gslot);
+
   const int qrow = q0 + wave * 32 + l32;
   const int qrow_c = min(qrow, n_q - 1);
   const int q_src = bt.q_rows ? min(max(bt.q_rows[b * bt.qp_bs + qrow_c], 0), bt.q_rows_n - 1) : qrow_c;
@@ -181,33 +257,32 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int w_last = min(q0 + wave * 32 + 31, n_q - 1);
   const int wave_pmin = q_pos ? q_pos[w_first] - pos_base : w_first;
   const int wave_pmax = q_pos ? q_pos[w_last] - pos_base : w_last;
-  const int b_last = min(q0 + kBQ - 1, n_q - 1);
+  const int b_last = min(q0 + kPPQ - 1, n_q - 1);
   const int block_pmax = q_pos ? q_pos[b_last] - pos_base : b_last;
   const int kv_end = min(n_kv, block_pmax + 1);
   const int n_tiles = (kv_end + kBKV - 1) / kBKV;
+  if (n_tiles <= 0) return;
   // Tiles this wave computes (keys k0 <= wave_pmax) and the first one that
   // holds a key past some query of the wave (needs the causal mask).
   const int n_w = min(n_tiles, wave_pmax / kBKV + 1);
   const int j_mask = min(n_w, (wave_pmin + 1) / kBKV);
 
-  unsigned char* kbuf0 = lds;
-  unsigned char* vbuf0 = lds + 2 * C::kTileBytes;
-  auto kbuf = [&](int i) { return kbuf0 + (i & 1) * C::kTileBytes; };
-  auto vbuf = [&](int i) { return vbuf0 + (i & 1) * C::kTileBytes; };
-  TileLoader<D, false> kload;
-  TileLoader<D, true> vload;
-  kload.init(kv_ld);
-  vload.init(kv_ld);
+  GroupTileLoader<D> ld;  // group 0 moves K tiles, group 1 V tiles
+  constexpr int kLoads = GroupTileLoader<D>::kLoads;
+  ld.init(kv_ld, grp == 1, gslot);
   const uint32_t tile_bytes = static_cast<uint32_t>(kBKV) * row_bytes;
 
-  // Prologue loads: K(0), K(1), V(0).
-  kload.issue(k_src, kbuf(0), 0u);
-  if (n_tiles > 1) kload.issue(k_src, kbuf(1), tile_bytes);
-  vload.issue(v_src, vbuf(0), 0u);
+  // Prologue loads: K(0), K(1) by group 0; V(0), V(1) by group 1.
+  if (grp == 0) {
+    ld.issue(k_src, lds_b_k0, 0u);
+    if (n_tiles > 1) ld.issue(k_src, lds_b_k1, tile_bytes);
+  } else {
+    ld.issue(v_src, lds_a_v0, 0u);
+    if (n_tiles > 1) ld.issue(v_src, lds_a_v1, tile_bytes);
+  }
 
-  // This lane's query as the B operand of S^T = K Q^T: 8 dims per k-step,
-  // pre-multiplied by log2(e)/sqrt(D) (rounded to bf16) so the scores come out
-  // in exp2 units.
+  // This lane's query as the B operand of S^T = K Q^T, pre-multiplied by
+  // log2(e)/sqrt(D) (rounded to bf16) so the scores come out in exp2 units.
   bf16x8 qreg[D / 16];
   {
     const uint16_t* qp = Q + static_cast<size_t>(q_src) * q_ld + h * D + hi * 8;
@@ -229,63 +304,123 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
   for (int r = 0; r < 16; ++r) m_neg[r] = 0.f;
   float l_run = 0.f;
+  u32x4 pk[4];        // P of the tile being multiplied, bf16 pairs (B operands of P V)
+  u32x4 vpre[D / 32]; // V^T operands of that tile's first key step, read ahead of its M phase
+  f32x16 s[2];        // scores of the tile after it (S^T - m, then in place through the softmax)
 
-  // K operand offsets: row kb*32 + l32, chunk 2*ks + hi (the kb term is an immediate).
   int koff[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * C::kRowBytes + 16 * k_slot<D>(l32, 2 * ks + hi);
-  // V^T operand (transposing reads): 16-lane group grp = (l32 / 16) covers d = db*32 + 16*grp .. +15;
-  // source lane j = lane % 16 reads key row kb0 + j/4, d chunk db*32 + 16*grp + 4*(j%4).
   const int tj = lane & 15;
   const int tgrp = (lane >> 4) & 1;
   int voffs[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
-    const int row = (tj >> 2) + 4 * hi;  // row within the tile for key step 0, part 0
-    const int e = db * 32 + 16 * tgrp + 4 * (tj & 3);  // first d element read
+    const int row = (tj >> 2) + 4 * hi;
+    const int e = db * 32 + 16 * tgrp + 4 * (tj & 3);
     voffs[db] = row * C::kRowBytes + 16 * v_slot<D>(row, e >> 3) + 2 * (e & 7);
   }
 
-  // S^T - m for one key tile: 2 blocks of 32 keys x this wave's 32 queries; the
-  // first MFMA of each block takes its accumulator from m_neg (-m, m = this
-  // lane's reference maximum, kept in a register block so no per-step fill is
-  // needed), so the softmax numerator is a bare exp2.
-  auto qk = [&](const unsigned char* kst, f32x16 (&s)[2], const f32x16& init) {
+  auto qk = [&](const unsigned char* kst, f32x16 (&s)[2]) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + koff[ks] + kb * 32 * C::kRowBytes);
-        s[kb] = mfma32x32x16(a, qreg[ks], ks == 0 ? init : s[kb]);
+        s[kb] = mfma32x32x16(a, qreg[ks], ks == 0 ? m_neg : s[kb]);
       }
   };
 
-  // Causal mask of a tile: keys past this lane's query position get -inf.
-  auto mask = [&](f32x16 (&s)[2], int k0) {
-    const int lim = my_pos - k0 - hi * 4;  // key offset c is visible iff c <= lim
+  auto pv = [&](const unsigned char* vst) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int stp = 0; stp < 4; ++stp) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[stp]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-        s[kb][r] = c > lim ? -__builtin_inff() : s[kb][r];
+      for (int db = 0; db < D / 32; ++db) {
+        u32x4 av;
+        if (stp == 0) {
+          av = vpre[db];
+        } else {
+          const i16x4 lo = lds_read_tr16(vst + voffs[db] + (16 * stp) * C::kRowBytes);
+          const i16x4 up = lds_read_tr16(vst + voffs[db] + (16 * stp + 8) * C::kRowBytes);
+          av = u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                     __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]};
+        }
+        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), pb, o[db]);
       }
+    }
+  };
+  // The V^T operands of the first key step of the tile in V buffer vst, read
+  // at the end of the softmax phase (the tile was published a phase earlier),
+  // so the next M phase starts on operands already in registers.
+  auto prefetch_v = [&](const unsigned char* vst) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const i16x4 lo = lds_read_tr16(vst + voffs[db]);
+      const i16x4 up = lds_read_tr16(vst + voffs[db] + 8 * C::kRowBytes);
+      vpre[db] = u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                       __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]};
+    }
   };
 
-  // Maximum of a (masked) score tile; moves the lazy reference maximum when the
-  // tile exceeds it by more than 2^kLazyLog2 in exp2 units (P then stays below
-  // 2^kLazyLog2) and rescales the accumulators for it.  Called on tile j+1 at
-  // the end of step j, so step j+1 itself needs no branch.
-  // The tile holds S - m_run; `first` marks the first tile (m_run not set yet).
-  auto update_max = [&](f32x16 (&s)[2], bool first) {
+  // M phase with both products: the scores of the next tile (s) and O += P V
+  // of the current one, their MFMAs interleaved; the LDS operand reads are
+  // kept several MFMAs ahead (scheduling groups), since the SIMD's other wave
+  // is in its vector-ALU phase and cannot cover their latency.
+  auto mphase = [&](const unsigned char* kst, const unsigned char* vst) {
+    // 2 * (D / 16) score MFMAs (two key blocks per k-step) and 4 * (D / 32)
+    // P V MFMAs (four key steps per output block): equal counts for every D
+    static_assert(2 * (D / 16) == 4 * (D / 32), "paired MFMA counts");
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 16); ++i) {
+      const int ks = i >> 1, kb = i & 1;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + koff[ks] + kb * 32 * C::kRowBytes);
+      s[kb] = mfma32x32x16(a, qreg[ks], ks == 0 ? m_neg : s[kb]);
+      {
+        const int stp = i / (D / 32), db = i % (D / 32);
+        u32x4 av;
+        if (stp == 0) {
+          av = vpre[db];
+        } else {
+          const i16x4 lo = lds_read_tr16(vst + voffs[db] + (16 * stp) * C::kRowBytes);
+          const i16x4 up = lds_read_tr16(vst + voffs[db] + (16 * stp + 8) * C::kRowBytes);
+          av = u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                     __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]};
+        }
+        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pk[stp]), o[db]);
+      }
+    }
+    // 3 LDS reads per pair of MFMAs: twelve reads ahead, then MFMA, two
+    // reads, MFMA, one read, ...
+    __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 16); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // Softmax phase of tile t held in s: causal mask where needed, the lazily
+  // updated reference maximum (rescaling O and the row sum when it moves),
+  // P = exp2(S - m), rounded to bf16 into pk, and the row sum of the rounded P.
+  auto vphase = [&](f32x16 (&s)[2], int t, bool first) {
+    if (t >= j_mask) {
+      const int lim = my_pos - t * kBKV - hi * 4;  // key offset c is visible iff c <= lim
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          s[kb][r] = c > lim ? -__builtin_inff() : s[kb][r];
+        }
+    }
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    // The two half-waves hold the same queries' other keys.  Only when some
-    // lane's own half exceeds the slack (or on the first tile) is the full
-    // row maximum needed, so the exchange sits inside the rare branch.
     if (__any(first || mx > kLazyLog2)) {
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const bool grow = first || mx > kLazyLog2;
@@ -304,129 +439,127 @@ void attn_fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
     }
-  };
-
-  // Softmax numerator of a tile in place: P = exp2(S - m_run).
-  auto softmax = [&](f32x16 (&s)[2]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(s[kb][r]);
-  };
-
-  // O^T += V^T P^T for one tile: P rounded to bf16 as the B operand; the V^T
-  // operand (8 keys of one d per lane) comes from two transposing reads.  The
-  // softmax denominator adds the same rounded P (two at a time with a bf16 dot).
-  auto pv = [&](const f32x16 (&s)[2], const unsigned char* vst) {
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float psum = 0.f;
+    // row sum of P in fp32, four independent chains (a bf16 dot product here
+    // would share the matrix unit's issue with the partner wave's MFMAs)
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp) {
       const int kb = stp >> 1;
       const int sub = stp & 1;
-      u32x4 pw;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf16x2 pr;
-        pr[0] = static_cast<__bf16>(s[kb][8 * sub + 2 * t]);
-        pr[1] = static_cast<__bf16>(s[kb][8 * sub + 2 * t + 1]);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
-        pw[t] = __builtin_bit_cast(uint32_t, pr);
-      }
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        // keys 16*stp + 4*hi + (0..3) and 16*stp + 8 + 4*hi + (0..3)
-        const i16x4 lo = lds_read_tr16(vst + voffs[db] + (16 * stp) * C::kRowBytes);
-        const i16x4 up = lds_read_tr16(vst + voffs[db] + (16 * stp + 8) * C::kRowBytes);
-        const u32x4 av = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                          __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]};
-        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), pb, o[db]);
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * sub + 2 * t2]);
+        const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * sub + 2 * t2 + 1]);
+        ps[t2] += p0 + p1;
+        pk[stp][t2] = pack_bf16x2(p0, p1);
       }
     }
-    l_run += psum;
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
 
-  // Step j: wait for K(j+1) and V(j), refill the freed buffers with K(j+2) and
-  // V(j+1); then, in one basic block, the scores of tile j+1 (MFMA) run beside
-  // the softmax of tile j (vector ALU) and O += P V for tile j follows while the
-  // maximum of tile j+1 is taken.  Tile j+1's reference maximum (and any
-  // accumulator rescale) is settled at the end of the step.
-  auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of K(j+1), V(j)
-    __builtin_amdgcn_s_barrier();        // everyone's; and everyone is past step j-1
-    if (j + 2 < n_tiles) kload.issue(k_src, kbuf(j), static_cast<uint32_t>(j + 2) * tile_bytes);
-    if (j + 1 < n_tiles) vload.issue(v_src, vbuf(j + 1), static_cast<uint32_t>(j + 1) * tile_bytes);
-    // The score MFMAs (which wait on their K operand reads) run at raised wave
-    // priority, so the SIMD's other wave fills in with its softmax and P V work
-    // rather than competing for the same issue slots.
-    if (j + 1 < j_mask) {  // steady state: tile j+1 fully visible
-      __builtin_amdgcn_s_setprio(1);
-      qk(kbuf(j + 1), s_nxt, m_neg);
-      __builtin_amdgcn_s_setprio(0);
-      softmax(s_cur);
-      pv(s_cur, vbuf(j));
-      update_max(s_nxt, false);
+  // This group's share of the tile loads in its V phase of tile t: group 0
+  // issues K(t+2) and waits for K(t+1); group 1 the same for V.  The buffer
+  // that receives tile t+2 is slot (t+2) % 3.
+  auto loads = [&](auto slot2, int t) {
+    if (t + 2 < n_tiles) {
+      if (grp == 0) ld.issue(k_src, kbuf(slot2), static_cast<uint32_t>(t + 2) * tile_bytes);
+      else ld.issue(v_src, vbuf(slot2), static_cast<uint32_t>(t + 2) * tile_bytes);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);  // vmcnt(kLoads): tile t+1 is in
     } else {
-      if (j + 1 < n_w) {
-        __builtin_amdgcn_s_setprio(1);
-        qk(kbuf(j + 1), s_nxt, m_neg);
-        __builtin_amdgcn_s_setprio(0);
-      }
-      if (j < n_w) {
-        softmax(s_cur);
-        pv(s_cur, vbuf(j));
-      }
-      if (j + 1 < n_w) {
-        if (j + 1 >= j_mask) mask(s_nxt, (j + 1) * kBKV);
-        update_max(s_nxt, false);
-      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
+  };
+
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): query registers and prologue tiles
-  __builtin_amdgcn_s_barrier();
-  f32x16 sa[2], sb[2];
-  if (n_w > 0) {
-    qk(kbuf(0), sa, m_neg);
-    if (j_mask == 0) mask(sa, 0);
-    update_max(sa, true);
+  barrier();
+  if (n_w > 0) qk(lds_b_k0, s);
+  if (grp == 0) {
+    if (n_w > 0) vphase(s, 0, true);
+    loads(Slot<2>{}, 0);
+    prefetch_v(lds_a_v0);
   }
-  int j = 0;
-  for (; j + 1 < n_tiles; j += 2) {
-    step(j, sa, sb);
-    step(j + 1, sb, sa);
+  barrier();
+  if (grp == 1) {
+    if (n_w > 0) vphase(s, 0, true);
+    loads(Slot<2>{}, 0);
+    prefetch_v(lds_a_v0);
+    barrier();
   }
-  if (j < n_tiles) step(j, sa, sb);
 
-  // Normalise and stage the 128 x D output tile through LDS for 16-byte stores.
+  // Step j: M(j) with K slot (j+1) % 3 and V slot j % 3, then V(j+1), whose
+  // loads fill slot (j+3) % 3 = j % 3.
+  auto step = [&](auto sj, int j) {
+    constexpr int a = decltype(sj)::value;
+    __builtin_amdgcn_s_setprio(1);
+    if (j + 1 < n_w) mphase(kbuf(Slot<(a + 1) % 3>{}), vbuf(Slot<a>{}));
+    else if (j < n_w) pv(vbuf(Slot<a>{}));
+    __builtin_amdgcn_s_setprio(0);
+    barrier();
+    if (j + 1 < n_w) vphase(s, j + 1, false);
+    loads(Slot<a>{}, j + 1);
+    prefetch_v(vbuf(Slot<(a + 1) % 3>{}));
+    barrier();
+  };
+  auto last = [&](auto sj, int j) {
+    constexpr int a = decltype(sj)::value;
+    __builtin_amdgcn_s_setprio(1);
+    if (j < n_w) pv(vbuf(Slot<a>{}));
+    __builtin_amdgcn_s_setprio(0);
+    barrier();
+  };
+
+  int j = 0;
+  for (; j + 3 <= n_tiles - 1; j += 3) {
+    step(Slot<0>{}, j);
+    step(Slot<1>{}, j + 1);
+    step(Slot<2>{}, j + 2);
+  }
+  if (j < n_tiles - 1) step(Slot<0>{}, j++);
+  if (j < n_tiles - 1) step(Slot<1>{}, j++);
+  if (j % 3 == 0) last(Slot<0>{}, j);
+  else if (j % 3 == 1) last(Slot<1>{}, j);
+  else last(Slot<2>{}, j);
+  if (grp == 0) barrier();  // group 1 ran one phase behind: every wave is past its last LDS read now
+
+  // Normalise; stage each wave's 32 x D output rows through LDS (two waves per
+  // buffer, 16-byte chunks XOR-swizzled by row) for 16-byte stores.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __syncthreads();                     // every wave is done with the K/V buffers
-  uint16_t* ot = reinterpret_cast<uint16_t*>(lds);
-  const int ql = wave * 32 + l32;
+  unsigned char* stage;
+  switch (wave >> 1) {
+    case 0: stage = lds_b_k0; break;
+    case 1: stage = lds_b_k1; break;
+    case 2: stage = lds_b_k2; break;
+    default: stage = lds_a_v0; break;
+  }
+  stage += (wave & 1) * (32 * C::kRowBytes);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const int d = db * 32 + gq * 8 + hi * 4;
-      u32x2 pk;
-      pk[0] = pack_bf16x2(o[db][gq * 4 + 0] * inv, o[db][gq * 4 + 1] * inv);
-      pk[1] = pack_bf16x2(o[db][gq * 4 + 2] * inv, o[db][gq * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(ot + ql * C::kORow + d) = pk;
+      const int c = db * 4 + gq;  // 16-byte chunk of the row
+      const int cs = c ^ (l32 % C::kChunks);
+      u32x2 pk2;
+      pk2[0] = pack_bf16x2(o[db][gq * 4 + 0] * inv, o[db][gq * 4 + 1] * inv);
+      pk2[1] = pack_bf16x2(o[db][gq * 4 + 2] * inv, o[db][gq * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(stage + l32 * C::kRowBytes + cs * 16 + hi * 8) = pk2;
     }
-  __syncthreads();
-  constexpr int kOutChunks = kBQ * D / 8;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are in
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int i = 0; i < kOutChunks / kAttnThreads; ++i) {
-    const int c = tid + i * kAttnThreads;
-    const int row = c / (D / 8);
-    const int dc = c % (D / 8);
-    const int q = q0 + row;
-    if (q < n_q)
-      *reinterpret_cast<u32x4*>(O + static_cast<size_t>(q) * q_ld + h * D + dc * 8) =
-          *reinterpret_cast<const u32x4*>(ot + row * C::kORow + dc * 8);
+  for (int i = 0; i < 32 * C::kChunks / 64; ++i) {
+    const int cid = lane + 64 * i;
+    const int row = cid / C::kChunks;
+    const int c = cid % C::kChunks;
+    const int q = q0 + wave * 32 + row;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * C::kRowBytes + 16 * (c ^ (row % C::kChunks)));
+    if (q < n_q) *reinterpret_cast<u32x4*>(O + static_cast<size_t>(q) * q_ld + h * D + c * 8) = v;
   }
 }
 
@@ -502,18 +635,17 @@ hipError_t launch_attention(int dtype, int B, int D, const void* Q, const void* 
   if (n_q_max <= 0 || B <= 0) return hipSuccess;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
   if (dtype == 1) {
-    const int n_qt = (n_q_max + kBQ - 1) / kBQ;
-    const dim3 grid(n_qt * Hq, B);
     const float c = scale * 1.4426950408889634f;
     auto q = static_cast<const uint16_t*>(Q);
     auto k = static_cast<const uint16_t*>(K);
     auto v = static_cast<const uint16_t*>(V);
     auto o = static_cast<uint16_t*>(O);
+    const dim3 grid(((n_q_max + kPPQ - 1) / kPPQ) * Hq, B);
     if (D == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
+      hipLaunchKernelGGL(attn_fwd_bf16_pp_kernel<128>, grid, dim3(kPPThreads), 0, stream, q, k, v, o, q_pos, n_dev,
                          n_q_max, n_kv, Hq, Hkv, c, bt);
     else if (D == 64)
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(kAttnThreads), 0, stream, q, k, v, o, q_pos, n_dev,
+      hipLaunchKernelGGL(attn_fwd_bf16_pp_kernel<64>, grid, dim3(kPPThreads), 0, stream, q, k, v, o, q_pos, n_dev,
                          n_q_max, n_kv, Hq, Hkv, c, bt);
     else
       return hipErrorInvalidValue;
