@@ -24,7 +24,7 @@ DASH_OP_ATTN_LAYER, DASH_OP_SELECT, DASH_OP_ATTN_ACTIVE, DASH_OP_DECODE = 0, 1, 
 
 EXPORTED = ("dash_create", "dash_destroy", "dash_last_error", "dash_version", "dash_keep_count",
             "dash_percentile_rank", "dash_workspace_size",
-            "dash_attn_layer", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
+            "dash_attn_layer", "dash_attn_layer_noalloc", "dash_select", "dash_compact", "dash_compact_many", "dash_compact_batch",
             "dash_attn_active", "dash_score", "dash_attn_layer_varlen", "dash_select_ragged",
             "dash_attn_active_varlen", "dash_attn_active_gather", "dash_decode",
             "dash_trace_start", "dash_trace_select", "dash_trace_stop", "dash_trace_read")
@@ -79,6 +79,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_attn_layer.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.dash_attn_layer.restype = c_int
+    lib.dash_attn_layer_noalloc.argtypes = [c_void_p, POINTER(DashShape), c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.dash_attn_layer_noalloc.restype = c_int
     lib.dash_select.argtypes = [c_void_p, POINTER(DashSel), c_void_p, c_void_p, c_void_p, c_int, c_int,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.dash_select.restype = c_int
@@ -207,6 +210,22 @@ def dash_attn_layer(Q, K, V, Wo, O, U, score=None, ws=None, stream=None) -> None
     _check(load().dash_attn_layer(None, ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(Wo), _ptr(O),
                                   _ptr(U), _ptr(score), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream)))
+
+
+def dash_attn_layer_noalloc(Q, K, V, Wo, O, U, score=None, stream=None) -> None:
+    """dash_attn_layer without a workspace: the score's partial sums live in the
+    library's built-in per-GPU scratch (see include/dash.h for its limit)."""
+    q = Q if Q.dim() == 4 else Q.unsqueeze(0)
+    k = K if K.dim() == 4 else K.unsqueeze(0)
+    B, S, Hq, D = q.shape
+    Hkv, hidden = k.shape[2], Wo.shape[0]
+    for t, n, name in ((K, B * S * Hkv * D, "K"), (V, B * S * Hkv * D, "V"), (Wo, hidden * Hq * D, "Wo"),
+                       (O, B * S * Hq * D, "O"), (U, B * S * hidden, "U")):
+        _need(t, n, Q.dtype, name)
+    _need(score, B * S, torch.float32, "score")
+    shape = make_shape(B, S, Hq, Hkv, D, hidden, _dtype_code(Q))
+    _check(load().dash_attn_layer_noalloc(None, ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(Wo), _ptr(O),
+                                          _ptr(U), _ptr(score), _stream(stream)))
 
 
 def dash_select(score, idx=None, *, mode: int = DASH_SEL_TOPK, k: int = 0, rank: int = 0, tau=None,

@@ -138,6 +138,35 @@ int attn_layer_launch(const dash_shape* s, const void* Q, const void* K, const v
   return DASH_OK;
 }
 
+// ---- built-in scratch for dash_attn_layer_noalloc -----------------------------
+// Every GPU the library runs on holds its own copy of this array until the
+// process ends.  Host code never uses the array's name as a device address:
+// the address of each device's copy is looked up once per device (with that
+// device current) and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DASH_E_HIP, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DASH_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return DASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -283,6 +312,29 @@ int dash_attn_layer(void* /*ctx*/, const dash_shape* s, const void* Q, const voi
       if (!aligned16(ws)) return fail(DASH_E_ALIGN, "workspace is not 16-byte aligned");
     }
     return attn_layer_launch(s, Q, K, V, Wo, O, U, score, static_cast<float*>(ws), static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(DASH_E_INVAL, "unexpected host exception");
+  }
+}
+
+int dash_attn_layer_noalloc(void* /*ctx*/, const dash_shape* s, const void* Q, const void* K, const void* V,
+                            const void* Wo, void* O, void* U, float* score, void* stream) {
+  try {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    rc = check_ptrs({{Q, "Q"}, {K, "K"}, {V, "V"}, {Wo, "Wo"}, {O, "O"}, {U, "U"}});
+    if (rc) return rc;
+    float* part = nullptr;
+    if (score) {
+      if (!aligned16(score)) return fail(DASH_E_ALIGN, "score is not 16-byte aligned");
+      const size_t need = score_ws_bytes(s, static_cast<int64_t>(s->B) * s->S);
+      if (need > kScratchBytes)
+        return fail(DASH_E_WORKSPACE, "the score partials need %zu bytes; the built-in scratch holds %zu", need,
+                    static_cast<size_t>(kScratchBytes));
+      rc = scratch_address(&part);
+      if (rc) return rc;
+    }
+    return attn_layer_launch(s, Q, K, V, Wo, O, U, score, part, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(DASH_E_INVAL, "unexpected host exception");
   }

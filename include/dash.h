@@ -144,6 +144,22 @@ int dash_attn_layer(void* ctx, const dash_shape* s,
                     void* O, void* U, float* score,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* dash_attn_layer without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as dash_attn_layer (the
+ * same kernels, bit-identical outputs) except that the Σu² partials of the
+ * score live in a scratch array built into the library: 16 MiB per GPU, held
+ * from the first call on that GPU until the process ends.  A score needs
+ * ceil(hidden / 224) * B * S * 4 bytes of it (hidden 3584: B * S <= 262144);
+ * larger calls with score != NULL return DASH_E_WORKSPACE and enqueue
+ * nothing.  score == NULL needs no scratch.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (several streams or host threads) race and must be serialised by
+ * the caller.  Nothing in the array needs to start at zero. */
+int dash_attn_layer_noalloc(void* ctx, const dash_shape* s,
+                            const void* Q, const void* K, const void* V, const void* Wo,
+                            void* O, void* U, float* score, void* stream);
+
 /* a3 / a3': selection ([P1] §2.3 and §3.1 step 3; [P2] 层间更新动态监测).
  *   TOPK:       score [rows, n_max] → idx [rows, k]: the k positions with the
  *               largest score, ties to the lower position, NaN below every
