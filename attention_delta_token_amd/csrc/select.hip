@@ -570,16 +570,6 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
     for (int e = 0; e < 4; ++e) keys[j][e] = score_key(__uint_as_float(v[e]));
   }
   auto valid = [&](int j) { return j * kWave + lane < n4; };
-  if (nan_out) {
-    uint32_t nan = 0u;
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-      if (valid(j))
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nan += keys[j][e] == 0u;
-    nan = wave_incl_scan32(nan);
-    if (lane == kWave - 1) nan_out[row] = static_cast<int32_t>(nan);
-  }
 
   // Bits shared by every key of the row are settled first (wave min/max of the
   // keys in registers); digits of up to 11 bits then start right below them, so
@@ -658,7 +648,7 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
 
   // Emit in position order: chunk j covers positions 256*j .. 256*j + 255, lane
   // l its four positions 256*j + 4*l + e.
-  uint32_t sel_before = 0u, eq_before = 0u;
+  uint32_t sel_before = 0u, eq_before = 0u, nan = 0u;  // nan: this lane's NaN scores (key 0)
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     uint32_t gt_bits = 0u, eq_bits = 0u;
@@ -667,6 +657,7 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
       for (int e = 0; e < 4; ++e) {
         if (keys[j][e] > cut) gt_bits |= 1u << e;
         else if (keys[j][e] == cut) eq_bits |= 1u << e;
+        nan += keys[j][e] == 0u;
       }
     }
     const uint32_t packed = (static_cast<uint32_t>(__popc(gt_bits)) << 16) | static_cast<uint32_t>(__popc(eq_bits));
@@ -688,6 +679,10 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
     const uint32_t tot_eq = tot & 0xffffu;
     sel_before += (tot >> 16) + (min(eq_before + tot_eq, take_eq) - min(eq_before, take_eq));
     eq_before += tot_eq;
+  }
+  if (nan_out) {
+    nan = wave_incl_scan32(nan);
+    if (lane == kWave - 1) nan_out[row] = static_cast<int32_t>(nan);
   }
 }
 
