@@ -366,31 +366,37 @@ void attn_fwd_bf16_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __r
   // M phase with both products: the scores of the next tile (s) and O += P V
   // of the current one, their MFMAs interleaved; the LDS operand reads are
   // kept several MFMAs ahead (scheduling groups), since the SIMD's other wave
-  // is in its vector-ALU phase and cannot cover their latency.
+  // is in its vector-ALU phase and cannot cover their latency.  The P V
+  // MFMAs of the first key step come first: their V operands were read in
+  // the softmax phase, so they run while the first K reads are in flight.
   auto mphase = [&](const unsigned char* kst, const unsigned char* vst) {
     // 2 * (D / 16) score MFMAs (two key blocks per k-step) and 4 * (D / 32)
     // P V MFMAs (four key steps per output block): equal counts for every D
-    static_assert(2 * (D / 16) == 4 * (D / 32), "paired MFMA counts");
+    constexpr int kN = 2 * (D / 16);
+    static_assert(kN == 4 * (D / 32), "paired MFMA counts");
+    auto pv_mfma = [&](int j) {  // stp = j / (D / 32), db = j % (D / 32)
+      const int stp = j / (D / 32), db = j % (D / 32);
+      u32x4 av;
+      if (stp == 0) {
+        av = vpre[db];
+      } else {
+        const i16x4 lo = lds_read_tr16(vst + voffs[db] + (16 * stp) * C::kRowBytes);
+        const i16x4 up = lds_read_tr16(vst + voffs[db] + (16 * stp + 8) * C::kRowBytes);
+        av = u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                   __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]};
+      }
+      o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pk[stp]), o[db]);
+    };
 #pragma unroll
-    for (int i = 0; i < 2 * (D / 16); ++i) {
+    for (int j = 0; j < D / 32; ++j) pv_mfma(j);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
       const int ks = i >> 1, kb = i & 1;
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(kst + koff[ks] + kb * 32 * C::kRowBytes);
       s[kb] = mfma32x32x16(a, qreg[ks], ks == 0 ? m_neg : s[kb]);
-      {
-        const int stp = i / (D / 32), db = i % (D / 32);
-        u32x4 av;
-        if (stp == 0) {
-          av = vpre[db];
-        } else {
-          const i16x4 lo = lds_read_tr16(vst + voffs[db] + (16 * stp) * C::kRowBytes);
-          const i16x4 up = lds_read_tr16(vst + voffs[db] + (16 * stp + 8) * C::kRowBytes);
-          av = u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                     __builtin_bit_cast(u32x2, up)[0], __builtin_bit_cast(u32x2, up)[1]};
-        }
-        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pk[stp]), o[db]);
-      }
+      if (i + D / 32 < kN) pv_mfma(i + D / 32);
     }
-    // 3 LDS reads per pair of MFMAs: twelve reads ahead, then MFMA, two
+    // 3 LDS reads per pair of MFMAs: ten reads ahead, then MFMA, two
     // reads, MFMA, one read, ...
     __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
 #pragma unroll
