@@ -539,15 +539,33 @@ namespace {
 // ---------------------------------------------------------------------------
 // Batched rows: one wave per row, no workgroup barrier anywhere.  Lane l holds
 // the keys of positions 256*j + 4*l + e (e < 4, j < J) in registers (one
-// 16-byte load each), counts into its wave's own 2048-bin LDS histogram, and
-// settles the cut with wave scans; the emit walks the 256-position chunks in
-// order with one scan each.  Rows are n % 4 == 0 scores, 16-byte aligned.
+// 16-byte load each).  The bits every key shares are settled from the wave's
+// smallest and largest key; digits of up to 11 bits follow, counted into the
+// wave's own 2048-bin LDS histogram.  The search stops as soon as the bin
+// holding the cut is taken whole (its count equals the keys still wanted), and
+// the emit then keeps every key >= that bin's lowest key: per 256-position
+// chunk, four compare masks and the set bits of the lanes below (mbcnt) give
+// each kept position its output slot.  Only a cut inside a run of equal keys
+// takes the slower emit, which ranks the equal keys with wave scans.
+// Full: the row fills all J chunks (n == 256 * J), so no position tests.
+// Rows are n % 4 == 0 scores, 16-byte aligned.
 // ---------------------------------------------------------------------------
 constexpr int kWaveRowsPerBlock = 4;
 
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-template <int J>
+// LDS word of histogram bin b in the one-wave kernel: bins are permuted
+// within each group of 32 so that the scan, where lane l reads bins 32l + i
+// for i = 0..31, touches 32 banks per read instead of 2.
+__device__ __forceinline__ uint32_t wave_bin_word(uint32_t b) { return b ^ ((b >> 5) & 31u); }
+
+// Number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+template <int J, bool Full>
 __global__ __launch_bounds__(kWaveRowsPerBlock * kWave)
 void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, int32_t* __restrict__ idx,
                       int32_t* __restrict__ nan_out) {
@@ -560,16 +578,31 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
   const u32x4* r4 = reinterpret_cast<const u32x4*>(score + static_cast<size_t>(row) * n);
   int32_t* out = idx + static_cast<size_t>(row) * k;
   const int n4 = n >> 2;
+  auto valid = [&](int j) { return Full || j * kWave + lane < n4; };
   uint32_t keys[J][4];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int i4 = j * kWave + lane;
+  for (int j = 0; j < J; ++j) {  // every load in flight before the first is used
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (i4 < n4) v = __builtin_nontemporal_load(r4 + i4);
+    if (valid(j)) v = __builtin_nontemporal_load(r4 + j * kWave + lane);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) keys[j][e] = score_key(__uint_as_float(v[e]));
+    for (int e = 0; e < 4; ++e) keys[j][e] = v[e];
   }
-  auto valid = [&](int j) { return j * kWave + lane < n4; };
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keys[j][e] = score_key(__uint_as_float(keys[j][e]));
+  if (nan_out) {  // NaN scores (key 0): per-lane counts, then one wave sum
+    uint32_t nan = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        nan += (valid(j) && keys[j][e] == 0u) ? 1u : 0u;
+        __builtin_amdgcn_sched_barrier(0);  // one key at a time: no 128 live compare results
+      }
+    nan = wave_incl_scan32(nan);
+    if (lane == kWave - 1) nan_out[row] = static_cast<int32_t>(nan);
+  }
 
   // Bits shared by every key of the row are settled first (wave min/max of the
   // keys in registers); digits of up to 11 bits then start right below them, so
@@ -596,21 +629,29 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
   uint32_t prefix = kmin & pmask, kk = static_cast<uint32_t>(k);
   constexpr int kBPL = kBins / kWave;  // bins per lane in the scan (32)
   int sh = 32 - common;
+  // whole: every key of the bin that holds the cut is kept, so the kept keys
+  // are exactly those >= prefix (the bin's lowest key).  With one key value
+  // in the row, that is when all n are kept.
+  bool whole = sh == 0 && kk == static_cast<uint32_t>(n);
 #pragma unroll 1
   while (sh > 0) {
     const int wd = sh < 11 ? sh : 11;
     sh -= wd;
     const uint32_t dm = (1u << wd) - 1u;
 #pragma unroll
-    for (int b = 0; b < kBPL; ++b) h[b * kWave + lane] = 0u;
+    for (int b = 0; b < kBPL / 4; ++b) reinterpret_cast<u32x4*>(h)[b * kWave + lane] = u32x4{0u, 0u, 0u, 0u};
     wave_lds_fence();
+    // Branch-free: every key adds 1 when it carries the prefix, else 0 (on the
+    // first digit every key does); per-key branches would keep 128 compare
+    // masks alive across the loop.
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (valid(j)) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if ((keys[j][e] & pmask) == prefix) atomicAdd(&h[(keys[j][e] >> sh) & dm], 1u);
+          atomicAdd(&h[wave_bin_word((keys[j][e] >> sh) & dm)], (keys[j][e] & pmask) == prefix ? 1u : 0u);
       }
+      __builtin_amdgcn_sched_barrier(0);  // no bin addresses of later chunks computed ahead
     }
     wave_lds_fence();
     const int nb = static_cast<int>(dm) + 1;
@@ -619,13 +660,13 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
     uint32_t mine = 0u;
 #pragma unroll
     for (int b = 0; b < kBPL; ++b) {
-      c[b] = (b0 + b < nb) ? h[b0 + b] : 0u;
+      c[b] = h[wave_bin_word(static_cast<uint32_t>(b0 + b))];  // bins >= nb stay zero
       mine += c[b];
     }
     const uint32_t incl = wave_incl_scan32(mine);
     const uint32_t tot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
     uint32_t upto = incl - mine;  // keys in bins below b0
-    uint32_t found_bin = 0u, found_kk = 0u;
+    uint32_t found_bin = 0u, found_kk = 0u, found_cnt = 0u;
     bool found = false;
 #pragma unroll
     for (int b = 0; b < kBPL; ++b) {
@@ -635,20 +676,52 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
         found = true;
         found_bin = static_cast<uint32_t>(b0 + b);
         found_kk = kk - above;
+        found_cnt = c[b];
       }
     }
     const uint64_t who = __ballot(found);
     const int src = static_cast<int>(__builtin_ctzll(who));
     const uint32_t bin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(found_bin), src));
+    const uint32_t cnt = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(found_cnt), src));
     kk = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(found_kk), src));
     prefix |= bin << sh;
     pmask |= dm << sh;
+    if (kk == cnt) {
+      whole = true;
+      break;
+    }
   }
-  const uint32_t cut = prefix, take_eq = kk;
 
-  // Emit in position order: chunk j covers positions 256*j .. 256*j + 255, lane
-  // l its four positions 256*j + 4*l + e.
-  uint32_t sel_before = 0u, eq_before = 0u, nan = 0u;  // nan: this lane's NaN scores (key 0)
+  if (whole) {
+    // Keep key >= prefix.  Chunk j: lane l's positions 256j + 4l + e follow
+    // every kept position of the lanes below it.
+    uint32_t before = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      bool t[4];
+      uint64_t m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[e] = valid(j) && keys[j][e] >= prefix;
+        m[e] = __ballot(t[e]);
+      }
+      uint32_t o = before + lanes_below(m[0]) + lanes_below(m[1]) + lanes_below(m[2]) + lanes_below(m[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (t[e] && o < static_cast<uint32_t>(k)) out[o] = j * 4 * kWave + 4 * lane + e;
+        o += t[e] ? 1u : 0u;
+      }
+      before += static_cast<uint32_t>(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]));
+      __builtin_amdgcn_sched_barrier(0);  // chunk by chunk: no masks of later chunks held early
+    }
+    return;
+  }
+
+  // The cut falls inside a run of keys equal to `prefix`: keep every greater
+  // key and the first kk equal ones in position order.  Chunk j covers
+  // positions 256*j .. 256*j + 255, lane l its four positions 256*j + 4*l + e.
+  const uint32_t cut = prefix, take_eq = kk;
+  uint32_t sel_before = 0u, eq_before = 0u;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     uint32_t gt_bits = 0u, eq_bits = 0u;
@@ -657,7 +730,6 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
       for (int e = 0; e < 4; ++e) {
         if (keys[j][e] > cut) gt_bits |= 1u << e;
         else if (keys[j][e] == cut) eq_bits |= 1u << e;
-        nan += keys[j][e] == 0u;
       }
     }
     const uint32_t packed = (static_cast<uint32_t>(__popc(gt_bits)) << 16) | static_cast<uint32_t>(__popc(eq_bits));
@@ -679,10 +751,6 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
     const uint32_t tot_eq = tot & 0xffffu;
     sel_before += (tot >> 16) + (min(eq_before + tot_eq, take_eq) - min(eq_before, take_eq));
     eq_before += tot_eq;
-  }
-  if (nan_out) {
-    nan = wave_incl_scan32(nan);
-    if (lane == kWave - 1) nan_out[row] = static_cast<int32_t>(nan);
   }
 }
 
@@ -724,12 +792,20 @@ hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_firs
                          n % 4 == 0 && n <= 8192 && (reinterpret_cast<uintptr_t>(score) & 15u) == 0;
   if (wave_rows) {
     const dim3 grid((rows + kWaveRowsPerBlock - 1) / kWaveRowsPerBlock), block(kWaveRowsPerBlock * kWave);
+#define DASH_WAVE_TOPK(J_)                                                                                 \
+  do {                                                                                                     \
+    if (n == 256 * (J_))                                                                                   \
+      hipLaunchKernelGGL((topk_wave_kernel<J_, true>), grid, block, 0, stream, score, rows, n, k, idx, nan_out); \
+    else                                                                                                   \
+      hipLaunchKernelGGL((topk_wave_kernel<J_, false>), grid, block, 0, stream, score, rows, n, k, idx, nan_out); \
+  } while (0)
     if (n <= 2048)
-      hipLaunchKernelGGL(topk_wave_kernel<8>, grid, block, 0, stream, score, rows, n, k, idx, nan_out);
+      DASH_WAVE_TOPK(8);
     else if (n <= 4096)
-      hipLaunchKernelGGL(topk_wave_kernel<16>, grid, block, 0, stream, score, rows, n, k, idx, nan_out);
+      DASH_WAVE_TOPK(16);
     else
-      hipLaunchKernelGGL(topk_wave_kernel<32>, grid, block, 0, stream, score, rows, n, k, idx, nan_out);
+      DASH_WAVE_TOPK(32);
+#undef DASH_WAVE_TOPK
   } else {
     launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, nullptr, nullptr, n_dev, n_out,
                                 nan_out, stream);

@@ -82,6 +82,28 @@ def test_topk_bit_exact(dash, kind, n):
         np.testing.assert_array_equal(idx.cpu().numpy()[:k], exp)
 
 
+@pytest.mark.parametrize("n", [8192, 8188, 4096, 2048, 1028])
+@pytest.mark.parametrize("kind", SCORE_KINDS)
+def test_topk_wave_rows_all_kinds(dash, kind, n):
+    """The one-wave-per-row batch path on every score family, rows that fill
+    their 256-score chunks (8192, 4096, 2048) and rows that do not; k from 1 to
+    n, so cuts fall inside runs of equal scores (fewvalues, equal, bf16ties)
+    as well as between distinct ones.  NaN counts per row checked too."""
+    rows = 256
+    s = np.stack([score_vector(kind, n, seed=1000 * r + n) for r in range(rows)])
+    sd = torch.from_numpy(s).cuda()
+    for k in (1, n // 3, n // 2 + 1, n - 1, n):
+        say("topk wave rows", kind, n, k)
+        idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+        st = dash.select_status(rows)
+        dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows, status=st)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        np.testing.assert_array_equal(st.cpu().numpy()[:rows], np.isnan(s).sum(axis=1))
+        for r in range(0, rows, 5):
+            np.testing.assert_array_equal(got[r], oracle.select_topk(s[r], k))
+
+
 @pytest.mark.parametrize("rows,n,k", [(48, 3000, 1234), (80, 3000, 1234), (70, 8192, 4096), (64, 8193, 100),
                                       (66, 1, 1), (65, 40000, 39999),
                                       (256, 8192, 4096), (300, 2048, 1000), (257, 4, 2), (512, 4100, 1),
