@@ -7,8 +7,8 @@
 // once, every 16-byte chunk of the row (across the gathered tensors) is loaded
 // before any is stored, consecutive lanes move consecutive chunks (coalesced
 // for any row width), and the stores bypass the caches' write-allocate
-// (nontemporal), which measured as fast as a plain device-to-device copy of
-// the same bytes.  The grid is sized from the row capacity, so a
+// (nontemporal), which measured faster than a plain device-to-device copy of
+// the same bytes after other work has left the caches dirty.  The grid is sized from the row capacity, so a
 // device-resident row count needs no host round trip.
 #include "dash_common.h"
 #include "dash_kernels.h"
@@ -84,6 +84,53 @@ void compact_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__
   }
 }
 
+// Rows of at most 64 * U chunks per tensor (U = 1: 1 KiB, 2: 2 KiB), e.g. the
+// K and V rows of a kv-head group, C tensors: each tensor's source row
+// address is scalar and a chunk costs one address add.  Every load is issued
+// unconditionally (a lane past the row's width re-reads the row's last chunk;
+// a source index outside the tensor reads the destination row instead), so
+// all of a row's loads are in flight before the first store; only the stores
+// are conditional.
+template <int U, int C>
+__global__ __launch_bounds__(kCompactThreads)
+void compact_rows_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ n_dev, int n_max,
+                         int per_sample, GatherSet g) {
+  int n = n_max;
+  if (n_dev) n = min(*n_dev, n_max);
+  const int r = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kCompactRows + (threadIdx.x >> 6));
+  if (r >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t src = idx[r];
+  uint64_t sample = 0;
+  if (per_sample > 0) sample = static_cast<uint32_t>(r) / static_cast<uint32_t>(per_sample);
+  u32x4 v[C][U];
+  bool ok[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    // branch-free selection of the row address, so every descriptor field is
+    // loaded up front instead of behind a branch
+    const uint32_t w = g.w[j];
+    ok[j] = static_cast<uint32_t>(src) < static_cast<uint32_t>(g.S[j]);
+    const uint64_t s_off = (sample * static_cast<uint64_t>(static_cast<uint32_t>(g.S[j])) +
+                            static_cast<uint64_t>(static_cast<uint32_t>(src))) * w;
+    const uint64_t d_off = static_cast<uint64_t>(r) * w;
+    const u32x4* row = ok[j] ? g.X[j] + s_off : g.Xa[j] + d_off;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      v[j][u] = __builtin_nontemporal_load(row + min(static_cast<uint32_t>(lane + 64 * u), w - 1u));
+  }
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const uint32_t w = g.w[j];
+    if (ok[j]) {
+      u32x4* row = g.Xa[j] + static_cast<uint64_t>(r) * w;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (static_cast<uint32_t>(lane + 64 * u) < w) __builtin_nontemporal_store(v[j][u], row + lane + 64 * u);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_max, const GatherItem* items,
@@ -111,6 +158,27 @@ hipError_t launch_compact_many(const int32_t* idx, const int32_t* n_dev, int n_m
   const uint64_t total = static_cast<uint64_t>(n_max) * acc;
   if (total >= 0x80000000ull) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((static_cast<uint64_t>(n_max) + kCompactRows - 1) / kCompactRows));
+  uint32_t wmax = 0;
+  for (int j = 0; j < count; ++j) wmax = g.w[j] > wmax ? g.w[j] : wmax;
+  if (wmax <= 128) {  // rows of at most 2 KiB per tensor
+#define DASH_ROWS(U_, C_) \
+  hipLaunchKernelGGL((compact_rows_kernel<U_, C_>), grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g)
+#define DASH_ROWS_C(U_)              \
+  switch (count) {                   \
+    case 1: DASH_ROWS(U_, 1); break; \
+    case 2: DASH_ROWS(U_, 2); break; \
+    case 3: DASH_ROWS(U_, 3); break; \
+    default: DASH_ROWS(U_, 4); break; \
+  }
+    if (wmax <= 64) {
+      DASH_ROWS_C(1)
+    } else {
+      DASH_ROWS_C(2)
+    }
+#undef DASH_ROWS_C
+#undef DASH_ROWS
+    return hipGetLastError();
+  }
   const uint32_t need = (acc + 63) / 64;  // chunks per lane for one row
   if (need <= 1)
     hipLaunchKernelGGL(compact_kernel<1>, grid, dim3(kCompactThreads), 0, stream, idx, n_dev, n_max, per_sample, g);

@@ -53,6 +53,9 @@ def parse():
                     help="warmup + timed + traced steps only (for rocprofv3); no dense stack, no CPU leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 512 MiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--hbm-kernels", action="store_true",
+                    help="only the HBM-bound kernels on synthetic inputs of the workload's shapes (batched "
+                         "top-k sweep, standalone score, K/V gather), warm and cold; one JSON line")
     return ap.parse_args()
 
 
@@ -108,6 +111,9 @@ def main():
     dev = torch.device("cuda:0")
     w = WORKLOADS[args.config]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if args.hbm_kernels:
+        hbm_kernels(dash, torch, dev, w, args)
+        return
 
     # Inputs: generated on the host layer by layer, narrowed to the element
     # type on the host (the values are exact in it), uploaded, kept resident.
@@ -407,6 +413,95 @@ def select_sweep(dash, torch, dev, rows=256, n=65536):
     gbps = rows * (4.0 * n + 4.0 * k) / (ms * 1e-3) / 1e9
     return {"rows": rows, "n": n, "k": k, "ms": ms, "GBps": gbps, "frac": gbps / PEAK_HBM_GBPS,
             "ms_single_call": sum(t) / len(t), "timing": f"{reps} calls back to back, events around the batch"}
+
+
+def timed_calls(torch, fn, reps, flush=None):
+    """Mean ms per call: `reps` calls back to back between one pair of events
+    (warm), or, with a flush buffer, each call alone after a write of the whole
+    buffer (cold: the inputs are evicted from L2 and the MALL)."""
+    fn()
+    if flush is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+    t = 0.0
+    for i in range(reps):
+        flush.fill_(i & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        t += e0.elapsed_time(e1)
+    return t / reps
+
+
+def hbm_kernels(dash, torch, dev, w, args):
+    """The HBM-bound kernels alone, on synthetic inputs of the workload's
+    shapes (values do not change their traffic): the batched top-k sweep, the
+    standalone score over an [S, hidden] U, and the one-launch gather of the
+    kept rows' K and V (k = the one-shot kept count), each warm and after a
+    1 GiB write.  Algorithmic bytes: top-k 4 B per score + 4 B per kept index;
+    score hidden * element size + 4 B per row; gather 2 * 2 * Hkv * D * element
+    size + 4 B per kept row."""
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    esz = 2 if w.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    out = {"workload": f"{w.name}: S={w.S}, Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, hidden={w.hidden}",
+           "peak_GBps": PEAK_HBM_GBPS, "select_sweep": [], "timing": "warm: 10 calls back to back between one "
+           "pair of events; cold: each call alone after a 1 GiB write"}
+    for rows, n in ((2048, 8192), (8192, 8192), (256, 65536)):
+        k = n // 2
+        score = torch.rand(rows, n, device=dev, generator=g)
+        idx = torch.empty(rows, k, dtype=torch.int32, device=dev)
+        fn = lambda: dash.dash_select(score, idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows)
+        nbytes = rows * (4.0 * n + 4.0 * k)
+        warm, cold = timed_calls(torch, fn, 10), timed_calls(torch, fn, 5, flush)
+        out["select_sweep"].append({"rows": rows, "n": n, "k": k, "bytes": nbytes, "ms": warm, "ms_cold": cold,
+                                    "frac": nbytes / (warm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                    "frac_cold": nbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS})
+        del score, idx
+    U = torch.randn(w.S, w.hidden, device=dev, generator=g).to(tdt)
+    sc = torch.empty(w.S, dtype=torch.float32, device=dev)
+    fn = lambda: dash.dash_score(U, sc)
+    nbytes = w.S * (w.hidden * esz + 4.0)
+    warm, cold = timed_calls(torch, fn, 10), timed_calls(torch, fn, 5, flush)
+    out["score"] = {"rows": w.S, "hidden": w.hidden, "bytes": nbytes, "ms": warm, "ms_cold": cold,
+                    "frac": nbytes / (warm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                    "frac_cold": nbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    del U, sc
+    k = dash.keep_count(w.S, w.keep)
+    K = torch.randn(w.S, w.Hkv, w.D, device=dev, generator=g).to(tdt)
+    V = torch.randn(w.S, w.Hkv, w.D, device=dev, generator=g).to(tdt)
+    kept = torch.sort(torch.randperm(w.S, device=dev, generator=g)[:k]).values.to(torch.int32)
+    Ka, Va = torch.empty(k, w.Hkv, w.D, dtype=tdt, device=dev), torch.empty(k, w.Hkv, w.D, dtype=tdt, device=dev)
+    fn = lambda: dash.dash_compact_many(kept, [(K, Ka), (V, Va)])
+    nbytes = k * (2.0 * 2 * w.Hkv * w.D * esz + 4.0)
+    warm, cold = timed_calls(torch, fn, 10), timed_calls(torch, fn, 5, flush)
+    assert torch.equal(Ka, K[kept.long()]) and torch.equal(Va, V[kept.long()])
+    out["gather_kv"] = {"rows": k, "bytes": nbytes, "ms": warm, "ms_cold": cold,
+                        "frac": nbytes / (warm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                        "frac_cold": nbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    # the same bytes as a plain device-to-device copy, for reference
+    src = torch.empty(int(nbytes) // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    fn = lambda: dst.copy_(src)
+    warm, cold = timed_calls(torch, fn, 10), timed_calls(torch, fn, 5, flush)
+    out["device_copy_same_bytes"] = {"ms": warm, "ms_cold": cold,
+                                     "frac": nbytes / (warm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                     "frac_cold": nbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    if args.calibrate_copy:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
 
 
 def score_measurements(dash, torch, dev, step, layer):

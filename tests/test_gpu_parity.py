@@ -368,7 +368,7 @@ def test_select_nan_status(dash):
 # compaction (bit-exact)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("row_bytes", [16, 48, 1024, 7168])
+@pytest.mark.parametrize("row_bytes", [16, 48, 1024, 1040, 2048, 2064, 7168])
 @pytest.mark.parametrize("device_n", [False, True])
 def test_compact_bit_exact(dash, row_bytes, device_n):
     S, n_max = 3001, 1500
@@ -386,7 +386,8 @@ def test_compact_bit_exact(dash, row_bytes, device_n):
     assert np.all(got[n:] == 0xAB)
 
 
-@pytest.mark.parametrize("widths", [(7168, 1024, 1024), (16,), (48, 16, 7168, 32), (1024, 48)])
+@pytest.mark.parametrize("widths", [(7168, 1024, 1024), (16,), (48, 16, 7168, 32), (1024, 48), (2048,),
+                                    (2048, 1040, 16), (1024, 1024, 512, 16), (2048, 2048, 2048, 1024)])
 @pytest.mark.parametrize("device_n", [False, True])
 def test_compact_many_bit_exact(dash, widths, device_n):
     """Several tensors of different row widths gathered at one index list in one
@@ -634,7 +635,7 @@ def test_attn_active_batched(dash, dtype, mode):
         assert np.all(np.abs(host(sc)[b] - ref_s) <= TOL_SCORE * ref_s)
 
 
-@pytest.mark.parametrize("widths", [(7168, 1024, 1024), (48,), (16, 32)])
+@pytest.mark.parametrize("widths", [(7168, 1024, 1024), (48,), (16, 32), (2048, 2048), (1024, 1024, 16)])
 def test_compact_batch_bit_exact(dash, widths):
     """Per-sample gathers of B = 4 samples (local positions, with out-of-range entries skipped)."""
     B, S, k = 4, 1000, 300
