@@ -255,9 +255,11 @@ def dash_select(score, idx=None, *, mode: int = DASH_SEL_TOPK, k: int = 0, rank:
                               _ptr(idx), _ptr(n_out), _ptr(tau_out), _ptr(status), ws_bytes, _stream(stream)))
 
 
-def select_status(rows: int = 1, device="cuda") -> torch.Tensor:
-    """An int32 device buffer for dash_select's NaN counts (one word per row)."""
-    n = dash_workspace_size(DASH_OP_SELECT, make_shape(rows, 1, 1, 1, 1, 1, DASH_F32), 0)
+def select_status(rows: int = 1, device="cuda", n_max: int = 0) -> torch.Tensor:
+    """An int32 device buffer for dash_select's NaN counts (one word per row);
+    with n_max, also the scratch a single long row's top-k spreads over many
+    workgroups with (dash_workspace_size(DASH_OP_SELECT, ..., n_max))."""
+    n = dash_workspace_size(DASH_OP_SELECT, make_shape(rows, 1, 1, 1, 1, 1, DASH_F32), n_max)
     return torch.zeros(max(n, 256) // 4, dtype=torch.int32, device=device)
 
 

@@ -283,9 +283,11 @@ size_t dash_workspace_size(void* /*ctx*/, int op, const dash_shape* s, int n_max
       case DASH_OP_ATTN_ACTIVE:
         if (check_shape(s, false) != DASH_OK || n_max < 0) return 0;
         return score_ws_bytes(s, static_cast<int64_t>(s->B) * n_max);
-      case DASH_OP_SELECT:  // one int32 NaN count per row (the selection state itself lives in LDS)
-        if (!s || s->B < 1 || s->B > (1 << 20)) return 0;
-        return align_up(static_cast<size_t>(s->B) * sizeof(int32_t));
+      case DASH_OP_SELECT:  // one int32 NaN count per row; for one row longer than 32768 scores, the
+                            // scratch of its multi-workgroup top-k
+        if (!s || s->B < 1 || s->B > (1 << 20) || n_max < 0) return 0;
+        return align_up(static_cast<size_t>(s->B) * sizeof(int32_t)) +
+               (s->B == 1 ? dash::topk_multi_ws_bytes(n_max, 0, 0) : 0);
       case DASH_OP_DECODE:
         if (check_shape(s, false) != DASH_OK || n_max < 1) return 0;
         return align_up(dash::decode_workspace_bytes(s->B, s->S, s->Hkv, s->D));
@@ -377,8 +379,18 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
         if (!idx && p->k > 0) return fail(DASH_E_INVAL, "idx is NULL");
         if (n_max == 0 && !n_out_dev && !nan_out) return DASH_OK;
         tr = trace_open(DASH_TR_SELECT, st);
-        e = dash::launch_topk(score, rows, n_max, p->k, p->keep_first, p->keep_last, pos, n_dev, idx, n_out_dev,
-                              nan_out, st);
+        // a single long row runs over many workgroups when the workspace holds
+        // their scratch (after the status word)
+        const size_t multi = (rows == 1 && !n_dev && p->k - p->keep_first - p->keep_last > 0)
+                                 ? dash::topk_multi_ws_bytes(n_max, p->keep_first, p->keep_last)
+                                 : 0;
+        const size_t status_bytes = align_up(sizeof(int32_t));
+        if (multi > 0 && ws && ws_bytes >= status_bytes + multi)
+          e = dash::launch_topk_multi(score, n_max, p->k, p->keep_first, p->keep_last, pos, idx, n_out_dev, nan_out,
+                                      static_cast<unsigned char*>(ws) + status_bytes, st);
+        else
+          e = dash::launch_topk(score, rows, n_max, p->k, p->keep_first, p->keep_last, pos, n_dev, idx, n_out_dev,
+                                nan_out, st);
         break;
       }
       case DASH_SEL_ORDER_STAT: {

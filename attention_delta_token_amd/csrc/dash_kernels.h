@@ -72,6 +72,12 @@ hipError_t launch_wo_gemm(int dtype, const void* A, const void* W, void* U, floa
 hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_first, int keep_last,
                        const int32_t* pos, const int32_t* n_dev, int32_t* idx, int32_t* n_out, int32_t* nan_out,
                        hipStream_t stream);
+// Single rows longer than 32768 scores (after the forced ends) over many
+// workgroups; scratch of topk_multi_ws_bytes bytes (0: the row is too short).
+size_t topk_multi_ws_bytes(int n_row, int keep_first, int keep_last);
+hipError_t launch_topk_multi(const float* score, int n_row, int k_total, int keep_first, int keep_last,
+                             const int32_t* pos, int32_t* idx, int32_t* n_out, int32_t* nan_out, void* scratch,
+                             hipStream_t stream);
 // Ragged top-k: sample b's scores are cu_n[b] .. cu_n[b+1]-1 of `score`
 // (n_total entries); it keeps cu_k[b+1] - cu_k[b] of them, written as packed
 // row indices to idx[cu_k[b] ..] (capacity k_cap); max_n bounds every

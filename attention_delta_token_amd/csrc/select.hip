@@ -754,6 +754,278 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// One long row over many workgroups (top-k of a single row longer than
+// kMultiMin scores, with a workspace): the row is cut into slices of kMSlice
+// consecutive scores, one workgroup each, and the radix select runs as a
+// chain of short launches on the same stream:
+//   minmax  - each slice's smallest and largest key and NaN count;
+//   seed    - (one workgroup) the bits every key shares, the forced ends, the
+//             kept count and NaN total;
+//   hist    - each slice's histogram of the next digit of the keys that carry
+//             the settled prefix (LDS, written out per slice);
+//   scan    - (one workgroup) the slice histograms summed, the cut bin found;
+//             hist/scan repeat up to three times and stop once the cut bin is
+//             taken whole or every bit is settled;
+//   count   - each slice's (greater, equal) counts against the cut;
+//   emit    - each slice writes its kept positions after those of the slices
+//             before it, ascending, ties to the lower position.
+// The state between launches lives in the workspace; no global atomics and no
+// grid-wide waits, so the result is deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kMT = 256;                // threads per workgroup
+constexpr int kMItems = 8;              // consecutive scores per thread
+constexpr int kMSlice = kMT * kMItems;  // scores per workgroup
+constexpr int kMultiMin = 32768;        // single rows longer than this take the chain
+
+struct MultiWs {
+  uint32_t* state;  // prefix, prefix mask, bits left, keys still wanted, taken whole
+  uint32_t* wg;     // [G][4]: min key, max key, NaN count
+  uint32_t* cnt;    // [G][2]: greater, equal
+  uint32_t* hist;   // [G][kBins]
+};
+
+__device__ __forceinline__ void multi_keys(const float* __restrict__ r, int n, uint32_t (&key)[kMItems],
+                                           int& valid) {
+  const int i0 = static_cast<int>(blockIdx.x) * kMSlice + static_cast<int>(threadIdx.x) * kMItems;
+  valid = min(kMItems, max(0, n - i0));
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e) key[e] = (e < valid) ? score_key(r[i0 + e]) : 0u;
+}
+
+__global__ __launch_bounds__(kMT)
+void topk_multi_minmax(const float* __restrict__ r, int n, MultiWs w) {
+  __shared__ uint32_t sh[3 * (kMT / kWave)];
+  uint32_t key[kMItems];
+  int valid;
+  multi_keys(r, n, key, valid);
+  uint32_t kmin = 0xffffffffu, kmax = 0u, nan = 0u;
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e) {
+    if (e < valid) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+      nan += key[e] == 0u;
+    }
+  }
+  kmin = wave_incl_scan_op(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
+  kmax = wave_incl_scan_op(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+  nan = wave_incl_scan32(nan);
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  if (lane == kWave - 1) {
+    sh[wid] = kmin;
+    sh[kMT / kWave + wid] = kmax;
+    sh[2 * (kMT / kWave) + wid] = nan;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = sh[0], b = sh[kMT / kWave], c = sh[2 * (kMT / kWave)];
+#pragma unroll
+    for (int i = 1; i < kMT / kWave; ++i) {
+      a = min(a, sh[i]);
+      b = max(b, sh[kMT / kWave + i]);
+      c += sh[2 * (kMT / kWave) + i];
+    }
+    w.wg[4 * blockIdx.x + 0] = a;
+    w.wg[4 * blockIdx.x + 1] = b;
+    w.wg[4 * blockIdx.x + 2] = c;
+  }
+}
+
+// row: the whole row (n_row scores); the middle n_mid = n_row - f - l take part.
+__global__ __launch_bounds__(kMT)
+void topk_multi_seed(const float* __restrict__ row, int n_row, int k_total, int f, int l, int G,
+                     const int32_t* __restrict__ pos, int32_t* __restrict__ out, int32_t* __restrict__ n_out,
+                     int32_t* __restrict__ nan_out, MultiWs w) {
+  __shared__ uint64_t sh_scan[2 * (kMT / kWave) + 8];
+  __shared__ uint32_t sh_mm[2 * (kMT / kWave)];
+  emit_forced<kMT>(n_row, k_total, f, l, pos, 0, out);
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  uint32_t nan = nan_out ? forced_nans<kMT>(row, n_row, f, l) : 0u;
+  for (int g = threadIdx.x; g < G; g += kMT) {
+    kmin = min(kmin, w.wg[4 * g + 0]);
+    kmax = max(kmax, w.wg[4 * g + 1]);
+    nan += w.wg[4 * g + 2];
+  }
+  kmin = wave_incl_scan_op(kmin, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
+  kmax = wave_incl_scan_op(kmax, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  if (lane == kWave - 1) {
+    sh_mm[wid] = kmin;
+    sh_mm[kMT / kWave + wid] = kmax;
+  }
+  uint64_t tot;
+  (void)block_excl_scan<kMT>(nan, sh_scan, tot);  // also orders the sh_mm writes before the reads below
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 1; i < kMT / kWave; ++i) {
+      sh_mm[0] = min(sh_mm[0], sh_mm[i]);
+      sh_mm[kMT / kWave] = max(sh_mm[kMT / kWave], sh_mm[kMT / kWave + i]);
+    }
+    const uint32_t a = sh_mm[0], b = sh_mm[kMT / kWave];
+    if (nan_out) *nan_out = static_cast<int32_t>(tot);
+    if (n_out) *n_out = k_total;
+    const int common = a == b ? 32 : __clz(a ^ b);
+    const uint32_t pmask = static_cast<uint32_t>(0xffffffff00000000ull >> common);
+    const uint32_t kk = static_cast<uint32_t>(k_total - f - l);
+    const int n_mid = n_row - f - l;
+    w.state[0] = a & pmask;
+    w.state[1] = pmask;
+    w.state[2] = static_cast<uint32_t>(32 - common);
+    w.state[3] = kk;
+    w.state[4] = (common == 32 && kk == static_cast<uint32_t>(n_mid)) ? 1u : 0u;
+  }
+}
+
+__global__ __launch_bounds__(kMT)
+void topk_multi_hist(const float* __restrict__ r, int n, MultiWs w) {
+  __shared__ uint32_t h[kBins];
+  const uint32_t prefix = w.state[0], pmask = w.state[1];
+  const int sh = static_cast<int>(w.state[2]);
+  if (w.state[4] != 0u || sh <= 0) return;  // settled: nothing to count
+  const int wd = sh < 11 ? sh : 11;
+  const int shift = sh - wd;
+  const uint32_t dm = (1u << wd) - 1u;
+  for (int b = threadIdx.x; b < kBins; b += kMT) h[b] = 0u;
+  uint32_t key[kMItems];
+  int valid;
+  multi_keys(r, n, key, valid);
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e)
+    if (e < valid && (key[e] & pmask) == prefix) atomicAdd(&h[(key[e] >> shift) & dm], 1u);
+  __syncthreads();
+  uint32_t* gh = w.hist + static_cast<size_t>(blockIdx.x) * kBins;
+  for (int b = threadIdx.x; b < kBins; b += kMT) gh[b] = h[b];
+}
+
+constexpr int kScanT = 1024;  // one workgroup, two bins per thread
+
+__global__ __launch_bounds__(kScanT)
+void topk_multi_scan(int G, MultiWs w) {
+  __shared__ uint64_t sh_scan[2 * (kScanT / kWave) + 8];
+  const uint32_t prefix = w.state[0], pmask = w.state[1], kk = w.state[3];
+  const int sh = static_cast<int>(w.state[2]);
+  if (w.state[4] != 0u || sh <= 0) return;
+  const int wd = sh < 11 ? sh : 11;
+  const int shift = sh - wd;
+  const uint32_t dm = (1u << wd) - 1u;
+  const int nb = static_cast<int>(dm) + 1;
+  const int b0 = 2 * static_cast<int>(threadIdx.x);
+  uint32_t c0 = 0u, c1 = 0u;
+  for (int g = 0; g < G; ++g) {
+    const uint32_t* gh = w.hist + static_cast<size_t>(g) * kBins;
+    c0 += gh[b0];
+    c1 += gh[b0 + 1];
+  }
+  uint64_t tot;
+  const uint32_t below = static_cast<uint32_t>(block_excl_scan<kScanT>(c0 + c1, sh_scan, tot));
+  // keys strictly above bin b = total - (keys in bins <= b); the cut bin b
+  // satisfies above(b) < kk <= above(b) + count(b)
+  const uint32_t c[2] = {c0, c1};
+  uint32_t upto = below;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    upto += c[j];
+    const uint32_t above = static_cast<uint32_t>(tot) - upto;
+    if (b0 + j < nb && above < kk && kk <= above + c[j]) {
+      w.state[0] = prefix | (static_cast<uint32_t>(b0 + j) << shift);
+      w.state[1] = pmask | (dm << shift);
+      w.state[2] = static_cast<uint32_t>(shift);
+      w.state[3] = kk - above;
+      w.state[4] = (kk - above == c[j]) ? 1u : 0u;
+    }
+  }
+}
+
+// Kept keys against the cut: whole -> every key >= cut; otherwise every key
+// > cut and the first take_eq keys == cut in position order.
+__device__ __forceinline__ void multi_flags(const uint32_t (&key)[kMItems], int valid, uint32_t cut, bool whole,
+                                            uint32_t& gt_bits, uint32_t& eq_bits) {
+  gt_bits = 0u;
+  eq_bits = 0u;
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e) {
+    if (e < valid) {
+      if (key[e] > cut || (whole && key[e] == cut)) gt_bits |= 1u << e;
+      else if (key[e] == cut) eq_bits |= 1u << e;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kMT)
+void topk_multi_count(const float* __restrict__ r, int n, MultiWs w) {
+  __shared__ uint64_t sh_scan[2 * (kMT / kWave) + 8];
+  const uint32_t cut = w.state[0];
+  const bool whole = w.state[4] != 0u;
+  uint32_t key[kMItems];
+  int valid;
+  multi_keys(r, n, key, valid);
+  uint32_t gt_bits, eq_bits;
+  multi_flags(key, valid, cut, whole, gt_bits, eq_bits);
+  uint64_t tot;
+  (void)block_excl_scan<kMT>((static_cast<uint64_t>(__popc(gt_bits)) << 32) | __popc(eq_bits), sh_scan, tot);
+  if (threadIdx.x == 0) {
+    w.cnt[2 * blockIdx.x + 0] = static_cast<uint32_t>(tot >> 32);
+    w.cnt[2 * blockIdx.x + 1] = static_cast<uint32_t>(tot & 0xffffffffu);
+  }
+}
+
+// out: the outputs of the middle (the whole row's out + f); positions are
+// f + i, or pos[f + i] with a position map.
+__global__ __launch_bounds__(kMT)
+void topk_multi_emit(const float* __restrict__ r, int n, int f, int k_mid, const int32_t* __restrict__ pos,
+                     int32_t* __restrict__ out, MultiWs w) {
+  __shared__ uint64_t sh_scan[2 * (kMT / kWave) + 8];
+  const uint32_t cut = w.state[0], take_eq = w.state[3];
+  const bool whole = w.state[4] != 0u;
+  // (greater, equal) counts of the slices before this one
+  uint64_t before = 0ull;
+  for (int g = threadIdx.x; g < static_cast<int>(blockIdx.x); g += kMT)
+    before += (static_cast<uint64_t>(w.cnt[2 * g]) << 32) | w.cnt[2 * g + 1];
+  uint64_t tb;
+  (void)block_excl_scan<kMT>(before, sh_scan, tb);
+  const uint32_t gt_before = static_cast<uint32_t>(tb >> 32), eq_before = static_cast<uint32_t>(tb & 0xffffffffu);
+  uint32_t key[kMItems];
+  int valid;
+  multi_keys(r, n, key, valid);
+  uint32_t gt_bits, eq_bits;
+  multi_flags(key, valid, cut, whole, gt_bits, eq_bits);
+  uint64_t tot;
+  const uint64_t excl =
+      block_excl_scan<kMT>((static_cast<uint64_t>(__popc(gt_bits)) << 32) | __popc(eq_bits), sh_scan, tot);
+  uint32_t eq_rank = eq_before + static_cast<uint32_t>(excl & 0xffffffffu);
+  uint32_t o = gt_before + min(eq_before, take_eq) + static_cast<uint32_t>(excl >> 32) +
+               (min(eq_rank, take_eq) - min(eq_before, take_eq));
+  const int i0 = static_cast<int>(blockIdx.x) * kMSlice + static_cast<int>(threadIdx.x) * kMItems;
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e) {
+    bool take = (gt_bits >> e) & 1u;
+    if ((eq_bits >> e) & 1u) {
+      take = eq_rank < take_eq;
+      ++eq_rank;
+    }
+    if (take) {
+      if (o < static_cast<uint32_t>(k_mid)) out[o] = pos ? pos[f + i0 + e] : f + i0 + e;
+      ++o;
+    }
+  }
+}
+
+MultiWs multi_ws_layout(void* base, int G) {
+  auto a256 = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  unsigned char* p = static_cast<unsigned char*>(base);
+  MultiWs w;
+  w.state = reinterpret_cast<uint32_t*>(p);
+  p += 256;
+  w.wg = reinterpret_cast<uint32_t*>(p);
+  p += a256(static_cast<size_t>(G) * 16);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += a256(static_cast<size_t>(G) * 8);
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  return w;
+}
+
 // n: the row length (ragged: the packed score count); n_longest: the longest
 // row (picks the kernel); cu_n / cu_k: ragged layout or null; n_dev: device
 // count of a single fixed row or null.
@@ -810,6 +1082,35 @@ hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_firs
     launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, nullptr, nullptr, n_dev, n_out,
                                 nan_out, stream);
   }
+  return hipGetLastError();
+}
+
+size_t topk_multi_ws_bytes(int n_row, int keep_first, int keep_last) {
+  const int n_mid = n_row - keep_first - keep_last;
+  if (n_mid <= kMultiMin) return 0;
+  const size_t G = static_cast<size_t>((n_mid + kMSlice - 1) / kMSlice);
+  auto a256 = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  return 256 + a256(G * 16) + a256(G * 8) + a256(G * kBins * 4);
+}
+
+hipError_t launch_topk_multi(const float* score, int n_row, int k_total, int keep_first, int keep_last,
+                             const int32_t* pos, int32_t* idx, int32_t* n_out, int32_t* nan_out, void* scratch,
+                             hipStream_t stream) {
+  const int f = keep_first, l = keep_last;
+  const int n_mid = n_row - f - l, k_mid = k_total - f - l;
+  if (n_mid <= kMultiMin || k_mid <= 0 || !scratch) return hipErrorInvalidValue;
+  const int G = (n_mid + kMSlice - 1) / kMSlice;
+  const MultiWs w = multi_ws_layout(scratch, G);
+  const float* r = score + f;
+  hipLaunchKernelGGL(topk_multi_minmax, dim3(G), dim3(kMT), 0, stream, r, n_mid, w);
+  hipLaunchKernelGGL(topk_multi_seed, dim3(1), dim3(kMT), 0, stream, score, n_row, k_total, f, l, G, pos, idx, n_out,
+                     nan_out, w);
+  for (int pass = 0; pass < 3; ++pass) {  // 32 key bits: at most 11 + 11 + 10
+    hipLaunchKernelGGL(topk_multi_hist, dim3(G), dim3(kMT), 0, stream, r, n_mid, w);
+    hipLaunchKernelGGL(topk_multi_scan, dim3(1), dim3(kScanT), 0, stream, G, w);
+  }
+  hipLaunchKernelGGL(topk_multi_count, dim3(G), dim3(kMT), 0, stream, r, n_mid, w);
+  hipLaunchKernelGGL(topk_multi_emit, dim3(G), dim3(kMT), 0, stream, r, n_mid, f, k_mid, pos, idx + f, w);
   return hipGetLastError();
 }
 

@@ -76,7 +76,7 @@ class OneShotStack:
         self.Ua = torch.empty(*lead, kk, hidden, device=dev, dtype=dt)
         dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
         self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(B, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
-        self.status = L.select_status(B, device=dev)
+        self.status = L.select_status(B, device=dev, n_max=S)
         self.record_post = False  # keep a copy of every post-halt layer's Oa and Ua (tests)
         self.trace = []
 

@@ -373,16 +373,19 @@ def main():
 
 
 def gpu_clocks():
-    """Current shader and memory clocks as rocm-smi reports them (clocks are
-    not pinned; recorded for context), or None when the tool is unavailable."""
+    """Current shader and memory clocks and the package power as rocm-smi
+    reports them (clocks are not pinned; recorded for context), or None when
+    the tool is unavailable."""
     import subprocess
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
         data = json.loads(r.stdout)
     except Exception:  # noqa: BLE001 - best effort only
         return None
     card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
-    return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()} or None
+    keep = ("sclk", "mclk", "power")
+    return {k: v for k, v in card.items() if any(x in k.lower() for x in keep)} or None
 
 
 def select_sweep(dash, torch, dev, rows=256, n=65536):

@@ -190,7 +190,12 @@ int dash_attn_layer_noalloc(void* ctx, const dash_shape* s,
  *   ranks or updates, forced ends included) is written to the int32 word r of
  *   ws; ws == NULL skips the count.
  * Workspace: dash_workspace_size(DASH_OP_SELECT, {B = rows, ...}, n_max)
- * bytes (4 per row, at least 256) when the NaN status is wanted. */
+ * bytes (4 per row, at least 256) when the NaN status is wanted.  For a
+ * single row (rows == 1, no n_dev) whose middle (n_max - keep_first -
+ * keep_last) exceeds 32768 scores, that size also covers the scratch of a
+ * top-k spread over many workgroups (a chain of short launches), which runs
+ * whenever the workspace is that large; with a smaller workspace (or none)
+ * the row takes one workgroup.  Same results either way. */
 int dash_select(void* ctx, const dash_sel* p, const float* score, const int32_t* pos,
                 const int32_t* n_dev, int n_max, int rows,
                 int32_t* idx, int32_t* n_out_dev, float* tau_out,

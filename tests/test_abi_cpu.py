@@ -323,6 +323,13 @@ def test_workspace_size(lib):
     # selection: one int32 NaN count per row (B rows), at least 256 bytes
     assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(_shape(B=1)), 8192) == 256
     assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(_shape(B=100)), 8192) == 512
+    # one row longer than 32768 scores: plus the multi-workgroup top-k's scratch
+    # (state 256 B; per 2048-score slice 16 B of extrema, 8 B of counts and a
+    # 2048-bin histogram, each array in 256-byte granules): 131072 -> 64 slices
+    assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(_shape(B=1)), 32768) == 256
+    assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(_shape(B=1)), 131072) == \
+        256 + 256 + 1024 + 512 + 64 * 2048 * 4
+    assert lib.dash_workspace_size(None, L.DASH_OP_SELECT, ctypes.byref(_shape(B=2)), 131072) == 256
     assert lib.dash_workspace_size(None, 17, ctypes.byref(s), 8192) == 0
     assert lib.dash_workspace_size(None, L.DASH_OP_ATTN_LAYER, ctypes.byref(_shape(D=33)), 8192) == 0
 

@@ -82,6 +82,38 @@ def test_topk_bit_exact(dash, kind, n):
         np.testing.assert_array_equal(idx.cpu().numpy()[:k], exp)
 
 
+@pytest.mark.parametrize("n", [32769, 40000, 65536 + 17, 131072, 262144 + 5])
+@pytest.mark.parametrize("kind", SCORE_KINDS)
+def test_topk_long_row_multi_workgroup(dash, kind, n):
+    """One row longer than 32768 scores with a workspace large enough for the
+    multi-workgroup top-k: bit-exact against the oracle for k from 1 to n,
+    with forced ends and a position map, NaN count in the status word; the
+    same outputs as the one-workgroup kernel (no workspace)."""
+    s = score_vector(kind, n, seed=7 * n + 1)
+    sd = torch.from_numpy(s).cuda()
+    st = dash.select_status(1, n_max=n)
+    for k, f, l in ((1, 0, 0), (n // 3, 0, 0), (n // 2 + 1, 0, 0), (n - 1, 0, 0), (n, 0, 0), (4096, 64, 32),
+                    (n - 5, 3, 2)):
+        say("topk long row", kind, n, k, f, l)
+        st.fill_(-1)
+        idx = torch.full((k,), -7, dtype=torch.int32, device="cuda")
+        dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, keep_first=f, keep_last=l, status=st)
+        ref = torch.full((k,), -9, dtype=torch.int32, device="cuda")
+        dash.dash_select(sd, ref, mode=dash.DASH_SEL_TOPK, k=k, keep_first=f, keep_last=l)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        np.testing.assert_array_equal(got, oracle.select_topk_forced(s, k, f, l))
+        np.testing.assert_array_equal(got, ref.cpu().numpy())
+        assert int(st[0].item()) == int(np.isnan(s).sum())
+    # position map (the multi-shot layout): positions are pos[i]
+    pos = torch.from_numpy(np.arange(n, dtype=np.int32) * 3 + 11).cuda()
+    k = n // 4
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, pos=pos, status=st)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.select_topk(s, k) * 3 + 11)
+
+
 @pytest.mark.parametrize("n", [8192, 8188, 4096, 2048, 1028])
 @pytest.mark.parametrize("kind", SCORE_KINDS)
 def test_topk_wave_rows_all_kinds(dash, kind, n):
