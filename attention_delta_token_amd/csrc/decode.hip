@@ -14,6 +14,8 @@
 // unnormalised output) in the workspace, and a second kernel merges the
 // chunks in a fixed order.  The work per byte of cache is tiny (VALU); what
 // matters is that many waves stream the cache at once with no serial step.
+#include <algorithm>
+
 #include "dash_common.h"
 #include "dash_kernels.h"
 
@@ -23,7 +25,8 @@ namespace {
 
 constexpr int kDecStep = kWave;       // keys per wave step (one per lane)
 constexpr int kDecMaxRows = 32;        // g * n_new rows per kv-head
-constexpr int kDecMaxChunks = 1024;    // key chunks per (sample, kv-head)
+constexpr int kDecMaxChunks = 1024;    // key chunks per (sample, kv-head), at most
+constexpr int kDecTargetGroups = 512;  // chunk workgroups per launch the split aims at
 
 // Wave-wide max / sum in registers: a rotate butterfly inside each 16-lane
 // row (DPP row_ror 8, 4, 2, 1), then the four row results through readlane,
@@ -330,12 +333,14 @@ void decode_merge_kernel(const float* __restrict__ part, int n_new, int Hq, int 
 }  // namespace
 
 int decode_chunks(int B, int S_cap, int Hkv, int* steps_out) {
-  // one wave per 64 keys while that gives at most kDecMaxChunks chunks per
-  // (sample, kv-head); longer caches give each wave several 64-key steps
-  (void)B;
-  (void)Hkv;
+  // one workgroup per 64 keys while that gives at most about kDecTargetGroups
+  // chunk workgroups in all (between 8 and kDecMaxChunks per (sample,
+  // kv-head)); longer caches give each workgroup several 64-key steps, which
+  // keeps the merge of the chunks short
+  const int64_t groups = static_cast<int64_t>(B > 0 ? B : 1) * (Hkv > 0 ? Hkv : 1);
+  const int64_t cap = std::max<int64_t>(8, std::min<int64_t>(kDecMaxChunks, kDecTargetGroups / groups));
   const int64_t tiles = (static_cast<int64_t>(S_cap) + kDecStep - 1) / kDecStep;
-  const int64_t steps = (tiles + kDecMaxChunks - 1) / kDecMaxChunks;
+  const int64_t steps = (tiles + cap - 1) / cap;
   *steps_out = static_cast<int>(steps < 1 ? 1 : steps);
   return static_cast<int>((tiles + *steps_out - 1) / *steps_out);
 }
