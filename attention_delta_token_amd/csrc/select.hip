@@ -393,6 +393,7 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
                      const int32_t* __restrict__ cu_k, const int32_t* __restrict__ n_dev,
                      int32_t* __restrict__ n_out, int32_t* __restrict__ nan_out) {
   static_assert(ITEMS <= 32, "masks are 32-bit");
+  using Mask = uint32_t;
   __shared__ uint32_t hist[kCopies * kBins];
   __shared__ uint64_t sh_scan[2 * (NT / kWave) + 8];
   __shared__ uint32_t sh_cut[2];
@@ -408,7 +409,16 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
   const int i0 = threadIdx.x * ITEMS;
   uint32_t keys[ITEMS];
 #pragma unroll
-  for (int e = 0; e < ITEMS; ++e) keys[e] = (i0 + e < n) ? score_key(r[i0 + e]) : 0u;
+  for (int e = 0; e < ITEMS; ++e) keys[e] = 0u;
+  if (n > 0) {
+    // every load unconditional (positions past the row re-read its last
+    // score; they are excluded through `valid` below), so all are in flight
+    // before the first is used
+#pragma unroll
+    for (int e = 0; e < ITEMS; ++e) keys[e] = __float_as_uint(r[min(i0 + e, n - 1)]);
+#pragma unroll
+    for (int e = 0; e < ITEMS; ++e) keys[e] = score_key(__uint_as_float(keys[e]));
+  }
   const int valid = n - i0;  // keys e < valid exist
   uint32_t nan = 0u;
   if (nan_out) {
@@ -421,18 +431,23 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
     return;
   }
   auto for_keys = [&](auto&& fn) {
+    // `valid` made opaque at every call: the per-item tests stay next to
+    // their use instead of being kept as one compare mask per item across
+    // the radix passes (scalar-register pressure)
+    int vld = valid;
+    asm volatile("" : "+v"(vld));
 #pragma unroll
     for (int e = 0; e < ITEMS; ++e)
-      if (e < valid) fn(keys[e]);
+      if (e < vld) fn(keys[e]);
   };
   uint32_t take_eq;
   const uint32_t cut = radix_cut<NT, true>(for_keys, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
-  uint32_t gt_mask = 0u, eq_mask = 0u;
+  Mask gt_mask = 0u, eq_mask = 0u;
 #pragma unroll
   for (int e = 0; e < ITEMS; ++e) {
     if (e < valid) {
-      if (keys[e] > cut) gt_mask |= 1u << e;
-      else if (keys[e] == cut) eq_mask |= 1u << e;
+      if (keys[e] > cut) gt_mask |= Mask(1) << e;
+      else if (keys[e] == cut) eq_mask |= Mask(1) << e;
     }
   }
   const uint32_t gt = __popc(gt_mask), eq = __popc(eq_mask);
