@@ -415,8 +415,16 @@ int dash_select(void* /*ctx*/, const dash_sel* p, const float* score, const int3
         if (pos && static_cast<const void*>(pos) == static_cast<const void*>(idx))
           return fail(DASH_E_INVAL, "idx must not alias pos");
         tr = trace_open(DASH_TR_SELECT, st);
-        e = dash::launch_threshold(score, pos, n_dev, n_max, p->tau, p->patience, p->counters, p->n_counters, idx,
-                                   n_out_dev, nan_out, st);
+        // more than 32768 rows run over many workgroups when the workspace holds
+        // their scratch (after the status word)
+        const size_t multi = dash::topk_multi_ws_bytes(n_max, 0, 0);
+        const size_t status_bytes = align_up(sizeof(int32_t));
+        if (multi > 0 && ws && ws_bytes >= status_bytes + multi)
+          e = dash::launch_threshold_multi(score, pos, n_dev, n_max, p->tau, p->patience, p->counters, p->n_counters,
+                                           idx, n_out_dev, nan_out, static_cast<unsigned char*>(ws) + status_bytes, st);
+        else
+          e = dash::launch_threshold(score, pos, n_dev, n_max, p->tau, p->patience, p->counters, p->n_counters, idx,
+                                     n_out_dev, nan_out, st);
         break;
       }
       default:

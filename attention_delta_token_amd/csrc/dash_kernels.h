@@ -90,6 +90,11 @@ hipError_t launch_order_stat(const float* score, const int32_t* n_dev, int n_max
 hipError_t launch_threshold(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,
                             const float* tau, int patience, uint8_t* counters, int n_counters, int32_t* out,
                             int32_t* n_out, int32_t* nan_out, hipStream_t stream);
+// The same step over many workgroups for more than 32768 rows (capacity),
+// with topk_multi_ws_bytes(n_max, 0, 0) bytes of scratch.
+hipError_t launch_threshold_multi(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,
+                                  const float* tau, int patience, uint8_t* counters, int n_counters, int32_t* out,
+                                  int32_t* n_out, int32_t* nan_out, void* scratch, hipStream_t stream);
 
 hipError_t launch_row_norm(int dtype, const void* U, const int32_t* n_dev, int n_max, int hidden, float* score,
                            hipStream_t stream);

@@ -1027,6 +1027,104 @@ void topk_multi_emit(const float* __restrict__ r, int n, int f, int k_mid, const
   }
 }
 
+// Threshold step over many workgroups (one row longer than kMultiMin rows,
+// with a workspace): slice g's rows are updated (counters written, the same
+// rule as threshold_kernel) and their survivors counted in one launch; the
+// second launch writes each slice's survivors after those of the slices
+// before it, re-reading the updated counters to tell them.  The slice counts
+// live in the workspace (cnt[g] = survivors, NaN scores).
+__device__ __forceinline__ int thr_rows(const int32_t* __restrict__ n_dev, int n_max) {
+  int n = n_dev ? *n_dev : n_max;
+  return max(0, min(n, n_max));
+}
+
+__global__ __launch_bounds__(kMT)
+void threshold_multi_update(const float* __restrict__ score, const int32_t* __restrict__ pos,
+                            const int32_t* __restrict__ n_dev, int n_max, const float* __restrict__ tau_p,
+                            int patience, uint8_t* __restrict__ counters, int n_counters, MultiWs w) {
+  __shared__ uint64_t sh_scan[2 * (kMT / kWave) + 8];
+  const int n = thr_rows(n_dev, n_max);
+  const int i0 = static_cast<int>(blockIdx.x) * kMSlice + static_cast<int>(threadIdx.x) * kMItems;
+  if (static_cast<int>(blockIdx.x) * kMSlice >= n) return;  // the whole workgroup: no slice rows
+  const float tau = *tau_p;
+  int32_t p[kMItems];
+  float sc[kMItems];
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e) {
+    const int i = min(i0 + e, n - 1);  // unconditional loads; rows past n are not used
+    p[e] = pos ? pos[i] : i;
+    sc[e] = score[i];
+  }
+  uint32_t kept = 0u, nan = 0u;
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e) {
+    if (i0 + e < n) {
+      nan += score_key(sc[e]) == 0u;
+      if (p[e] >= 0 && p[e] < n_counters) {  // positions outside the counters are dropped
+        const uint32_t c = (sc[e] < tau) ? static_cast<uint32_t>(counters[p[e]]) + 1u : 0u;
+        counters[p[e]] = static_cast<uint8_t>(c > 255u ? 255u : c);
+        kept += c < static_cast<uint32_t>(patience);
+      }
+    }
+  }
+  uint64_t tot;
+  (void)block_excl_scan<kMT>((static_cast<uint64_t>(kept) << 32) | nan, sh_scan, tot);
+  if (threadIdx.x == 0) {
+    w.cnt[2 * blockIdx.x + 0] = static_cast<uint32_t>(tot >> 32);
+    w.cnt[2 * blockIdx.x + 1] = static_cast<uint32_t>(tot & 0xffffffffu);
+  }
+}
+
+__global__ __launch_bounds__(kMT)
+void threshold_multi_emit(const int32_t* __restrict__ pos, const int32_t* __restrict__ n_dev, int n_max,
+                          int patience, const uint8_t* __restrict__ counters, int n_counters,
+                          int32_t* __restrict__ out, int32_t* __restrict__ n_out, int32_t* __restrict__ nan_out,
+                          int G, MultiWs w) {
+  __shared__ uint64_t sh_scan[2 * (kMT / kWave) + 8];
+  const int n = thr_rows(n_dev, n_max);
+  const int g_used = (n + kMSlice - 1) / kMSlice;  // slices that hold rows (and wrote their counts)
+  const int g = static_cast<int>(blockIdx.x);
+  // survivors of the slices before this one (slice 0 also totals every slice)
+  uint64_t before = 0ull, all = 0ull;
+  for (int j = threadIdx.x; j < g_used; j += kMT) {
+    const uint64_t v = (static_cast<uint64_t>(w.cnt[2 * j]) << 32) | w.cnt[2 * j + 1];
+    if (j < g) before += v;
+    all += v;
+  }
+  uint64_t tb, ta;
+  (void)block_excl_scan<kMT>(before, sh_scan, tb);
+  if (g == 0) {
+    (void)block_excl_scan<kMT>(all, sh_scan, ta);
+    if (threadIdx.x == 0) {
+      *n_out = static_cast<int32_t>(ta >> 32);
+      if (nan_out) *nan_out = static_cast<int32_t>(ta & 0xffffffffu);
+    }
+  }
+  if (g >= g_used) return;
+  const int i0 = g * kMSlice + static_cast<int>(threadIdx.x) * kMItems;
+  uint32_t keep_bits = 0u;
+  int32_t p[kMItems];
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e) {
+    const int i = min(i0 + e, n - 1);
+    p[e] = pos ? pos[i] : i;
+  }
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e)
+    if (i0 + e < n && p[e] >= 0 && p[e] < n_counters && counters[p[e]] < static_cast<uint32_t>(patience))
+      keep_bits |= 1u << e;
+  uint64_t tot;
+  const uint32_t o0 = static_cast<uint32_t>(tb >> 32) +
+                      static_cast<uint32_t>(block_excl_scan<kMT>(__popc(keep_bits), sh_scan, tot));
+  uint32_t o = o0;
+#pragma unroll
+  for (int e = 0; e < kMItems; ++e)
+    if (keep_bits & (1u << e)) {
+      if (o < static_cast<uint32_t>(n_max)) out[o] = p[e];  // never beyond the capacity
+      ++o;
+    }
+}
+
 MultiWs multi_ws_layout(void* base, int G) {
   auto a256 = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   unsigned char* p = static_cast<unsigned char*>(base);
@@ -1141,6 +1239,19 @@ hipError_t launch_order_stat(const float* score, const int32_t* n_dev, int n_max
                              int32_t* nan_out, hipStream_t stream) {
   hipLaunchKernelGGL(order_stat_kernel, dim3(1), dim3(kSelThreads), 0, stream, score, n_dev, n_max, rank,
                      tau_out, nan_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_threshold_multi(const float* score, const int32_t* pos, const int32_t* n_dev, int n_max,
+                                  const float* tau, int patience, uint8_t* counters, int n_counters, int32_t* out,
+                                  int32_t* n_out, int32_t* nan_out, void* scratch, hipStream_t stream) {
+  if (n_max <= kMultiMin || !scratch) return hipErrorInvalidValue;
+  const int G = (n_max + kMSlice - 1) / kMSlice;
+  const MultiWs w = multi_ws_layout(scratch, G);
+  hipLaunchKernelGGL(threshold_multi_update, dim3(G), dim3(kMT), 0, stream, score, pos, n_dev, n_max, tau, patience,
+                     counters, n_counters, w);
+  hipLaunchKernelGGL(threshold_multi_emit, dim3(G), dim3(kMT), 0, stream, pos, n_dev, n_max, patience, counters,
+                     n_counters, out, n_out, nan_out, G, w);
   return hipGetLastError();
 }
 

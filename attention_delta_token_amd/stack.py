@@ -331,7 +331,7 @@ class ThresholdStack:
         self.Oa = torch.empty(S, Hq * D, device=dev, dtype=dt)
         dtc = L.DASH_BF16 if dt == torch.bfloat16 else L.DASH_F32
         self.ws = L.workspace(L.DASH_OP_ATTN_LAYER, L.make_shape(1, S, Hq, Hkv, D, hidden, dtc), S, device=dev)
-        self.status = L.select_status(1, device=dev)
+        self.status = L.select_status(1, device=dev, n_max=S)
         self.record = record                  # keep per-layer host-visible copies (tests, measurement)
         self.record_outputs = record_outputs  # ... including scores and U, not only the active sets
         self.trace = []

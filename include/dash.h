@@ -195,7 +195,9 @@ int dash_attn_layer_noalloc(void* ctx, const dash_shape* s,
  * keep_last) exceeds 32768 scores, that size also covers the scratch of a
  * top-k spread over many workgroups (a chain of short launches), which runs
  * whenever the workspace is that large; with a smaller workspace (or none)
- * the row takes one workgroup.  Same results either way. */
+ * the row takes one workgroup.  The threshold step with n_max > 32768 uses
+ * the same scratch the same way (two launches; a device count n_dev is
+ * allowed).  Same results either way. */
 int dash_select(void* ctx, const dash_sel* p, const float* score, const int32_t* pos,
                 const int32_t* n_dev, int n_max, int rows,
                 int32_t* idx, int32_t* n_out_dev, float* tau_out,

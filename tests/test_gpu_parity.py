@@ -82,6 +82,56 @@ def test_topk_bit_exact(dash, kind, n):
         np.testing.assert_array_equal(idx.cpu().numpy()[:k], exp)
 
 
+@pytest.mark.parametrize("n_max,n,with_pos", [(40000, 40000, False), (65536, 65536, True), (65536, 33000, True),
+                                               (131072, 100001, True), (70000, 0, True)])
+def test_threshold_step_multi_workgroup(dash, n_max, n, with_pos):
+    """Threshold steps over more than 32768 rows with a workspace large enough
+    for the multi-workgroup kernels: survivors, counters, survivor count and
+    NaN count bit-exact against the oracle's step and against the
+    one-workgroup kernel (no workspace); device row count, positions outside
+    the counters (dropped), NaN scores, two steps in a row."""
+    rng = np.random.default_rng(n_max + n)
+    S = n_max + 5000
+    s = np.abs(rng.standard_normal(n_max)).astype(np.float32)
+    s[rng.choice(n_max, 50, replace=False)] = np.nan
+    if with_pos:
+        posv = np.sort(rng.choice(S, n_max, replace=False)).astype(np.int32)
+        posv[-3:] = [S + 1, S + 9, -4][: min(3, n_max)]  # outside the counters: dropped
+    else:
+        posv = np.arange(n_max, dtype=np.int32)
+    S_c = S if with_pos else n_max
+    c0 = rng.integers(0, 3, S_c).astype(np.uint8)
+    tau = np.float32(0.6)
+    sd = torch.from_numpy(s).cuda()
+    pd = torch.from_numpy(posv).cuda() if with_pos else None
+    nd = torch.tensor([n], dtype=torch.int32, device="cuda")
+    tdev = torch.tensor([tau], device="cuda")
+    say("threshold multi", n_max, n, with_pos)
+    outs = []
+    for status in (dash.select_status(1, n_max=n_max), None):
+        cnt = torch.from_numpy(c0.copy()).cuda()
+        for _ in range(2):
+            out = torch.full((n_max,), -7, dtype=torch.int32, device="cuda")
+            nout = torch.zeros(1, dtype=torch.int32, device="cuda")
+            st = status if status is not None else dash.select_status(1)
+            dash.dash_select(sd, out, mode=dash.DASH_SEL_THRESHOLD, tau=tdev, patience=2, counters=cnt, pos=pd,
+                             n_dev=nd, n_max=n_max, n_out=nout, status=st)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy()[: int(nout.item())], cnt.cpu().numpy(), int(st[0].item())))
+    # the oracle: two steps over the first n rows (positions outside the counters dropped)
+    rows = posv[:n]
+    keep_rows = (rows >= 0) & (rows < S_c)
+    c = c0.copy()
+    for _ in range(2):
+        exp_pos, c_new = oracle.threshold_step(s[:n][keep_rows], rows[keep_rows], c, tau, 2)
+        c = c_new
+    np.testing.assert_array_equal(outs[0][0], exp_pos)
+    np.testing.assert_array_equal(outs[0][1], c)
+    assert outs[0][2] == int(np.isnan(s[:n]).sum())
+    for a, b in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b)
+
+
 @pytest.mark.parametrize("n", [32769, 40000, 65536 + 17, 131072, 262144 + 5])
 @pytest.mark.parametrize("kind", SCORE_KINDS)
 def test_topk_long_row_multi_workgroup(dash, kind, n):
