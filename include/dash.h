@@ -17,6 +17,9 @@
  *   - All tensor pointers are DEVICE pointers, 16-byte aligned, owned by the
  *     caller.  The library never allocates or frees device memory; scratch
  *     space comes from the caller's workspace (size from dash_workspace_size).
+ *     A call uses its workspace until its last launch has run on its stream:
+ *     calls that may overlap in time (other streams) must not share one.
+ *     Nothing in a workspace needs to start at any particular value.
  *   - Every call is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the default stream) and returns without waiting.  Counts that depend on
  *     the data stay on the device (n_dev / n_out_dev), so no call performs a
