@@ -8,10 +8,13 @@
 //
 // bf16 path: 256x256 output tile per 512-thread workgroup (8 waves of 64x128),
 // K stepped by 64, operands streamed into a double-buffered LDS ring by direct
-// global->LDS loads (no register staging) one step ahead of the MFMAs
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation); rows are XOR-swizzled so the
-// operand reads are free of bank conflicts, and tiles are grouped so the
-// workgroups running together share their A rows and W slices in L2.  The tile is computed transposed (C^T = Wo_tile · O_tile^T) so
+// global->LDS loads (no register staging) a whole step ahead of their use
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  Inside a step the operand
+// reads of each 16-wide k-step are issued between the MFMAs of the previous
+// one in a fixed order, so two waves per SIMD keep the matrix unit fed; rows
+// are XOR-swizzled so the operand reads are free of bank conflicts, and tiles
+// are grouped so the workgroups running together share their A rows and W
+// slices in L2.  The tile is computed transposed (C^T = Wo_tile · O_tile^T) so
 // that every lane holds a single output row: the row's sum of squares is then
 // accumulated in registers straight from the fp32 accumulators, before U is
 // rounded to bf16.  Each (row, column tile) partial is written to the
@@ -19,6 +22,7 @@
 // the square root, so the score is bit-reproducible run to run (no atomics).
 // A 224-column variant (below) is picked when it fills the chip better.
 #include <atomic>
+#include <type_traits>
 
 #include "dash_common.h"
 #include "dash_kernels.h"
@@ -45,8 +49,10 @@ constexpr int kMB = 2;                                  // 32-row blocks per wav
 // Row r keeps its 16-byte chunk c at slot c ^ ((r / kRowsPerLine) % kRowChunks):
 // the 16 lanes of one 16-byte operand read (16 consecutive rows) then hit
 // distinct banks of the 64-bank LDS.
+template <int RB = kRowBytes>
 __device__ __forceinline__ int gemm_slot(int row, int chunk) {
-  return chunk ^ ((row / kRowsPerLine) % kRowChunks);
+  constexpr int kChunksT = RB / 16, kPerLineT = 256 / RB;
+  return chunk ^ ((row / kPerLineT) % kChunksT);
 }
 
 // Buffer resource over `bytes` bytes from `base` (capped at the 32-bit range,
@@ -61,26 +67,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_rsrc(const void* base, in
 // offset (row, swizzled chunk) is fixed and the k step rides in the scalar
 // offset; rows past the matrix edge read zeros (their results are never
 // stored).  The wave index is made uniform so the LDS destinations stay scalar.
-template <int BN>
+template <int BN, int NW = kGemmThreads / 64, int RB = kRowBytes>
 struct GemmLoadPlan {
-  static constexpr int kWBytes = BN * kRowBytes;
-  static constexpr int kStage = kATileBytes + kWBytes;
+  static constexpr int kABytes = kBM * RB;
+  static constexpr int kWBytes = BN * RB;
+  static constexpr int kStage = kABytes + kWBytes;
   static constexpr int kChunks = kStage / 1024;                              // 1 KiB per wave-wide load
-  static constexpr int kPerWave = (kChunks + kGemmThreads / 64 - 1) / (kGemmThreads / 64);
+  static constexpr int kPerWave = (kChunks + NW - 1) / NW;
   static_assert(kStage % 1024 == 0, "whole KiB per stage");
   __amdgpu_buffer_rsrc_t a_src, w_src;
   uint32_t voff[kPerWave];  // this lane's row and swizzled chunk, at k = 0
   __device__ __forceinline__ void init(const uint16_t* A, const uint16_t* W, int m0, int n0, int M, int N, int K) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    constexpr int kRowsPerKiB = 1024 / kRowBytes;
+    constexpr int kRowsPerKiB = 1024 / RB;
+    constexpr int kChunksPerRow = RB / 16;
     a_src = gemm_rsrc(A + static_cast<size_t>(m0) * K, static_cast<int64_t>(M - m0) * K * 2);
     w_src = gemm_rsrc(W + static_cast<size_t>(n0) * K, static_cast<int64_t>(N - n0) * K * 2);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int q = min(wave + 8 * i, kChunks - 1);  // 1 KiB chunk of the stage
-      const int is_a = q < kATileBytes / 1024;
-      const int local_row = (is_a ? q : q - kATileBytes / 1024) * kRowsPerKiB + lane / kRowChunks;
-      const int chunk = gemm_slot(local_row, lane % kRowChunks);
+      const int q = min(wave + NW * i, kChunks - 1);  // 1 KiB chunk of the stage
+      const int is_a = q < kABytes / 1024;
+      const int local_row = (is_a ? q : q - kABytes / 1024) * kRowsPerKiB + lane / kChunksPerRow;
+      const int chunk = gemm_slot<RB>(local_row, lane % kChunksPerRow);
       voff[i] = static_cast<uint32_t>(local_row) * static_cast<uint32_t>(K) * 2u + chunk * 16;
     }
   }
@@ -88,19 +96,49 @@ struct GemmLoadPlan {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
-      const int q = wave + 8 * i;
-      // A chunks are q < 32 = 4 per wave: load i of every wave is an A chunk iff i < 4
-      static_assert((kATileBytes / 1024) % 8 == 0, "A chunks split evenly over the waves");
-      if (8 * (i + 1) <= kChunks || q < kChunks)  // only the last load can be missing (wave-uniform)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < kATileBytes / 1024 / 8 ? a_src : w_src,
+      const int q = wave + NW * i;
+      // A chunks come first and split evenly over the waves: load i of every
+      // wave is an A chunk iff i < (A chunks) / NW
+      static_assert((kABytes / 1024) % NW == 0, "A chunks split evenly over the waves");
+      if (NW * (i + 1) <= kChunks || q < kChunks)  // only the last load can be missing (wave-uniform)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(i < kABytes / 1024 / NW ? a_src : w_src,
                                                  (__attribute__((address_space(3))) void*)(stage + q * 1024), 16,
                                                  voff[i], k0 * 2, 0, 0);
+    }
+  }
+  // After two issue() calls: wait until this wave's loads of the first have
+  // landed.  When the chunks do not split evenly, waves differ in how many
+  // loads a stage takes, so they wait for both.
+  __device__ __forceinline__ void wait_first_of_two() const {
+    if constexpr (kChunks % NW == 0) {
+      static_assert(kPerWave < 64, "vmcnt range");
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (kPerWave & 15) | ((kPerWave >> 4) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
     }
   }
 };
 
 __device__ __forceinline__ void wait_vmcnt_0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 __device__ __forceinline__ void wait_lgkm_0() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+
+// Issue order inside one 16-wide k-step: one MFMA first, then the LDS reads
+// of the next k-step (and, in the last k-step of a stage, the global->LDS
+// loads of the stage after next) one between each pair of the remaining
+// MFMAs, so that a read or load waiting for its unit does not hold up the
+// matrix unit.  Masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read.
+template <bool kLoads, bool kReads>
+__device__ __forceinline__ void gemm_ks_order() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    if (kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  if (kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
 
 __global__ __launch_bounds__(kGemmThreads, 1)
 void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
@@ -149,37 +187,65 @@ void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // The operands of 16-wide k-step ks+1 are read while step ks multiplies,
+  // and step kt+1's first operands are read during step kt's last MFMAs.
+  // Step kt+2 is loaded into step kt's stage as soon as every wave has read
+  // step kt (the barrier in the last k-step), a whole step ahead of its use.
+  // The last two steps are peeled off (no loads after them, no reads after
+  // the last) so that every k-step's issue order is fixed at compile time.
   const int KT = K / kBK;
-  plan.issue(lds, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_vmcnt_0();                 // this wave's part of step kt has landed
-    __builtin_amdgcn_s_barrier();   // ... and every wave's; step kt-1 is done
-    if (kt + 1 < KT) plan.issue(lds + ((kt + 1) & 1) * kStageBytes, (kt + 1) * kBK);
-    const unsigned char* st = lds + (kt & 1) * kStageBytes;
-    bf16x8 opw[2][kNB], opa[2][kMB];
+  auto stage = [&](int kt) { return lds + (kt & 1) * kStageBytes; };
+  bf16x8 opw[2][kNB], opa[2][kMB];
+  auto read_ks = [&](const unsigned char* st, int ks, int buf) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
-      opw[0][nb] = *reinterpret_cast<const bf16x8*>(st + w_row + nb * 32 * kRowBytes + koff[0]);
+      opw[buf][nb] = *reinterpret_cast<const bf16x8*>(st + w_row + nb * 32 * kRowBytes + koff[ks]);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb)
-      opa[0][mb] = *reinterpret_cast<const bf16x8*>(st + a_row + mb * 32 * kRowBytes + koff[0]);
+      opa[buf][mb] = *reinterpret_cast<const bf16x8*>(st + a_row + mb * 32 * kRowBytes + koff[ks]);
+  };
+  auto step = [&](int kt, auto loads_c, auto next_c) {
+    constexpr bool kLoadNext = decltype(loads_c)::value;  // kt + 2 < KT
+    constexpr bool kHasNext = decltype(next_c)::value;    // kt + 1 < KT
+    const unsigned char* st = stage(kt);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < kBK / 16) {  // operands of the next 16-wide step are read while this one multiplies
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          opw[cur ^ 1][nb] = *reinterpret_cast<const bf16x8*>(st + w_row + nb * 32 * kRowBytes + koff[ks + 1]);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-          opa[cur ^ 1][mb] = *reinterpret_cast<const bf16x8*>(st + a_row + mb * 32 * kRowBytes + koff[ks + 1]);
+      if (ks + 1 < kBK / 16) {
+        read_ks(st, ks + 1, cur ^ 1);
+      } else {
+        wait_lgkm_0();                 // this wave's reads of step kt are done
+        wait_vmcnt_0();                // its part of step kt+1 has landed
+        __builtin_amdgcn_s_barrier();  // ... and every wave's; no wave reads stage kt any more
+        __builtin_amdgcn_sched_barrier(0);
+        if (kLoadNext) plan.issue(stage(kt), (kt + 2) * kBK);
+        if (kHasNext) read_ks(stage(kt + 1), 0, cur ^ 1);
       }
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) acc[nb][mb] = mfma32x32x16(opw[cur][nb], opa[cur][mb], acc[nb][mb]);
+      if (ks + 1 < kBK / 16)
+        gemm_ks_order<false, true>();
+      else
+        gemm_ks_order<kLoadNext, kHasNext>();
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  plan.issue(stage(0), 0);
+  if (KT > 1) {
+    plan.issue(stage(1), kBK);
+    plan.wait_first_of_two();
+  } else {
+    wait_vmcnt_0();
   }
+  __builtin_amdgcn_s_barrier();
+  read_ks(stage(0), 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) step(kt, std::true_type{}, std::true_type{});
+  if (kt + 1 < KT) step(kt++, std::false_type{}, std::true_type{});
+  if (kt < KT) step(kt, std::false_type{}, std::false_type{});
 
   // ---- epilogue -----------------------------------------------------------
   // acc[nb][mb][r] = U[m][n] with m = m0 + wm*64 + mb*32 + l32,
@@ -260,6 +326,20 @@ constexpr int kStage224 = kATileBytes + kBN224 * kRowBytes;  // 60 KiB
 constexpr int kTB = 4;  // 16-token blocks per wave (64 tokens)
 constexpr int kCB = 7;  // 16-channel blocks per wave (112 channels)
 
+// Issue order of one 32-wide k-step of the 224-column kernel (28 MFMAs of
+// 16x16x32, 11 operand reads, up to 8 loads in the last k-step of a stage).
+template <bool kLoads, bool kReads>
+__device__ __forceinline__ void gemm224_ks_order() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+  for (int i = 0; i < 11; ++i) {
+    if (kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (kLoads && i < 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+}
+
 __global__ __launch_bounds__(kGemmThreads, 1)
 void wo_gemm_bf16_n224_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                               uint16_t* __restrict__ U, float* __restrict__ part,
@@ -304,33 +384,62 @@ void wo_gemm_bf16_n224_kernel(const uint16_t* __restrict__ A, const uint16_t* __
 #pragma unroll
     for (int j = 0; j < kTB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Same pipeline as the 256-column kernel, in 32-wide k-steps: the
+  // operands of the second half of a stage are read while the first half
+  // multiplies, and the next stage's first operands while the second does.
   const int KT = K / kBK;
-  plan.issue(lds, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_vmcnt_0();
-    __builtin_amdgcn_s_barrier();
-    if (kt + 1 < KT) plan.issue(lds + ((kt + 1) & 1) * kStage224, (kt + 1) * kBK);
-    const unsigned char* st = lds + (kt & 1) * kStage224;
-    bf16x8 opw[2][kCB], opa[2][kTB];
+  auto stage = [&](int kt) { return lds + (kt & 1) * kStage224; };
+  bf16x8 opw[2][kCB], opa[2][kTB];
+  auto read_ks = [&](const unsigned char* st, int ks, int buf) {
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb)
-      opw[0][cb] = *reinterpret_cast<const bf16x8*>(st + w_row + cb * 16 * kRowBytes + koff[0]);
+      opw[buf][cb] = *reinterpret_cast<const bf16x8*>(st + w_row + cb * 16 * kRowBytes + koff[ks]);
 #pragma unroll
     for (int tb = 0; tb < kTB; ++tb)
-      opa[0][tb] = *reinterpret_cast<const bf16x8*>(st + a_row + tb * 16 * kRowBytes + koff[0]);
+      opa[buf][tb] = *reinterpret_cast<const bf16x8*>(st + a_row + tb * 16 * kRowBytes + koff[ks]);
+  };
+  auto step = [&](int kt, auto loads_c, auto next_c) {
+    constexpr bool kLoadNext = decltype(loads_c)::value;  // kt + 2 < KT
+    constexpr bool kHasNext = decltype(next_c)::value;    // kt + 1 < KT
+    const unsigned char* st = stage(kt);
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
-      opw[1][cb] = *reinterpret_cast<const bf16x8*>(st + w_row + cb * 16 * kRowBytes + koff[1]);
-#pragma unroll
-    for (int tb = 0; tb < kTB; ++tb)
-      opa[1][tb] = *reinterpret_cast<const bf16x8*>(st + a_row + tb * 16 * kRowBytes + koff[1]);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < kBK / 32) {
+        read_ks(st, ks + 1, cur ^ 1);
+      } else {
+        wait_lgkm_0();
+        wait_vmcnt_0();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (kLoadNext) plan.issue(stage(kt), (kt + 2) * kBK);
+        if (kHasNext) read_ks(stage(kt + 1), 0, cur ^ 1);
+      }
 #pragma unroll
       for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-        for (int tb = 0; tb < kTB; ++tb) acc[cb][tb] = mfma16x16x32(opw[ks][cb], opa[ks][tb], acc[cb][tb]);
+        for (int tb = 0; tb < kTB; ++tb) acc[cb][tb] = mfma16x16x32(opw[cur][cb], opa[cur][tb], acc[cb][tb]);
+      if (ks + 1 < kBK / 32)
+        gemm224_ks_order<false, true>();
+      else
+        gemm224_ks_order<kLoadNext, kHasNext>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  plan.issue(stage(0), 0);
+  if (KT > 1) {
+    plan.issue(stage(1), kBK);
+    plan.wait_first_of_two();
+  } else {
+    wait_vmcnt_0();
   }
+  __builtin_amdgcn_s_barrier();
+  read_ks(stage(0), 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  int kt = 0;
+  for (; kt + 2 < KT; ++kt) step(kt, std::true_type{}, std::true_type{});
+  if (kt + 1 < KT) step(kt++, std::false_type{}, std::true_type{});
+  if (kt < KT) step(kt, std::false_type{}, std::false_type{});
 
   // ---- epilogue -----------------------------------------------------------
   // acc[cb][tb][r] = U[m][n] with m = m0 + wm*64 + tb*16 + l16,

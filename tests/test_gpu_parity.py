@@ -547,6 +547,10 @@ def _run_layer(dash, x, dtype=torch.bfloat16, with_score=True):
     # (the 224-wide grid would spill into a second wave of workgroups); the
     # shapes above take the 224-wide ones
     (4096, 32, 8, 128, 4096),
+    # contraction Hq*D of one, two and three 64-wide steps (the GEMM's peeled
+    # last steps with no loop iteration before them), both tile widths
+    (50, 1, 1, 64, 136), (260, 2, 1, 64, 264), (300, 3, 1, 64, 520),
+    (4096, 1, 1, 64, 4096), (4096, 3, 1, 64, 4096),
 ])
 def test_attn_layer_bf16(dash, S, Hq, Hkv, D, hidden):
     x = _layer(S, Hq, Hkv, D, hidden, seed=S)
