@@ -26,7 +26,7 @@ namespace {
 constexpr int kDecStep = kWave;       // keys per wave step (one per lane)
 constexpr int kDecMaxRows = 32;        // g * n_new rows per kv-head
 constexpr int kDecMaxChunks = 1024;    // key chunks per (sample, kv-head), at most
-constexpr int kDecTargetGroups = 512;  // chunk workgroups per launch the split aims at
+constexpr int kDecTargetGroups = 2048;  // chunk workgroups per launch the split aims at
 
 // Wave-wide max / sum in registers: a rotate butterfly inside each 16-lane
 // row (DPP row_ror 8, 4, 2, 1), then the four row results through readlane,
@@ -255,33 +255,36 @@ void decode_chunk_kernel(const uint16_t* __restrict__ Qd, const uint16_t* __rest
   }
 }
 
-// One wave per (sample, token, q-head): merges the chunks.  Lanes load every
-// chunk's (max, sum) in one pass for the overall maximum and sum; the output
-// columns are then summed over the chunks, 32 chunks' loads in flight at a
-// time, with the weights broadcast from LDS (fixed order).
+// One workgroup of kMergeWaves waves per (sample, token, q-head) merges the
+// chunks.  Threads load every chunk's (max, sum) in one pass for the overall
+// maximum and sum (workgroup reductions in a fixed order); wave w then sums the
+// output columns of its contiguous range of chunks, 32 chunks' loads in flight
+// at a time, with the weights from LDS, and the waves' sums are added in wave
+// order: the result does not depend on timing.
+constexpr int kMergeWaves = 8;
+
 template <int D>
-__global__ __launch_bounds__(kWave)
+__global__ __launch_bounds__(kMergeWaves * kWave)
 void decode_merge_kernel(const float* __restrict__ part, int n_new, int Hq, int Hkv, int n_chunks,
                          uint16_t* __restrict__ Od) {
   constexpr int DL = D / kWave;
-  constexpr int kPer = kDecMaxChunks / kWave;  // chunks per lane in the (max, sum) pass
-  constexpr int kBatch = 32;                   // chunks per column batch
+  constexpr int NT = kMergeWaves * kWave;
+  constexpr int kPer = (kDecMaxChunks + NT - 1) / NT;  // chunks per thread in the (max, sum) pass
+  constexpr int kBatch = 32;                           // chunks per column batch
   __shared__ float w_s[kDecMaxChunks];
+  __shared__ float red[2][kMergeWaves];
+  __shared__ float acc_s[kMergeWaves][D];
   const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = Hq / Hkv;
   const int kvh = h / g, r = i * g + (h % g);
   const float* base = part + (static_cast<int64_t>(b) * Hkv + kvh) * n_chunks * kDecMaxRows * (D + 2);
   float mc[kPer], lc[kPer];
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
+    const int c = tid + NT * t;
     mc[t] = -__builtin_inff();
     lc[t] = 0.f;
-  }
-#pragma unroll
-  for (int t = 0; t < kPer; ++t) {
-    if (kWave * t >= n_chunks) break;  // wave-uniform
-    const int c = lane + kWave * t;
     if (c < n_chunks) {
       const float* pc = base + (c * kDecMaxRows + r) * (D + 2);
       mc[t] = pc[0];
@@ -292,41 +295,58 @@ void decode_merge_kernel(const float* __restrict__ part, int n_new, int Hq, int 
 #pragma unroll
   for (int t = 1; t < kPer; ++t) M = fmaxf(M, mc[t]);
   M = wave_max(M);
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, red[0][w]);
   float L = 0.f;
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    const int c = lane + kWave * t;
+    const int c = tid + NT * t;
     const float w = mc[t] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mc[t] - M);
     if (c < n_chunks) w_s[c] = w;
     L += w * lc[t];
   }
   L = wave_sum(L);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane == 0) red[1][wave] = L;
+  __syncthreads();  // weights and per-wave sums visible to every wave
+  L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) L += red[1][w];
+  const int per = (n_chunks + kMergeWaves - 1) / kMergeWaves;
+  const int c_beg = min(n_chunks, wave * per), c_end = min(n_chunks, c_beg + per);
   float acc[DL];
 #pragma unroll
   for (int u = 0; u < DL; ++u) acc[u] = 0.f;
-  for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+  for (int c0 = c_beg; c0 < c_end; c0 += kBatch) {
     float v[kBatch][DL];
 #pragma unroll
     for (int t = 0; t < kBatch; ++t)
 #pragma unroll
       for (int u = 0; u < DL; ++u)
-        v[t][u] = c0 + t < n_chunks ? base[((c0 + t) * kDecMaxRows + r) * (D + 2) + 2 + u * kWave + lane] : 0.f;
+        v[t][u] = c0 + t < c_end ? base[((c0 + t) * kDecMaxRows + r) * (D + 2) + 2 + u * kWave + lane] : 0.f;
 #pragma unroll
     for (int t = 0; t < kBatch; ++t) {
-      const float w = c0 + t < n_chunks ? w_s[c0 + t] : 0.f;
+      const float w = c0 + t < c_end ? w_s[c0 + t] : 0.f;
 #pragma unroll
       for (int u = 0; u < DL; ++u) acc[u] = fmaf(w, v[t][u], acc[u]);
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* o = Od + ((static_cast<int64_t>(b) * n_new + i) * Hq + h) * D;
 #pragma unroll
-  for (int u = 0; u < DL; ++u) {
-    const __bf16 ov = static_cast<__bf16>(acc[u] * inv);
-    o[u * kWave + lane] = __builtin_bit_cast(uint16_t, ov);
+  for (int u = 0; u < DL; ++u) acc_s[wave][u * kWave + lane] = acc[u];
+  __syncthreads();
+  if (wave == 0) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* o = Od + ((static_cast<int64_t>(b) * n_new + i) * Hq + h) * D;
+#pragma unroll
+    for (int u = 0; u < DL; ++u) {
+      float sum = acc_s[0][u * kWave + lane];
+#pragma unroll
+      for (int w = 1; w < kMergeWaves; ++w) sum += acc_s[w][u * kWave + lane];
+      const __bf16 ov = static_cast<__bf16>(sum * inv);
+      o[u * kWave + lane] = __builtin_bit_cast(uint16_t, ov);
+    }
   }
 }
 
@@ -376,7 +396,7 @@ hipError_t launch_decode(int D, const void* Qd, const void* Kc, const void* Vc, 
       chunk_kernel(decode_chunk_kernel<128, 4>);
     else
       chunk_kernel(decode_chunk_kernel<128, 8>);
-    hipLaunchKernelGGL(decode_merge_kernel<128>, g2, dim3(kWave), 0, stream, part, n_new, Hq, Hkv, n_chunks, o);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, g2, dim3(kMergeWaves * kWave), 0, stream, part, n_new, Hq, Hkv, n_chunks, o);
   } else if (D == 64) {
     if (G <= 8)
       chunk_kernel(decode_chunk_kernel<64, 2>);
@@ -384,7 +404,7 @@ hipError_t launch_decode(int D, const void* Qd, const void* Kc, const void* Vc, 
       chunk_kernel(decode_chunk_kernel<64, 4>);
     else
       chunk_kernel(decode_chunk_kernel<64, 8>);
-    hipLaunchKernelGGL(decode_merge_kernel<64>, g2, dim3(kWave), 0, stream, part, n_new, Hq, Hkv, n_chunks, o);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, g2, dim3(kMergeWaves * kWave), 0, stream, part, n_new, Hq, Hkv, n_chunks, o);
   } else {
     return hipErrorInvalidValue;
   }

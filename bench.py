@@ -322,7 +322,7 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, lognormal V row scales, N(0,1/hidden) W_o; no trained weights)",
         "config": {"workload": describe(w, step), "global_batch": 1, "seq_len": S, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if bf16 else "alu",
-                     "kernel": f"attn_fwd_{'bf16' if bf16 else 'f32'}_kernel<{D}>",
+                     "kernel": f"attn_fwd_{'bf16_pp' if bf16 else 'f32'}_kernel<{D}>",
                      "achieved": attn_tflops, "peak": peak, "unit": "TFLOP/s",
                      "frac": attn_tflops / peak, "traffic": traffic,
                      "launches": attn_launches, "avg_launch_ms": attn_ms_total / max(1, attn_launches),
