@@ -5,15 +5,11 @@
 //
 // Flash-decoding split over the keys: one wave owns a chunk of the cache of
 // one (sample, kv-head) and handles all g q-heads x n_new new tokens of that
-// kv-head (the rows of the group) against it, one key per lane: a lane reads
-// its key row with 16-byte loads and forms the rows' scores against queries
-// broadcast from LDS; the softmax maximum and sum of each row are wave
-// reductions; for P V each lane owns D/64 output columns, reads its columns
-// of the value rows (coalesced) and takes P from a wave-private LDS table.
-// The wave keeps fp32 partials (row maximum, sum of exponentials,
-// unnormalised output) in the workspace, and a second kernel merges the
-// chunks in a fixed order.  The work per byte of cache is tiny (VALU); what
-// matters is that many waves stream the cache at once with no serial step.
+// kv-head (the rows of the group, up to 32) against it on the matrix cores
+// (see decode_mfma_kernel).  The wave keeps fp32 partials (row maximum, sum of
+// exponentials, unnormalised output) in the workspace, and a second kernel
+// merges the chunks in a fixed order.  What matters is that many waves stream
+// the cache at once: the arithmetic per byte of cache is small.
 #include <algorithm>
 
 #include "dash_common.h"
@@ -23,10 +19,10 @@ namespace dash {
 
 namespace {
 
-constexpr int kDecStep = kWave;       // keys per wave step (one per lane)
+constexpr int kDecStep = 64;          // keys per chunk step (two 32-key sub-steps)
 constexpr int kDecMaxRows = 32;        // g * n_new rows per kv-head
 constexpr int kDecMaxChunks = 1024;    // key chunks per (sample, kv-head), at most
-constexpr int kDecTargetGroups = 2048;  // chunk workgroups per launch the split aims at
+constexpr int kDecTargetGroups = 1024;  // chunk workgroups per launch the split aims at
 
 // Wave-wide max / sum in registers: a rotate butterfly inside each 16-lane
 // row (DPP row_ror 8, 4, 2, 1), then the four row results through readlane,
@@ -56,201 +52,179 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
-constexpr int kDecWaves = 4;  // waves per chunk: each takes a quarter of the rows
+// ---------------------------------------------------------------------------
+// Chunk kernel: one wave per chunk holds all g * n_new rows of its (sample,
+// kv-head) (up to 32, one per lane pair) and runs each 32-key sub-step as two
+// small products on v_mfma_f32_32x32x16_bf16:
+//   S^T = K Q^T (keys x rows; K read straight from memory in operand layout,
+//   Q pre-scaled into exp2 units once), the online softmax per row (a lane
+//   and its partner 32 lanes away hold one row), P rounded to bf16 in the
+//   accumulator's key order, and O^T += V^T P^T with V staged in LDS (rows
+//   XOR-swizzled by 16-byte chunk) and read transposed (ds_read_b64_tr_b16)
+//   in the key order P arrives in.  Rows past g * n_new compute on zero
+//   queries and are not written.  The partials have the layout the merge
+//   kernel reads.
+// ---------------------------------------------------------------------------
+typedef short dec_i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t dec_u32x2 __attribute__((ext_vector_type(2)));
 
-// A workgroup of kDecWaves waves owns one chunk; wave w handles rows
-// w * RPW .. w * RPW + RPW - 1 (rows past g * n_new carry zero queries and are
-// not written).  Chunk c covers keys [c * steps * 64, (c + 1) * steps * 64).
-// Every global load of a step is issued before the first use: the query rows
-// (16-byte loads), this lane's key row (each wave reads it; the copies after
-// the first come from L2) and a quarter of the step's value rows per wave
-// (16-byte loads, parked in LDS for all waves as soon as they arrive).
-template <int D, int RPW>
-__global__ __launch_bounds__(kDecWaves * kWave)
-void decode_chunk_kernel(const uint16_t* __restrict__ Qd, const uint16_t* __restrict__ Kc,
-                         const uint16_t* __restrict__ Vc, const int32_t* __restrict__ n_kv_dev, int S_cap,
-                         int n_new, int Hq, int Hkv, float c_log2, int steps, int n_chunks,
-                         float* __restrict__ part) {
-  constexpr int DL = D / kWave;                                    // output columns per lane
-  constexpr int kQLoads = (RPW * D / 8 + kWave - 1) / kWave;       // 16-byte query loads per lane
-  constexpr int kVLoads = kDecStep * D / 8 / (kDecWaves * kWave);  // 16-byte value loads per thread and step
-  __shared__ __attribute__((aligned(16))) float q_s[kDecWaves][RPW][D];
-  __shared__ __attribute__((aligned(16))) float p_s[kDecWaves][kDecStep][RPW < 4 ? 4 : RPW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_s[kDecStep][D];
-  constexpr int kPS = RPW < 4 ? 4 : RPW;  // p_s row length (float4 writes)
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__device__ __forceinline__ dec_i16x4 dec_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) dec_i16x4*)(p));
+}
+
+// Slot of 16-byte chunk c of V row r in LDS: the four rows x 64 bytes one
+// transposing read fetches for 32 lanes land in distinct banks.
+template <int D>
+__device__ __forceinline__ int dec_v_slot(int r, int c) {
+  constexpr int kRowBytes = D * 2, kChunks = kRowBytes / 16, kRowsPerLine = 256 / kRowBytes;
+  return c ^ (4 * ((r / kRowsPerLine) % (kChunks / 4)));
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave, 2)  // at least two waves per SIMD
+void decode_mfma_kernel(const uint16_t* __restrict__ Qd, const uint16_t* __restrict__ Kc,
+                        const uint16_t* __restrict__ Vc, const int32_t* __restrict__ n_kv_dev, int S_cap,
+                        int n_new, int Hq, int Hkv, float c_log2, int steps, int n_chunks,
+                        float* __restrict__ part) {
+  constexpr int kRowBytes = D * 2;
+  constexpr int kChunks = kRowBytes / 16;                 // 16-byte chunks per key row
+  constexpr int kSub = 32;                                // keys per sub-step (one MFMA key block)
+  constexpr int kVLoads = kSub * kChunks / kWave;         // 16-byte V loads per lane and sub-step
+  __shared__ __attribute__((aligned(16))) unsigned char vt[kSub * kRowBytes];
+  const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int g = Hq / Hkv;
   const int G = g * n_new;  // row r = token (r / g), q-head kvh * g + r % g
-  const int r0 = wave * RPW;
   const int kv_ld = Hkv * D;
   const uint16_t* Kb = Kc + static_cast<int64_t>(b) * S_cap * kv_ld + static_cast<int64_t>(kvh) * D;
   const uint16_t* Vb = Vc + static_cast<int64_t>(b) * S_cap * kv_ld + static_cast<int64_t>(kvh) * D;
-  // The key and value loads are bounded by the capacity S_cap (rows past the
-  // sample's count are allocated), so they need not wait for the count; rows
-  // at or past n_kv are masked once it has arrived.
-  const int n_kv_raw = n_kv_dev[b];
+  const int n_kv = max(0, min(n_kv_dev[b], S_cap));
+  const int row = l32;
+  // keys t <= lim are visible to this lane's row (its own token and the cache before it)
+  const int lim = min(n_kv - n_new + row / g, n_kv - 1);
 
-  // this wave's query rows, pre-scaled into exp2 units (rows past G are zero)
+  // B operand of S^T = K Q^T: this lane's row, d = 16 ks + 8 hi .. +7, times log2(e)/sqrt(D)
+  bf16x8 qreg[D / 16];
   {
-    u32x4 qq[kQLoads];
+    u32x4 raw[D / 16];
+    const int tok = row / g, jh = row % g;
+    const uint16_t* qp = Qd + ((static_cast<int64_t>(b) * n_new + (row < G ? tok : 0)) * Hq + kvh * g + jh) * D + hi * 8;
 #pragma unroll
-    for (int i = 0; i < kQLoads; ++i) {
-      const int e = lane + kWave * i;
-      const int rr = e / (D / 8), d0 = (e % (D / 8)) * 8;
-      const int r = r0 + rr;
-      qq[i] = u32x4{0u, 0u, 0u, 0u};
-      if (rr < RPW && r < G) {
-        const int tok = r / g, jh = r % g;
-        qq[i] = *reinterpret_cast<const u32x4*>(Qd + ((static_cast<int64_t>(b) * n_new + tok) * Hq + kvh * g + jh) * D + d0);
+    for (int ks = 0; ks < D / 16; ++ks) raw[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float lo = row < G ? __uint_as_float(raw[ks][w] << 16) * c_log2 : 0.f;
+        const float up = row < G ? __uint_as_float(raw[ks][w] & 0xffff0000u) * c_log2 : 0.f;
+        qreg[ks][2 * w] = static_cast<__bf16>(lo);
+        qreg[ks][2 * w + 1] = static_cast<__bf16>(up);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < kQLoads; ++i) {
-      const int e = lane + kWave * i;
-      const int rr = e / (D / 8), d0 = (e % (D / 8)) * 8;
-      if (rr < RPW) {
-        float4 lo, hi;
-        lo.x = __uint_as_float(qq[i][0] << 16) * c_log2;
-        lo.y = __uint_as_float(qq[i][0] & 0xffff0000u) * c_log2;
-        lo.z = __uint_as_float(qq[i][1] << 16) * c_log2;
-        lo.w = __uint_as_float(qq[i][1] & 0xffff0000u) * c_log2;
-        hi.x = __uint_as_float(qq[i][2] << 16) * c_log2;
-        hi.y = __uint_as_float(qq[i][2] & 0xffff0000u) * c_log2;
-        hi.z = __uint_as_float(qq[i][3] << 16) * c_log2;
-        hi.w = __uint_as_float(qq[i][3] & 0xffff0000u) * c_log2;
-        *reinterpret_cast<float4*>(&q_s[wave][rr][d0]) = lo;
-        *reinterpret_cast<float4*>(&q_s[wave][rr][d0 + 4]) = hi;
-      }
-    }
   }
-  float m_run[RPW], l_run[RPW], acc[RPW][DL];
+  // transposed V operand offsets (lane-dependent part), as P's key order requires
+  const int tj = lane & 15, tgrp = (lane >> 4) & 1;
+  int voffs[D / 32];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    m_run[r] = -__builtin_inff();
-    l_run[r] = 0.f;
-#pragma unroll
-    for (int e = 0; e < DL; ++e) acc[r][e] = 0.f;
+  for (int db = 0; db < D / 32; ++db) {
+    const int vr = (tj >> 2) + 4 * hi;
+    const int e = db * 32 + 16 * tgrp + 4 * (tj & 3);
+    voffs[db] = vr * kRowBytes + 16 * dec_v_slot<D>(vr, e >> 3) + 2 * (e & 7);
   }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  float m_run = -__builtin_inff(), l_run = 0.f;  // l_run: this half-wave's keys
 #pragma unroll 1
-  for (int st = 0; st < steps; ++st) {
-    const int t0 = (c * steps + st) * kDecStep;
-    if (t0 >= S_cap) break;  // the same for every wave of the workgroup
-    const int t = t0 + lane;
-    u32x4 kq[D / 8];
-    const uint16_t* kr = Kb + static_cast<int64_t>(t < S_cap ? t : 0) * kv_ld;
-#pragma unroll
-    for (int dc = 0; dc < D / 8; ++dc) kq[dc] = *reinterpret_cast<const u32x4*>(kr + dc * 8);
+  for (int sst = 0; sst < 2 * steps; ++sst) {
+    const int t0 = c * steps * kDecStep + sst * kSub;
+    if (t0 >= S_cap) break;
+    // every load of the sub-step issued before the first use (addresses
+    // clamped into the cache; rows at or past n_kv are masked or zeroed below)
+    bf16x8 kop[D / 16];
     {
-      u32x4 vq[kVLoads];
+      const int t = min(t0 + l32, S_cap - 1);
 #pragma unroll
-      for (int i = 0; i < kVLoads; ++i) {
-        const int e = tid + kDecWaves * kWave * i;
-        const int j = e / (D / 8), d0 = (e % (D / 8)) * 8;
-        vq[i] = u32x4{0u, 0u, 0u, 0u};
-        if (t0 + j < S_cap) vq[i] = *reinterpret_cast<const u32x4*>(Vb + static_cast<int64_t>(t0 + j) * kv_ld + d0);
-      }
-      const int n_kv = max(0, min(n_kv_raw, S_cap));
+      for (int ks = 0; ks < D / 16; ++ks)
+        kop[ks] = *reinterpret_cast<const bf16x8*>(Kb + static_cast<int64_t>(t) * kv_ld + ks * 16 + hi * 8);
+    }
+    u32x4 vq[kVLoads];
 #pragma unroll
-      for (int i = 0; i < kVLoads; ++i) {
-        const int j = (tid + kDecWaves * kWave * i) / (D / 8);
-        if (t0 + j >= n_kv) vq[i] = u32x4{0u, 0u, 0u, 0u};  // unused rows may hold anything
-      }
-      __syncthreads();  // every wave is done with the previous step's value rows
+    for (int i = 0; i < kVLoads; ++i) {
+      const int e = lane + kWave * i;
+      const int t = min(t0 + e / kChunks, S_cap - 1);
+      vq[i] = *reinterpret_cast<const u32x4*>(Vb + static_cast<int64_t>(t) * kv_ld + (e % kChunks) * 8);
+    }
+    f32x16 s;
 #pragma unroll
-      for (int i = 0; i < kVLoads; ++i) {
-        const int e = tid + kDecWaves * kWave * i;
-        *reinterpret_cast<u32x4*>(&v_s[e / (D / 8)][(e % (D / 8)) * 8]) = vq[i];
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) s = mfma32x32x16(kop[ks], qreg[ks], s);
+    // V rows of the sub-step into LDS (rows past n_kv as zeros: cache rows there may hold anything)
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i) {
+      const int e = lane + kWave * i;
+      const int vr = e / kChunks;
+      const u32x4 v = t0 + vr < n_kv ? vq[i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(vt + vr * kRowBytes + 16 * dec_v_slot<D>(vr, e % kChunks)) = v;
+    }
+    // online softmax of this sub-step's keys, in exp2 units
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = t0 + (r >> 2) * 8 + hi * 4 + (r & 3);
+      s[r] = t <= lim ? s[r] : -__builtin_inff();
+      mx = fmaxf(mx, s[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const bool none = m_new == -__builtin_inff();
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float mref = none ? 0.f : m_new;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    u32x4 pk[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const float p0 = __builtin_amdgcn_exp2f(s[8 * sub + 2 * t2] - mref);
+        const float p1 = __builtin_amdgcn_exp2f(s[8 * sub + 2 * t2 + 1] - mref);
+        ps += p0 + p1;
+        pk[sub][t2] = pack_bf16x2(p0, p1);
       }
     }
-    const int n_kv = max(0, min(n_kv_raw, S_cap));
-    const bool valid = t < n_kv;
-    float sc[RPW];
+    l_run = l_run * alpha + ps;
+    // O^T += V^T P^T (the V writes above precede these reads in the wave's LDS order)
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) sc[r] = 0.f;
-    // (inside a branch: the scheduler then keeps the query reads next to their use)
-    if (valid)
+    for (int stp = 0; stp < 2; ++stp)
 #pragma unroll
-      for (int dc = 0; dc < D / 8; ++dc) {
-        float kf[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          kf[2 * w] = __uint_as_float(kq[dc][w] << 16);
-          kf[2 * w + 1] = __uint_as_float(kq[dc][w] & 0xffff0000u);
-        }
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const float4 qa = *reinterpret_cast<const float4*>(&q_s[wave][r][dc * 8]);
-          const float4 qb = *reinterpret_cast<const float4*>(&q_s[wave][r][dc * 8 + 4]);
-          float a = sc[r];
-          a = fmaf(qa.x, kf[0], a);
-          a = fmaf(qa.y, kf[1], a);
-          a = fmaf(qa.z, kf[2], a);
-          a = fmaf(qa.w, kf[3], a);
-          a = fmaf(qb.x, kf[4], a);
-          a = fmaf(qb.y, kf[5], a);
-          a = fmaf(qb.z, kf[6], a);
-          a = fmaf(qb.w, kf[7], a);
-          sc[r] = a;
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        const dec_i16x4 lo = dec_read_tr16(vt + voffs[db] + (16 * stp) * kRowBytes);
+        const dec_i16x4 up = dec_read_tr16(vt + voffs[db] + (16 * stp + 8) * kRowBytes);
+        const u32x4 av = u32x4{__builtin_bit_cast(dec_u32x2, lo)[0], __builtin_bit_cast(dec_u32x2, lo)[1],
+                               __builtin_bit_cast(dec_u32x2, up)[0], __builtin_bit_cast(dec_u32x2, up)[1]};
+        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pk[stp]), o[db]);
       }
-    // softmax of this step's keys, folded into the running row state
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      // key t is visible to row r iff t <= n_kv - n_new + r / g (its own token and the cache before it)
-      const bool vis = valid && t <= n_kv - n_new + (r0 + r) / g;
-      const float sr = vis ? sc[r] : -__builtin_inff();
-      const float m_new = fmaxf(m_run[r], wave_max(sr));
-      const bool none = m_new == -__builtin_inff();
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
-      const float pr = none ? 0.f : __builtin_amdgcn_exp2f(sr - m_new);
-      l_run[r] = l_run[r] * alpha + wave_sum(pr);
-      m_run[r] = m_new;
-#pragma unroll
-      for (int e = 0; e < DL; ++e) acc[r][e] *= alpha;
-      sc[r] = pr;
-    }
-#pragma unroll
-    for (int r = 0; r < kPS; r += 4)
-      *reinterpret_cast<float4*>(&p_s[wave][lane][r]) = {sc[r], r + 1 < RPW ? sc[(r + 1) % RPW] : 0.f,
-                                                          r + 2 < RPW ? sc[(r + 2) % RPW] : 0.f,
-                                                          r + 3 < RPW ? sc[(r + 3) % RPW] : 0.f};
-    __syncthreads();  // value rows from every wave; this wave's P
-    // O += P V: lane owns columns lane*DL .. +DL-1
-#pragma unroll 4
-    for (int j = 0; j < kDecStep; ++j) {
-      float v[DL];
-      if constexpr (DL == 2) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(&v_s[j][lane * 2]);
-        v[0] = __uint_as_float(w << 16);
-        v[DL - 1] = __uint_as_float(w & 0xffff0000u);
-      } else {
-        v[0] = bf16_to_f32(v_s[j][lane]);
-      }
-#pragma unroll
-      for (int r = 0; r < kPS; r += 4) {
-        const float4 pj = *reinterpret_cast<const float4*>(&p_s[wave][j][r]);
-        const float pv[4] = {pj.x, pj.y, pj.z, pj.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (r + q < RPW)
-#pragma unroll
-            for (int e = 0; e < DL; ++e) acc[(r + q) % RPW][e] = fmaf(pv[q], v[e], acc[(r + q) % RPW][e]);
-      }
-    }
   }
-  // partial of this chunk: [b][kvh][c][r] -> (m, l, o[D])
-  float* out = part + ((static_cast<int64_t>(b) * Hkv + kvh) * n_chunks + c) * kDecMaxRows * (D + 2);
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  // partial of this chunk: [b][kvh][c][r] -> (m, l, o[D]); o^T element (d, row) with
+  // d = 32 db + 8 (r / 4) + 4 hi + r % 4
+  if (row < G) {
+    float* out = part + (((static_cast<int64_t>(b) * Hkv + kvh) * n_chunks + c) * kDecMaxRows + row) * (D + 2);
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int r = r0 + rr;
-    if (r < G) {
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int e = 0; e < DL; ++e) out[r * (D + 2) + 2 + lane * DL + e] = acc[rr][e];
-      if (lane == 0) {
-        out[r * (D + 2)] = m_run[rr];
-        out[r * (D + 2) + 1] = l_run[rr];
-      }
+      for (int r = 0; r < 16; ++r) out[2 + db * 32 + (r >> 2) * 8 + hi * 4 + (r & 3)] = o[db][r];
+    if (hi == 0) {
+      out[0] = m_run;
+      out[1] = l_tot;
     }
   }
 }
@@ -386,25 +360,17 @@ hipError_t launch_decode(int D, const void* Qd, const void* Kc, const void* Vc, 
   auto v = static_cast<const uint16_t*>(Vc);
   auto o = static_cast<uint16_t*>(Od);
   auto chunk_kernel = [&](auto kern) {
-    hipLaunchKernelGGL(kern, g1, dim3(kDecWaves * kWave), 0, stream, q, k, v, n_kv, S_cap, n_new, Hq, Hkv, c, steps,
-                       n_chunks, part);
+    hipLaunchKernelGGL(kern, g1, dim3(kWave), 0, stream, q, k, v, n_kv, S_cap, n_new, Hq, Hkv, c, steps, n_chunks,
+                       part);
   };
   if (D == 128) {
-    if (G <= 8)
-      chunk_kernel(decode_chunk_kernel<128, 2>);
-    else if (G <= 16)
-      chunk_kernel(decode_chunk_kernel<128, 4>);
-    else
-      chunk_kernel(decode_chunk_kernel<128, 8>);
-    hipLaunchKernelGGL(decode_merge_kernel<128>, g2, dim3(kMergeWaves * kWave), 0, stream, part, n_new, Hq, Hkv, n_chunks, o);
+    chunk_kernel(decode_mfma_kernel<128>);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, g2, dim3(kMergeWaves * kWave), 0, stream, part, n_new, Hq, Hkv,
+                       n_chunks, o);
   } else if (D == 64) {
-    if (G <= 8)
-      chunk_kernel(decode_chunk_kernel<64, 2>);
-    else if (G <= 16)
-      chunk_kernel(decode_chunk_kernel<64, 4>);
-    else
-      chunk_kernel(decode_chunk_kernel<64, 8>);
-    hipLaunchKernelGGL(decode_merge_kernel<64>, g2, dim3(kMergeWaves * kWave), 0, stream, part, n_new, Hq, Hkv, n_chunks, o);
+    chunk_kernel(decode_mfma_kernel<64>);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, g2, dim3(kMergeWaves * kWave), 0, stream, part, n_new, Hq, Hkv,
+                       n_chunks, o);
   } else {
     return hipErrorInvalidValue;
   }
