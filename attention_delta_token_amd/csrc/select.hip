@@ -565,7 +565,7 @@ namespace {
 // Full: the row fills all J chunks (n == 256 * J), so no position tests.
 // Rows are n % 4 == 0 scores, 16-byte aligned.
 // ---------------------------------------------------------------------------
-constexpr int kWaveRowsPerBlock = 4;
+constexpr int kWaveRowsPerBlock = 1;  // one row per workgroup: a slow row holds up no other row's slot
 
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
@@ -1184,7 +1184,9 @@ hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_firs
     else                                                                                                   \
       hipLaunchKernelGGL((topk_wave_kernel<J_, false>), grid, block, 0, stream, score, rows, n, k, idx, nan_out); \
   } while (0)
-    if (n <= 2048)
+    if (n <= 1024)
+      DASH_WAVE_TOPK(4);
+    else if (n <= 2048)
       DASH_WAVE_TOPK(8);
     else if (n <= 4096)
       DASH_WAVE_TOPK(16);
