@@ -467,6 +467,125 @@ void topk_reg_kernel(const float* __restrict__ score, int n_row, int k_total, in
   if (nan_out) write_block_total<NT>(nan, sh_scan, nan_out + blockIdx.x);
 }
 
+// Batched rows of up to 64 keys per thread (NT threads, C chunks), plain rows
+// only (no forced ends, position map or device count; n % 4 == 0, 16-byte
+// aligned): chunk c of a row is positions 4 (c NT + t) + q, so every load of
+// a chunk is one coalesced 16-byte load per thread and the whole row sits in
+// registers for the radix passes.  The emit counts, per chunk and thread, the
+// keys above the cut and equal to it; a workgroup scan of those counts per
+// chunk (wave scans, then the waves' totals in wave order inside a chunk and
+// the chunks' totals in chunk order) gives every kept key its output slot in
+// ascending position order, ties to the lower position.
+template <int NT, int C>
+__global__ __launch_bounds__(NT, 1)
+void topk_strided_kernel(const float* __restrict__ score, int n, int k, int32_t* __restrict__ idx,
+                         int32_t* __restrict__ nan_out) {
+  constexpr int kW = NT / kWave;
+  static_assert(C <= kWave, "one lane per chunk in the base scan");
+  __shared__ uint32_t hist[kCopies * kBins];
+  __shared__ uint64_t sh_scan[2 * kW + 8];
+  __shared__ uint32_t sh_cut[2];
+  __shared__ uint32_t sh_tot[kW][C];    // per wave and chunk: (greater << 16) | equal
+  __shared__ uint32_t sh_wbase[kW][C];  // the same, summed over the lower waves of the chunk
+  __shared__ uint32_t sh_cbase[2][C];   // greater / equal keys in all lower chunks
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const u32x4* r4 = reinterpret_cast<const u32x4*>(score + static_cast<size_t>(blockIdx.x) * n);
+  int32_t* out = idx + static_cast<size_t>(blockIdx.x) * k;
+  const int n4 = n >> 2;
+  uint32_t keys[C][4];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {  // unconditional loads, all in flight before the first use
+    const u32x4 v = __builtin_nontemporal_load(r4 + min(c * NT + t, n4 - 1));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) keys[c][q] = v[q];
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) keys[c][q] = score_key(__uint_as_float(keys[c][q]));
+  const int vld_n = n4 - t;  // chunk c of this thread exists iff c NT < vld_n
+  uint32_t nan = 0u;
+  if (nan_out) {
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) nan += (c * NT < vld_n && keys[c][q] == 0u) ? 1u : 0u;
+  }
+  if (k > 0) {
+    auto for_keys = [&](auto&& fn) {
+      int vld = vld_n;  // opaque at every call: the chunk tests stay next to their use
+      asm volatile("" : "+v"(vld));
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (c * NT < vld)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) fn(keys[c][q]);
+    };
+    uint32_t take_eq;
+    const uint32_t cut = radix_cut<NT, true>(for_keys, static_cast<uint32_t>(k), hist, sh_scan, sh_cut, &take_eq);
+    auto counts = [&](int c) {  // (greater << 16) | equal over this thread's four keys of chunk c
+      uint32_t gt = 0u, eq = 0u;
+      if (c * NT < vld_n) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gt += keys[c][q] > cut ? 1u : 0u;
+          eq += keys[c][q] == cut ? 1u : 0u;
+        }
+      }
+      return (gt << 16) | eq;
+    };
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const uint32_t incl = wave_incl_scan32(counts(c));  // fields stay below 2^16 (256 per wave)
+      if (lane == kWave - 1) sh_tot[wave][c] = incl;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t gt = 0u, eq = 0u;  // lane c: chunk c, its waves in order
+      if (lane < C) {
+        uint32_t run = 0u;
+        for (int w = 0; w < kW; ++w) {
+          sh_wbase[w][lane] = run;
+          run += sh_tot[w][lane];  // per chunk at most NT * 4 = 4096 per field
+        }
+        gt = run >> 16;
+        eq = run & 0xffffu;
+      }
+      const uint32_t gi = wave_incl_scan32(gt), ei = wave_incl_scan32(eq);
+      if (lane < C) {
+        sh_cbase[0][lane] = gi - gt;
+        sh_cbase[1][lane] = ei - eq;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const uint32_t mine = counts(c);
+      const uint32_t excl = wave_incl_scan32(mine) - mine + sh_wbase[wave][c];
+      uint32_t gt_before = sh_cbase[0][c] + (excl >> 16);
+      uint32_t eq_before = sh_cbase[1][c] + (excl & 0xffffu);
+      if (c * NT < vld_n) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int32_t p = 4 * (c * NT + t) + q;
+          if (keys[c][q] > cut) {
+            const uint32_t o = gt_before + min(eq_before, take_eq);
+            if (o < static_cast<uint32_t>(k)) out[o] = p;
+            ++gt_before;
+          } else if (keys[c][q] == cut) {
+            if (eq_before < take_eq) {
+              const uint32_t o = gt_before + eq_before;
+              if (o < static_cast<uint32_t>(k)) out[o] = p;
+            }
+            ++eq_before;
+          }
+        }
+      }
+    }
+  }
+  if (nan_out) write_block_total<NT>(nan, sh_scan, nan_out + blockIdx.x);
+}
+
 __global__ __launch_bounds__(kSelThreads, 1)
 void order_stat_kernel(const float* __restrict__ score, const int32_t* __restrict__ n_dev, int n_max,
                        int rank, float* __restrict__ tau_out, int32_t* __restrict__ nan_out) {
@@ -1193,6 +1312,10 @@ hipError_t launch_topk(const float* score, int rows, int n, int k, int keep_firs
     else
       DASH_WAVE_TOPK(32);
 #undef DASH_WAVE_TOPK
+  } else if (rows >= 2 && !pos && !n_dev && !n_out && keep_first == 0 && keep_last == 0 && n % 4 == 0 &&
+             n > kSelThreads * 32 && n <= kSelThreads * 64 && (reinterpret_cast<uintptr_t>(score) & 15u) == 0) {
+    hipLaunchKernelGGL((topk_strided_kernel<kSelThreads, 16>), dim3(rows), dim3(kSelThreads), 0, stream, score, n, k,
+                       idx, nan_out);
   } else {
     launch_topk_nt<kSelThreads>(score, rows, n, k, keep_first, keep_last, pos, idx, nullptr, nullptr, n_dev, n_out,
                                 nan_out, stream);

@@ -186,6 +186,27 @@ def test_topk_wave_rows_all_kinds(dash, kind, n):
             np.testing.assert_array_equal(got[r], oracle.select_topk(s[r], k))
 
 
+@pytest.mark.parametrize("n", [65536, 40004, 32772])
+@pytest.mark.parametrize("kind", SCORE_KINDS)
+def test_topk_strided_rows_all_kinds(dash, kind, n):
+    """Batches of rows wider than 32768 scores (plain rows, n % 4 == 0) take the
+    register-resident workgroup kernel with strided key ownership: every score
+    family, k from 1 to n, NaN counts per row."""
+    rows = 3
+    s = np.stack([score_vector(kind, n, seed=7000 * r + n) for r in range(rows)])
+    sd = torch.from_numpy(s).cuda()
+    for k in (1, n // 3, n // 2 + 1, n - 1, n):
+        say("topk strided rows", kind, n, k)
+        idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+        st = dash.select_status(rows)
+        dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows, status=st)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        np.testing.assert_array_equal(st.cpu().numpy()[:rows], np.isnan(s).sum(axis=1))
+        for r in range(rows):
+            np.testing.assert_array_equal(got[r], oracle.select_topk(s[r], k))
+
+
 @pytest.mark.parametrize("rows,n,k", [(48, 3000, 1234), (80, 3000, 1234), (70, 8192, 4096), (64, 8193, 100),
                                       (66, 1, 1), (65, 40000, 39999),
                                       (256, 8192, 4096), (300, 2048, 1000), (257, 4, 2), (512, 4100, 1),
