@@ -1046,11 +1046,20 @@ void topk_multi_scan(int G, MultiWs w) {
   const uint32_t dm = (1u << wd) - 1u;
   const int nb = static_cast<int>(dm) + 1;
   const int b0 = 2 * static_cast<int>(threadIdx.x);
+  // this thread's two bins summed over the slices, 16 slices' loads in flight
+  // at a time (addresses clamped into the slices that exist)
   uint32_t c0 = 0u, c1 = 0u;
-  for (int g = 0; g < G; ++g) {
-    const uint32_t* gh = w.hist + static_cast<size_t>(g) * kBins;
-    c0 += gh[b0];
-    c1 += gh[b0 + 1];
+  constexpr int kBatch = 16;
+  for (int g0 = 0; g0 < G; g0 += kBatch) {
+    u32x2 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      v[i] = *reinterpret_cast<const u32x2*>(w.hist + static_cast<size_t>(min(g0 + i, G - 1)) * kBins + b0);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      c0 += g0 + i < G ? v[i][0] : 0u;
+      c1 += g0 + i < G ? v[i][1] : 0u;
+    }
   }
   uint64_t tot;
   const uint32_t below = static_cast<uint32_t>(block_excl_scan<kScanT>(c0 + c1, sh_scan, tot));
