@@ -265,6 +265,17 @@ void decode_merge_kernel(const float* __restrict__ part, int n_new, int Hq, int 
       lc[t] = pc[1];
     }
   }
+  // This wave's contiguous run of chunks; the output columns of its first
+  // kBatch chunks are loaded together with the (max, sum) pass (chunk indices
+  // clamped into the existing chunks, their weights zeroed below).
+  const int per = (n_chunks + kMergeWaves - 1) / kMergeWaves;
+  const int c_beg = min(n_chunks, wave * per), c_end = min(n_chunks, c_beg + per);
+  float v0[kBatch][DL];
+#pragma unroll
+  for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+    for (int u = 0; u < DL; ++u)
+      v0[t][u] = base[(min(c_beg + t, n_chunks - 1) * kDecMaxRows + r) * (D + 2) + 2 + u * kWave + lane];
   float M = mc[0];
 #pragma unroll
   for (int t = 1; t < kPer; ++t) M = fmaxf(M, mc[t]);
@@ -288,12 +299,16 @@ void decode_merge_kernel(const float* __restrict__ part, int n_new, int Hq, int 
   L = 0.f;
 #pragma unroll
   for (int w = 0; w < kMergeWaves; ++w) L += red[1][w];
-  const int per = (n_chunks + kMergeWaves - 1) / kMergeWaves;
-  const int c_beg = min(n_chunks, wave * per), c_end = min(n_chunks, c_beg + per);
   float acc[DL];
 #pragma unroll
   for (int u = 0; u < DL; ++u) acc[u] = 0.f;
-  for (int c0 = c_beg; c0 < c_end; c0 += kBatch) {
+#pragma unroll
+  for (int t = 0; t < kBatch; ++t) {
+    const float w = c_beg + t < c_end ? w_s[c_beg + t] : 0.f;
+#pragma unroll
+    for (int u = 0; u < DL; ++u) acc[u] = fmaf(w, v0[t][u], acc[u]);
+  }
+  for (int c0 = c_beg + kBatch; c0 < c_end; c0 += kBatch) {
     float v[kBatch][DL];
 #pragma unroll
     for (int t = 0; t < kBatch; ++t)
