@@ -572,6 +572,8 @@ def _run_layer(dash, x, dtype=torch.bfloat16, with_score=True):
     # last steps with no loop iteration before them), both tile widths
     (50, 1, 1, 64, 136), (260, 2, 1, 64, 264), (300, 3, 1, 64, 520),
     (4096, 1, 1, 64, 4096), (4096, 3, 1, 64, 4096),
+    # 256-wide tiles with a partial last row tile (4000 = 15 * 256 + 160)
+    (4000, 4, 1, 64, 4096),
 ])
 def test_attn_layer_bf16(dash, S, Hq, Hkv, D, hidden):
     x = _layer(S, Hq, Hkv, D, hidden, seed=S)
@@ -962,6 +964,34 @@ def test_decode_vs_oracle(dash, S, n_new, mode, Hq, Hkv, D):
     for b in range(B):
         ref = oracle.decode_step(new[b]["Q"], new[b]["K"], new[b]["V"], pre[b]["K"], pre[b]["V"], idx[b], mode)
         assert maxrel(host(Od)[b], ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_decode_ignores_rows_past_the_count(dash, D):
+    """Cache rows at or past a sample's count may hold anything (here NaN and
+    infinities in K and V): the output equals the one over a clean cache."""
+    B, S, n_new, Hq, Hkv = 2, 3000, 2, 14, 2
+    w = WORKLOADS[1].scaled(S=S, Hq=Hq, Hkv=Hkv, D=D, hidden=Hq * D)
+    x = [layer_inputs(w, 90 + b, 0) for b in range(B)]
+    n_kv = [1700, 2333]
+    Kc = np.zeros((B, S, Hkv, D), np.float32)
+    Vc = np.zeros((B, S, Hkv, D), np.float32)
+    for b in range(B):
+        Kc[b, :n_kv[b]], Vc[b, :n_kv[b]] = x[b]["K"][:n_kv[b]], x[b]["V"][:n_kv[b]]
+    Qd = dev_t(np.stack([x[b]["Q"][n_kv[b] - n_new:n_kv[b]] for b in range(B)]))
+    nk = torch.tensor(n_kv, dtype=torch.int32, device="cuda")
+    say("decode rows past the count", D)
+    clean = torch.zeros(B, n_new, Hq * D, device="cuda", dtype=torch.bfloat16)
+    dash.dash_decode(Qd, dev_t(Kc), dev_t(Vc), nk, clean)
+    for b in range(B):
+        Kc[b, n_kv[b]:] = np.nan
+        Vc[b, n_kv[b]:] = np.inf
+        Kc[b, n_kv[b]::7] = -np.inf
+    dirty = torch.zeros(B, n_new, Hq * D, device="cuda", dtype=torch.bfloat16)
+    dash.dash_decode(Qd, dev_t(Kc), dev_t(Vc), nk, dirty)
+    torch.cuda.synchronize()
+    assert torch.equal(clean, dirty)
+    assert bool(torch.isfinite(clean.float()).all())
 
 
 def test_decode_graph_replay(dash):
