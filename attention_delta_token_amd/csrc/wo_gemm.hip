@@ -604,14 +604,15 @@ int device_cus() {
 
 // Column tile for the bf16 path: the width whose whole waves of workgroups
 // (one per CU) cost least, a wave of 224-wide tiles counting 224/256 of a
-// wave of 256-wide ones.  (With 256 CUs: 8192 x 3584 takes 224-wide tiles,
-// 4096 x 4096 and 131072 x 3584 take 256-wide ones.)
+// wave of 256-wide ones times 1.06 (the 224-wide kernel's lower MFMA
+// efficiency, measured).  (With 256 CUs: 8192 x 3584 takes 224-wide tiles,
+// 4096 x 4096, 39321 x 3584 and 131072 x 3584 take 256-wide ones.)
 int bf16_tile_n(int M, int N) {
   const long tm = (M + kBM - 1) / kBM;
   const long cus = device_cus();
   const long w256 = (tm * ((N + kBN - 1) / kBN) + cus - 1) / cus;
   const long w224 = (tm * ((N + kBN224 - 1) / kBN224) + cus - 1) / cus;
-  return w224 * kBN224 < w256 * kBN ? kBN224 : kBN;
+  return w224 * kBN224 * 106 < w256 * kBN * 100 ? kBN224 : kBN;
 }
 
 }  // namespace
