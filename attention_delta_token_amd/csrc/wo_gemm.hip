@@ -255,19 +255,22 @@ void wo_gemm_bf16_kernel(const uint16_t* __restrict__ A, const uint16_t* __restr
   float* red = reinterpret_cast<float*>(lds);                // [2 wn][256 m] partial sums
   uint16_t* ct = reinterpret_cast<uint16_t*>(lds + 4096);    // staging [128 m][kLdsC], one half at a time
   constexpr int kLdsC = kBN + 8;
+  if (part) {  // the score's partial sums only when the score is asked for
+    const bool full = n0 + kBN <= N;  // no column of the tile past the matrix edge
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-    float ss = 0.f;
+    for (int mb = 0; mb < kMB; ++mb) {
+      float ss = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
+      for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int nl = wn * 128 + nb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-        const float v = (n0 + nl < N) ? acc[nb][mb][r] : 0.f;
-        ss += v * v;
-      }
-    ss += __shfl_xor(ss, 32, 64);
-    if (hi == 0) red[wn * kBM + wm * 64 + mb * 32 + l32] = ss;
+        for (int r = 0; r < 16; ++r) {
+          const int nl = wn * 128 + nb * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+          const float v = (full || n0 + nl < N) ? acc[nb][mb][r] : 0.f;
+          ss += v * v;
+        }
+      ss += __shfl_xor(ss, 32, 64);
+      if (hi == 0) red[wn * kBM + wm * 64 + mb * 32 + l32] = ss;
+    }
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -450,20 +453,23 @@ void wo_gemm_bf16_n224_kernel(const uint16_t* __restrict__ A, const uint16_t* __
   uint16_t* ct = reinterpret_cast<uint16_t*>(lds + 4096);  // staging [256 m][kLdsC]
   constexpr int kLdsC = kBN224 + 8;
   static_assert(4096 + kBM * kLdsC * 2 <= kStages * kStage224, "staging fits the ring");
+  const bool full = n0 + kBN224 <= N;  // no column of the tile past the matrix edge
 #pragma unroll
   for (int tb = 0; tb < kTB; ++tb) {
-    float ss = 0.f;
+    if (part) {  // the score's partial sums only when the score is asked for
+      float ss = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
+      for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int nl = wn * 112 + cb * 16 + q4 * 4 + r;
-        const float v = (n0 + nl < N) ? acc[cb][tb][r] : 0.f;
-        ss += v * v;
-      }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    if (q4 == 0) red[wn * kBM + wm * 64 + tb * 16 + l16] = ss;
+        for (int r = 0; r < 4; ++r) {
+          const int nl = wn * 112 + cb * 16 + q4 * 4 + r;
+          const float v = (full || n0 + nl < N) ? acc[cb][tb][r] : 0.f;
+          ss += v * v;
+        }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (q4 == 0) red[wn * kBM + wm * 64 + tb * 16 + l16] = ss;
+    }
     const int ml = wm * 64 + tb * 16 + l16;
 #pragma unroll
     for (int cb = 0; cb < kCB; ++cb) {
