@@ -699,13 +699,301 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
+// ---------------------------------------------------------------------------
+// Bracketed one-wave top-k (rows of more than 2048 scores).  The digit passes
+// over every key are most of the one-wave kernel's instructions (a bin
+// address, a prefix test and an LDS atomic per key and pass); here they run
+// over a few hundred keys instead:
+//  1. A fixed sample of 16 keys per lane (chunks spread over the row) is
+//     counted into the histogram of the digit right below the sample's common
+//     key prefix.  The sample ranks r - d and r + d around the cut's expected
+//     rank r = k m / n (m sampled keys, d = three binomial standard deviations
+//     plus two) name two bins whose outer edges bound a score interval
+//     [lo, hi] that holds the cut unless the sample misleads.
+//  2. One compare pass over the row counts the scores above hi and stores the
+//     scores inside [lo, hi] in lane-private LDS slots.
+//  3. If fewer than k scores lie above hi, at least k lie at or above lo and
+//     every candidate found a slot, the cut is the (k - above)-th largest
+//     candidate, found by the usual digit passes over the candidates alone.
+//  4. The emit compares every score of the row with the cut.
+// Every decision is a float compare, which ranks -0 and +0 as equal and NaN
+// below every number, exactly as the keys do.  A row whose bracket misses
+// returns false and takes the digit passes over all its keys: the result is
+// the same either way, only the time differs.
+// ---------------------------------------------------------------------------
+constexpr int kCandRows = 32;  // candidate slots per lane
+
+// Bins holding the keys of ranks R[t] (1-based, counted from the largest) in
+// the wave's histogram of nb bins: bin[t], the rank within that bin
+// (rank_in[t]) and the bin's count (cnt[t]); ok[t] is false when R[t] lies
+// outside 1..total.  tot = number of keys counted.  Two levels: the lane whose
+// 32 bins hold the rank (a scan of the lane totals), then the bin among those
+// 32 (one bin per lane, a second scan).
+template <int NTGT>
+__device__ __forceinline__ void wave_find_bins(const uint32_t* h, const uint32_t (&R)[NTGT], int lane,
+                                               uint32_t& tot, uint32_t (&bin)[NTGT], uint32_t (&rank_in)[NTGT],
+                                               uint32_t (&cnt)[NTGT], bool (&ok)[NTGT]) {
+  constexpr int kBPL = kBins / kWave;
+  const uint32_t b0 = static_cast<uint32_t>(lane) * kBPL;
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int b = 0; b < kBPL; ++b) mine += h[wave_bin_word(b0 + b)];  // unused bins stay zero
+  const uint32_t incl = wave_incl_scan32(mine);
+  tot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+  const uint32_t above_lane = tot - incl;  // keys in the bins of the lanes above
+  uint32_t src[NTGT], rin[NTGT], c[NTGT];
+#pragma unroll
+  for (int t = 0; t < NTGT; ++t) {
+    const uint64_t who = __ballot(above_lane < R[t] && R[t] <= above_lane + mine);
+    ok[t] = who != 0ull;
+    src[t] = ok[t] ? static_cast<uint32_t>(__builtin_ctzll(who)) : 0u;
+    rin[t] = R[t] - static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(above_lane), static_cast<int>(src[t])));
+    c[t] = lane < kBPL ? h[wave_bin_word(src[t] * kBPL + static_cast<uint32_t>(lane))] : 0u;
+  }
+#pragma unroll
+  for (int t = 0; t < NTGT; ++t) {
+    const uint32_t ci = wave_incl_scan32(c[t]);
+    const uint32_t ltot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ci), kBPL - 1));
+    const uint32_t above = ltot - ci;  // keys in this lane's higher bins
+    const uint64_t who = __ballot(lane < kBPL && above < rin[t] && rin[t] <= above + c[t]);
+    const int bl = who != 0ull ? static_cast<int>(__builtin_ctzll(who)) : 0;
+    ok[t] = ok[t] && who != 0ull;
+    bin[t] = src[t] * kBPL + static_cast<uint32_t>(bl);
+    rank_in[t] = rin[t] - static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(above), bl));
+    cnt[t] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c[t]), bl));
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_sum32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan32(v)), kWave - 1));
+}
+
+__device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
+  v = wave_incl_scan_op(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), kWave - 1));
+}
+
+__device__ __forceinline__ uint32_t wave_min32(uint32_t v) {
+  v = wave_incl_scan_op(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); });
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), kWave - 1));
+}
+
+// raw[j][e]: the bits of the score at position 256 j + 4 lane + e.  Returns
+// false (nothing written) when the bracket misses; true once the row's k
+// outputs are written.  Needs 0 < k < n and J >= 16.
 template <int J, bool Full>
-__global__ __launch_bounds__(kWaveRowsPerBlock * kWave)
+__device__ __forceinline__ bool wave_topk_bracket(const uint32_t (&raw)[J][4], int lane, int n, int k,
+                                                  uint32_t* h, uint32_t* cand, int32_t* __restrict__ out) {
+  static_assert(J >= 16 && J % 16 == 0, "the sample takes one key of every J/16-th chunk");
+  const int n4 = n >> 2;
+  auto valid = [&](int j) { return Full || j * kWave + lane < n4; };
+  constexpr int kS = 16;  // sampled keys per lane: key t & 3 of chunk t * J / 16
+
+  // 1. the bracket from the sample
+  uint32_t sk[kS];
+  uint32_t smin = 0xffffffffu, smax = 0u, mine = 0u;
+#pragma unroll
+  for (int t = 0; t < kS; ++t) {
+    sk[t] = score_key(__uint_as_float(raw[t * (J / 16)][t & 3]));
+    if (valid(t * (J / 16))) {
+      smin = min(smin, sk[t]);
+      smax = max(smax, sk[t]);
+      ++mine;
+    }
+  }
+  smin = wave_min32(smin);
+  smax = wave_max32(smax);
+  const uint32_t m = wave_sum32(mine);
+  if (m == 0u) return false;
+  const int common = smin == smax ? 32 : __clz(smin ^ smax);
+  const uint32_t sprefix = smin & static_cast<uint32_t>(0xffffffff00000000ull >> common);
+  const int rem = 32 - common;
+  const int wd = rem < 11 ? rem : 11;
+  const int sh = rem - wd;
+  const uint32_t dm = (1u << wd) - 1u;
+#pragma unroll
+  for (int b = 0; b < kBins / kWave / 4; ++b) reinterpret_cast<u32x4*>(h)[b * kWave + lane] = u32x4{0u, 0u, 0u, 0u};
+  wave_lds_fence();
+#pragma unroll
+  for (int t = 0; t < kS; ++t)
+    atomicAdd(&h[wave_bin_word((sk[t] >> sh) & dm)], valid(t * (J / 16)) ? 1u : 0u);
+  wave_lds_fence();
+  const float p = static_cast<float>(k) / static_cast<float>(n);
+  const float r = p * static_cast<float>(m);
+  const float d = 3.0f * __builtin_sqrtf(static_cast<float>(m) * p * (1.0f - p)) + 2.0f;
+  const float rh = __builtin_floorf(r - d), rl = __builtin_ceilf(r + d);
+  const bool has_hi = rh >= 1.0f, has_lo = rl <= static_cast<float>(m);
+  const uint32_t R[2] = {has_hi ? static_cast<uint32_t>(rh) : 1u, has_lo ? static_cast<uint32_t>(rl) : m};
+  uint32_t stot, sbin[2], srank[2], scnt[2];
+  bool sok[2];
+  wave_find_bins<2>(h, R, lane, stot, sbin, srank, scnt, sok);
+  float hi_f = __builtin_inff(), lo_f = -__builtin_inff();
+  if (has_hi) {
+    const uint32_t hk = sprefix | (sbin[0] << sh) | ((1u << sh) - 1u);  // top key of the bin
+    if (!sok[0] || hk < 0x007fffffu) return false;  // the sample's upper ranks are NaN
+    if (hk < 0xff800000u) hi_f = key_score(hk);
+  }
+  if (has_lo) {
+    const uint32_t lk = sprefix | (sbin[1] << sh);  // bottom key of the bin
+    if (!sok[1]) return false;
+    if (lk > 0x007fffffu) lo_f = key_score(lk);
+  }
+
+  // 2. one compare pass: count above hi, store [lo, hi] in lane-private slots
+  // (lane l's i-th candidate in word i * 64 + l).  Every key is stored at the
+  // lane's next free slot and the slot advances only for candidates, so no
+  // per-key select of the address; a lane whose slots may run out before a
+  // chunk is clamped to the last four rows and flagged, and its row falls back.
+  uint32_t above = 0u;
+  const uint32_t base = static_cast<uint32_t>(lane) * 4u;
+  const uint32_t last = base + static_cast<uint32_t>(kCandRows - 4) * kWave * 4u;
+  uint32_t addr = base;  // byte offset of the next free slot
+  bool ovf = false;
+  char* cb = reinterpret_cast<char*>(cand);
+#pragma unroll
+  for (int jj = 0; jj < J; ++jj) {  // chunk order is free here; even chunks arrived first
+    const int j = jj < J / 2 ? 2 * jj : 2 * (jj - J / 2) + 1;
+    const bool vj = valid(j);
+    ovf = ovf || addr > last;
+    addr = min(addr, last);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = __uint_as_float(raw[j][e]);
+      const bool a = vj && x > hi_f;
+      const bool in = vj && x >= lo_f && !a;
+      above += static_cast<uint32_t>(__popcll(__ballot(a)));
+      *reinterpret_cast<uint32_t*>(cb + addr) = raw[j][e];
+      addr += in ? static_cast<uint32_t>(kWave * 4) : 0u;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // chunk by chunk: no compare results of later chunks held early
+  }
+  const uint32_t cnt = (addr - base) / static_cast<uint32_t>(kWave * 4);
+  const uint32_t cmax = wave_max32(cnt);
+  const uint32_t ctot = wave_sum32(cnt);
+  if (__ballot(ovf) != 0ull || above >= static_cast<uint32_t>(k) || above + ctot < static_cast<uint32_t>(k))
+    return false;
+
+  // 3. the (k - above)-th largest candidate: digit passes below the bits that
+  // every key in [lo, hi] shares
+  wave_lds_fence();
+  uint32_t kk = static_cast<uint32_t>(k) - above;
+  const uint32_t klo = score_key(lo_f), khi = score_key(hi_f);
+  const int common2 = klo == khi ? 32 : __clz(klo ^ khi);
+  uint32_t pmask = static_cast<uint32_t>(0xffffffff00000000ull >> common2);
+  uint32_t prefix = klo & pmask;
+  int sh2 = 32 - common2;
+  bool whole = sh2 == 0 && kk == ctot;
+#pragma unroll 1
+  while (sh2 > 0) {
+    const int wd2 = sh2 < 11 ? sh2 : 11;
+    sh2 -= wd2;
+    const uint32_t dm2 = (1u << wd2) - 1u;
+#pragma unroll
+    for (int b = 0; b < kBins / kWave / 4; ++b) reinterpret_cast<u32x4*>(h)[b * kWave + lane] = u32x4{0u, 0u, 0u, 0u};
+    wave_lds_fence();
+#pragma unroll 4
+    for (uint32_t t = 0; t < cmax; ++t) {
+      const uint32_t key = score_key(__uint_as_float(cand[t * kWave + lane]));
+      atomicAdd(&h[wave_bin_word((key >> sh2) & dm2)], (t < cnt && (key & pmask) == prefix) ? 1u : 0u);
+    }
+    wave_lds_fence();
+    uint32_t ctot2, bin[1], rin[1], bc[1];
+    bool bok[1];
+    const uint32_t Rk[1] = {kk};
+    wave_find_bins<1>(h, Rk, lane, ctot2, bin, rin, bc, bok);
+    prefix |= bin[0] << sh2;
+    pmask |= dm2 << sh2;
+    kk = rin[0];
+    if (kk == bc[0]) {
+      whole = true;
+      break;
+    }
+  }
+
+  // 4. emit, ascending positions: chunk j, lane l's positions 256 j + 4 l + e
+  // follow every kept position of the lanes below it
+  if (whole) {
+    // keep x >= t: everything above hi, and the candidates whose key is at
+    // least the cut bin's lowest key
+    const float t_f = fmaxf(lo_f, key_score(prefix));
+    // stores through a buffer resource over the row's k outputs: the base
+    // stays in scalar registers, a lane whose key is not kept stores to an
+    // offset past the end (dropped by the hardware, so no branch per key), and
+    // so is a store past the k-th slot (impossible while the counts hold)
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        out, static_cast<short>(0), k * static_cast<int>(sizeof(int32_t)), 0x00020000);
+    uint32_t before = 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      bool t[4];
+      uint64_t mk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[e] = valid(j) && __uint_as_float(raw[j][e]) >= t_f;
+        mk[e] = __ballot(t[e]);
+      }
+      uint32_t ob = (before + lanes_below(mk[0]) + lanes_below(mk[1]) + lanes_below(mk[2]) + lanes_below(mk[3])) * 4u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(j * 4 * kWave + 4 * lane + e), orsrc,
+                                              static_cast<int>(t[e] ? ob : 0x7ffffff0u), 0, 0);
+        ob += t[e] ? 4u : 0u;
+      }
+      before += static_cast<uint32_t>(__popcll(mk[0]) + __popcll(mk[1]) + __popcll(mk[2]) + __popcll(mk[3]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return true;
+  }
+  // the cut lies inside a run of scores equal to c: keep every greater score
+  // and the first kk equal ones in position order
+  const float c = key_score(prefix);
+  const uint32_t take_eq = kk;
+  uint32_t sel_before = 0u, eq_before = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    uint32_t gt_bits = 0u, eq_bits = 0u;
+    if (valid(j)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = __uint_as_float(raw[j][e]);
+        if (x > c) gt_bits |= 1u << e;
+        else if (x == c) eq_bits |= 1u << e;
+      }
+    }
+    const uint32_t packed = (static_cast<uint32_t>(__popc(gt_bits)) << 16) | static_cast<uint32_t>(__popc(eq_bits));
+    const uint32_t incl = wave_incl_scan32(packed);  // per-chunk sums stay below 2^16
+    const uint32_t tot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+    const uint32_t excl = incl - packed;
+    uint32_t eq_rank = eq_before + (excl & 0xffffu);
+    const uint32_t taken_eq_before = min(eq_rank, take_eq) - min(eq_before, take_eq);
+    uint32_t o = sel_before + (excl >> 16) + taken_eq_before;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool take = (gt_bits >> e) & 1u;
+      if ((eq_bits >> e) & 1u) {
+        take = eq_rank < take_eq;
+        ++eq_rank;
+      }
+      if (take) {
+        if (o < static_cast<uint32_t>(k)) out[o] = j * 4 * kWave + 4 * lane + e;
+        ++o;
+      }
+    }
+    const uint32_t tot_eq = tot & 0xffffu;
+    sel_before += (tot >> 16) + (min(eq_before + tot_eq, take_eq) - min(eq_before, take_eq));
+    eq_before += tot_eq;
+  }
+  return true;
+}
+
+template <int J, bool Full>
+__global__ __launch_bounds__(kWaveRowsPerBlock * kWave, J >= 32 ? 2 : 3)
 void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, int32_t* __restrict__ idx,
                       int32_t* __restrict__ nan_out) {
   __shared__ uint32_t hist_all[kWaveRowsPerBlock * kBins];
+  __shared__ uint32_t cand_all[J >= 16 ? kWaveRowsPerBlock * kCandRows * kWave : 1];
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  const int w = kWaveRowsPerBlock == 1 ? 0 : static_cast<int>(threadIdx.x) / kWave;  // uniform row base
   const int row = blockIdx.x * kWaveRowsPerBlock + w;
   if (row >= rows) return;  // the whole wave leaves; nothing below synchronises waves
   uint32_t* h = hist_all + w * kBins;
@@ -714,29 +1002,36 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
   const int n4 = n >> 2;
   auto valid = [&](int j) { return Full || j * kWave + lane < n4; };
   uint32_t keys[J][4];
+  // every load in flight before the first is used; even chunks first (the
+  // bracket's sample reads them), so the sample waits for half the loads only
 #pragma unroll
-  for (int j = 0; j < J; ++j) {  // every load in flight before the first is used
+  for (int jj = 0; jj < J; ++jj) {
+    const int j = jj < J / 2 ? 2 * jj : 2 * (jj - J / 2) + 1;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (valid(j)) v = __builtin_nontemporal_load(r4 + j * kWave + lane);
 #pragma unroll
     for (int e = 0; e < 4; ++e) keys[j][e] = v[e];
   }
-#pragma unroll
-  for (int j = 0; j < J; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) keys[j][e] = score_key(__uint_as_float(keys[j][e]));
-  if (nan_out) {  // NaN scores (key 0): per-lane counts, then one wave sum
+  if (nan_out) {  // NaN scores: per-lane counts, then one wave sum
     uint32_t nan = 0u;
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        nan += (valid(j) && keys[j][e] == 0u) ? 1u : 0u;
+        nan += (valid(j) && (keys[j][e] & 0x7fffffffu) > 0x7f800000u) ? 1u : 0u;
         __builtin_amdgcn_sched_barrier(0);  // one key at a time: no 128 live compare results
       }
     nan = wave_incl_scan32(nan);
     if (lane == kWave - 1) nan_out[row] = static_cast<int32_t>(nan);
   }
+  if constexpr (J >= 16) {
+    if (k > 0 && k < n && wave_topk_bracket<J, Full>(keys, lane, n, k, h, cand_all + w * kCandRows * kWave, out))
+      return;
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keys[j][e] = score_key(__uint_as_float(keys[j][e]));
 
   // Bits shared by every key of the row are settled first (wave min/max of the
   // keys in registers); digits of up to 11 bits then start right below them, so
