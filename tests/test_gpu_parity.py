@@ -207,6 +207,34 @@ def test_topk_strided_rows_all_kinds(dash, kind, n):
             np.testing.assert_array_equal(got[r], oracle.select_topk(s[r], k))
 
 
+@pytest.mark.parametrize("n", [8192, 8188, 4096, 4092])
+def test_topk_wave_rows_sample_misleads(dash, n):
+    """Rows whose sampled chunks (the even 256-score chunks of a row held by
+    one wave) hold only small scores while the odd chunks hold large ones: the
+    sample's estimate of the cut is far off, the bracket misses and the row
+    takes the digit passes over all its keys.  Mixed in a batch with random
+    rows, which take the bracket; every row bit-exact against the oracle,
+    including cuts inside runs of equal scores."""
+    rows = 256
+    g = np.random.default_rng(n)
+    s = g.random((rows, n), dtype=np.float32)
+    pos = np.arange(n)
+    odd = ((pos // 256) % 2) == 1
+    for r in range(0, rows, 2):
+        s[r, odd] += 10.0
+    for r in range(1, rows, 4):  # ties: few distinct values in the odd rows' upper half
+        s[r, n // 2:] = np.floor(s[r, n // 2:] * 4.0)
+    sd = torch.from_numpy(s).cuda()
+    for k in (1, n // 3, n // 2 - 7, n - 1):
+        say("topk sample misleads", n, k)
+        idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+        dash.dash_select(sd, idx, mode=dash.DASH_SEL_TOPK, k=k, n_max=n, rows=rows)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for r in range(rows):
+            np.testing.assert_array_equal(got[r], oracle.select_topk(s[r], k))
+
+
 @pytest.mark.parametrize("rows,n,k", [(48, 3000, 1234), (80, 3000, 1234), (70, 8192, 4096), (64, 8193, 100),
                                       (66, 1, 1), (65, 40000, 39999),
                                       (256, 8192, 4096), (300, 2048, 1000), (257, 4, 2), (512, 4100, 1),
