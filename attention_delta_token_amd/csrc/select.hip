@@ -12,7 +12,8 @@
 //   层间更新动态监测 and 选择性停止机制.
 //
 // One workgroup of 1024 threads owns one row of scores (batches of at least
-// 256 rows of at most 8192 aligned scores take one wave per row instead).
+// 256 rows of at most 8192 aligned scores take one wave per row instead, and
+// rows of more than 2048 of those bracket the cut from a sample first).
 // Scores map to order-preserving 32-bit keys.  A radix select over LDS
 // histograms finds the cut key T and how many keys equal to T must be taken:
 // for rows held in registers and for a single long row, the bits shared by the
@@ -673,7 +674,9 @@ namespace {
 // ---------------------------------------------------------------------------
 // Batched rows: one wave per row, no workgroup barrier anywhere.  Lane l holds
 // the keys of positions 256*j + 4*l + e (e < 4, j < J) in registers (one
-// 16-byte load each).  The bits every key shares are settled from the wave's
+// 16-byte load each).  Rows of more than 2048 scores first try the bracket
+// above (wave_topk_bracket); the rest, and rows whose bracket misses, take the
+// digit passes over every key described here.  The bits every key shares are settled from the wave's
 // smallest and largest key; digits of up to 11 bits follow, counted into the
 // wave's own 2048-bin LDS histogram.  The search stops as soon as the bin
 // holding the cut is taken whole (its count equals the keys still wanted), and
@@ -1002,8 +1005,9 @@ void topk_wave_kernel(const float* __restrict__ score, int rows, int n, int k, i
   const int n4 = n >> 2;
   auto valid = [&](int j) { return Full || j * kWave + lane < n4; };
   uint32_t keys[J][4];
-  // every load in flight before the first is used; even chunks first (the
-  // bracket's sample reads them), so the sample waits for half the loads only
+  // every load in flight before the first is used; even chunks first (with
+  // 32 chunks the bracket's sample reads only those, so it waits for half the
+  // loads)
 #pragma unroll
   for (int jj = 0; jj < J; ++jj) {
     const int j = jj < J / 2 ? 2 * jj : 2 * (jj - J / 2) + 1;
