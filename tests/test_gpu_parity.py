@@ -164,11 +164,13 @@ def test_topk_long_row_multi_workgroup(dash, kind, n):
     np.testing.assert_array_equal(idx.cpu().numpy(), oracle.select_topk(s, k) * 3 + 11)
 
 
-@pytest.mark.parametrize("n", [8192, 8188, 4096, 2048, 1028, 1024, 1020, 500])
+@pytest.mark.parametrize("n", [8192, 8188, 4100, 4096, 2052, 2048, 1028, 1024, 1020, 500])
 @pytest.mark.parametrize("kind", SCORE_KINDS)
 def test_topk_wave_rows_all_kinds(dash, kind, n):
     """The one-wave-per-row batch path on every score family, rows that fill
-    their 256-score chunks (8192, 4096, 2048, 1024) and rows that do not; k from 1 to
+    their 256-score chunks (8192, 4096, 2048, 1024) and rows that do not (4100
+    and 2052: the smallest rows of the bracketed path for 32 and 16 chunks per
+    lane, whose sample holds partly filled chunks); k from 1 to
     n, so cuts fall inside runs of equal scores (fewvalues, equal, bf16ties)
     as well as between distinct ones.  NaN counts per row checked too."""
     rows = 256
